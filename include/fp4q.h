@@ -1,0 +1,175 @@
+/*
+ * fp4q.h -- C ABI of the MI355X (gfx950) block-scaled FP4 quantization library.
+ *
+ * The operations follow these web pages on the method:
+ *   [TRACE-JA] ai-papers.net summary "TRACE ... ロールアウト誘導型QAT",
+ *              sections "TRACEの仕組み" (guided rounding: pick the upper or
+ *              lower adjacent codeword the rollout chose) and
+ *              "量子化情報キャッシュ" (keep 1 mantissa bit + the block scale,
+ *              deep layers only, about 1/6 of the full record).
+ *   [TRACE-KO] sns.style summary, section "작동 원리의 공학적 이해": a few
+ *              values share one scale, each value is 4 bits, the rounding
+ *              direction is a per-value choice; the rollout engine exports its
+ *              quantization result and the trainer consumes it.
+ *   [FQT-FP4]  aibr.jp FP4 training summary, section 3: NVFP4 = 16-value
+ *              blocks of E2M1 with an E4M3 scale; round-to-nearest forward,
+ *              stochastic rounding backward.
+ *   [TETRAJET] aibr.jp MXFP4 summary, section 3: per-group scale.
+ *   [UFP4]     UFP4 recipe page, RHT and uniform-grid sections.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor arguments are DEVICE pointers owned by the caller; the library
+ *     allocates nothing, keeps no pointer after returning and never
+ *     synchronizes.  Work is enqueued asynchronously on `stream` (NULL = the
+ *     default stream); buffers must stay valid until the stream reaches it.
+ *   - bf16 inputs are row-major [rows, cols] with row stride `ld` elements
+ *     (ld >= cols, ld % 8 == 0, base 16-byte aligned).  Outputs are dense.
+ *   - Element index i = r*cols + c (independent of ld) orders codes, guide
+ *     bits and the stochastic-rounding random stream.
+ *   - Packed codes: uint8[rows*cols/2], element i in nibble i%2 of byte i/2;
+ *     a code is sign<<3 | k, k the 3-bit magnitude index on the grid.
+ *   - Block scales: uint8[rows*cols/B], one per block of B consecutive
+ *     elements of a row (B = 16 NVFP4, 32 MXFP4).  NVFP4: OCP E4M3FN code;
+ *     MXFP4: E8M0 biased exponent.  0x7F (E4M3) / 0xFF (E8M0) mark a block
+ *     that held a non-finite value; its codes are all zero.
+ *   - Guide bitplane: uint8[rows*cols/8], bit i%8 of byte i/8 = LSB of k_i.
+ *   - Device pointer alignment: x, codes, guide bits, dequant output and
+ *     unpack output 16 bytes; scales 1 byte; tensor scales 4 bytes.
+ *   - Errors are detected on the host before any launch and returned as an
+ *     fp4_status; nothing is launched then.  A failed launch returns
+ *     FP4_ERR_HIP.  fp4_last_error() gives the message (per thread).
+ *   - rows*cols == 0 is a no-op that returns FP4_OK.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP4_OK = 0,
+    FP4_ERR_ARG = 1,         /* null pointer, unknown enum, negative size */
+    FP4_ERR_SHAPE = 2,       /* cols % B != 0, ld < cols, too many elements */
+    FP4_ERR_ALIGN = 3,       /* misaligned pointer or ld % 8 != 0 */
+    FP4_ERR_UNSUPPORTED = 4, /* combination not provided */
+    FP4_ERR_HIP = 5          /* the HIP runtime reported an error */
+} fp4_status;
+
+typedef enum { FP4_NVFP4 = 0, FP4_MXFP4 = 1 } fp4_format;
+typedef enum { FP4_GRID_E2M1 = 0, FP4_GRID_UNIFORM = 1 } fp4_grid;
+typedef enum { FP4_RTN = 0, FP4_SR = 1 } fp4_rounding;
+typedef enum { FP4_OUT_F32 = 0, FP4_OUT_BF16 = 1 } fp4_dtype;
+typedef enum { FP4_MODE_RTN = 0, FP4_MODE_SR = 1, FP4_MODE_GUIDED = 2 } fp4_mode;
+
+/* Quantizer configuration (40 bytes, no padding).
+ *   format   fp4_format: NVFP4 (16-blocks, E4M3 scale, fp32 tensor scale
+ *            [FQT-FP4 §3]) or MXFP4 (32-blocks, E8M0 scale [TETRAJET §3]).
+ *   grid     fp4_grid: E2M1 {0,.5,1,1.5,2,3,4,6} or the uniform INT4 grid
+ *            {0..7} [UFP4].
+ *   rounding fp4_rounding, used by fp4_quantize only.
+ *   rht16    nonzero: apply y = 1/4 H16 D x to each 16-group first [UFP4].
+ *   sr_seed  Philox4x32-10 key of stochastic rounding; sr_offset is added to
+ *            the 16-element group index to form the counter.
+ *   rht_seed Philox4x32-10 key of the RHT sign diagonal D. */
+typedef struct {
+    int32_t format;
+    int32_t grid;
+    int32_t rounding;
+    int32_t rht16;
+    uint64_t sr_seed;
+    uint64_t sr_offset;
+    uint64_t rht_seed;
+} fp4_cfg;
+
+/* Tensor scale for the NVFP4 block format [FQT-FP4 §3 E4M3 block scales
+ * under one fp32 tensor scale]: s_t = amax / (Gmax*448), amax the largest
+ * finite |y| of the tensor (y = x, or the RHT of x when cfg->rht16), and
+ * s_t = 1 for an all-zero tensor.  Writes one float to tensor_scale_out
+ * (device, also used as the reduction accumulator). */
+fp4_status fp4_tensor_scale(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
+                            int64_t ld, float* tensor_scale_out, hipStream_t stream);
+
+/* Block quantization with round-to-nearest-even or stochastic rounding
+ * [FQT-FP4 §3; TRACE-KO].  Per block: NVFP4 scale code = E4M3 RNE of
+ * amax / RN(Gmax*s_t), saturating at 448, elements multiplied by
+ * RN(1/RN(dec(code)*s_t)); MXFP4 scale exponent e = floor(log2 amax) - 2,
+ * elements multiplied by 2^-e.  Scaled magnitudes are clamped to Gmax and
+ * rounded to the grid: RTN ties to the even code; SR rounds up iff
+ * 2u+1 < 512 f, u the element's byte (i%16) of Philox4x32-10(key = sr_seed,
+ * counter = (i/16 + sr_offset, 0, 0)), f its position in the bracket.
+ *   tensor_scale   NVFP4: device pointer to s_t (positive, finite);
+ *                  MXFP4: ignored (may be NULL).
+ *   codes, scales  outputs (see conventions).
+ *   guide_bits_out NULL, or the guide bitplane of the result, emitted in the
+ *                  same pass (rollout side of [TRACE-JA] "量子化情報キャッシュ"). */
+fp4_status fp4_quantize(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
+                        int64_t ld, const float* tensor_scale, void* codes, void* scales,
+                        void* guide_bits_out, hipStream_t stream);
+
+/* Rollout-guided quantization [TRACE-JA "TRACEの仕組み"; TRACE-KO]: the
+ * block scale (and NVFP4 tensor scale) come from the guide; each element is
+ * rounded to the one of its two bracketing codewords whose LSB equals its
+ * guide bit (a value on a codeword keeps it).  `scales` receives a copy of
+ * guide_scales.  A block whose guide scale is a NaN code, or whose input
+ * holds a non-finite value, gets all-zero codes. */
+fp4_status fp4_quantize_guided(const fp4_cfg* cfg, const void* x_bf16, int64_t rows,
+                               int64_t cols, int64_t ld, const void* guide_bits,
+                               const void* guide_scales, const float* guide_tensor_scale,
+                               void* codes, void* scales, hipStream_t stream);
+
+/* Dequantization [TRACE-KO: shared block scale, 4-bit values]:
+ * NVFP4 val = RN(RN(G[k]*dec(scale))*s_t); MXFP4 val = G[k]*2^e; the code's
+ * sign applied; fp32 output, or bf16 by round-to-nearest-even of that fp32.
+ * A NaN scale code gives the canonical quiet NaN for its block.
+ * out: [rows, cols] with row stride ld_out elements (ld_out >= cols,
+ * ld_out*size % 16 == 0). */
+fp4_status fp4_dequantize(const fp4_cfg* cfg, const void* codes, const void* scales,
+                          const float* tensor_scale, int64_t rows, int64_t cols, void* out,
+                          int64_t ld_out, fp4_dtype dtype, hipStream_t stream);
+
+/* Guidance-cache packing [TRACE-JA "量子化情報キャッシュ"; TRACE-KO
+ * "가수와 스케일"]: guide bit i = LSB of code i, guide_scales = scales. */
+fp4_status guide_pack(const fp4_cfg* cfg, const void* codes, const void* scales, int64_t rows,
+                      int64_t cols, void* guide_bits, void* guide_scales, hipStream_t stream);
+
+/* Inverse view of the guide: mant_u8[i] = guide bit i (0 or 1), scales_out =
+ * guide_scales. */
+fp4_status guide_unpack(const fp4_cfg* cfg, const void* guide_bits, const void* guide_scales,
+                        int64_t rows, int64_t cols, void* mant_u8, void* scales_out,
+                        hipStream_t stream);
+
+/* Standalone 16-point random Hadamard transform [UFP4 RHT section] of each
+ * 16-group of a bf16 matrix: forward y = 1/4 H16 D x, inverse x = D 1/4 H16 y,
+ * Sylvester order, butterfly stages h = 1,2,4,8 in fp32.  D_j = -1 iff bit j
+ * of word 0 of Philox4x32-10(key = seed, counter = (0,0,1,0)).  cols % 16 == 0.
+ * Output dense fp32 or bf16 (RNE). */
+fp4_status fp4_rht16(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
+                     int inverse, void* out, fp4_dtype dtype, hipStream_t stream);
+
+/* Element encode of n pre-scaled fp32 values (the per-element rounding step
+ * on its own, for exhaustive verification): out[i] = sign<<3 | k of v[i]
+ * clamped to Gmax; mode FP4_MODE_RTN, FP4_MODE_SR (aux[i] = random byte) or
+ * FP4_MODE_GUIDED (aux[i] = guide bit).  aux may be NULL for RTN.
+ * n % 8 == 0; v 16-byte aligned, aux and out 8-byte aligned. */
+fp4_status fp4_encode_values(int grid, int mode, const float* v, const uint8_t* aux, int64_t n,
+                             uint8_t* out, hipStream_t stream);
+
+/* Buffer sizes in bytes. */
+size_t fp4_codes_bytes(int64_t rows, int64_t cols);
+size_t fp4_scales_bytes(int format, int64_t rows, int64_t cols);
+/* Guide bitplane + guide scales + 4 bytes of tensor scale. */
+size_t fp4_guide_bytes(int format, int64_t rows, int64_t cols);
+
+const char* fp4_status_str(fp4_status s);
+/* Message of the last error on the calling thread ("" if none). */
+const char* fp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4Q_H */

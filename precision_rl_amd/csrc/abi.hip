@@ -1,0 +1,273 @@
+// abi.hip -- the extern "C" entry points of libfp4q: argument validation,
+// parameter blocks and kernel launches.  No allocation, no synchronization.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/fp4q.h"
+#include "device.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fp4_status fail(fp4_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fp4_status ok() {
+    g_err[0] = '\0';
+    return FP4_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int block_of(int format) { return format == FP4_MXFP4 ? 32 : 16; }
+
+fp4_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Shared checks of a bf16 [rows, cols] input with row stride ld.
+fp4_status check_cfg(const fp4_cfg* cfg) {
+    if (!cfg) return fail(FP4_ERR_ARG, "cfg is NULL");
+    if (cfg->format != FP4_NVFP4 && cfg->format != FP4_MXFP4)
+        return fail(FP4_ERR_ARG, "unknown format %d", cfg->format);
+    if (cfg->grid != FP4_GRID_E2M1 && cfg->grid != FP4_GRID_UNIFORM)
+        return fail(FP4_ERR_ARG, "unknown grid %d", cfg->grid);
+    if (cfg->rounding != FP4_RTN && cfg->rounding != FP4_SR)
+        return fail(FP4_ERR_ARG, "unknown rounding %d", cfg->rounding);
+    return FP4_OK;
+}
+
+fp4_status check_matrix(int64_t rows, int64_t cols, int64_t ld, int B, const void* x, uint64_t* ngroups) {
+    if (rows < 0 || cols < 0) return fail(FP4_ERR_ARG, "negative shape rows=%lld cols=%lld",
+                                          (long long)rows, (long long)cols);
+    if (cols % B != 0) return fail(FP4_ERR_SHAPE, "cols=%lld is not a multiple of the block size %d",
+                                   (long long)cols, B);
+    if (rows > 0 && cols > 0) {
+        if (ld < cols) return fail(FP4_ERR_SHAPE, "ld=%lld < cols=%lld", (long long)ld, (long long)cols);
+        if (ld % 8 != 0) return fail(FP4_ERR_ALIGN, "ld=%lld is not a multiple of 8 elements", (long long)ld);
+        if (!x) return fail(FP4_ERR_ARG, "input pointer is NULL");
+        if (!aligned(x, 16)) return fail(FP4_ERR_ALIGN, "input pointer is not 16-byte aligned");
+    }
+    const uint64_t g = (uint64_t)rows * (uint64_t)cols / 16;
+    if (g >= (1ull << 31)) return fail(FP4_ERR_SHAPE, "too many elements (%llu groups of 16)",
+                                       (unsigned long long)g);
+    if (cols / 16 >= (1ll << 31)) return fail(FP4_ERR_SHAPE, "cols too large");
+    *ngroups = g;
+    return FP4_OK;
+}
+
+fp4_status need(const void* p, uintptr_t align, const char* name) {
+    if (!p) return fail(FP4_ERR_ARG, "%s is NULL", name);
+    if (!aligned(p, align)) return fail(FP4_ERR_ALIGN, "%s is not %u-byte aligned", name, (unsigned)align);
+    return FP4_OK;
+}
+
+#define FP4Q_TRY(expr)                       \
+    do {                                     \
+        fp4_status _s = (expr);              \
+        if (_s != FP4_OK) return _s;         \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t fp4_codes_bytes(int64_t rows, int64_t cols) { return (size_t)(rows * cols / 2); }
+
+size_t fp4_scales_bytes(int format, int64_t rows, int64_t cols) {
+    return (size_t)(rows * cols / block_of(format));
+}
+
+size_t fp4_guide_bytes(int format, int64_t rows, int64_t cols) {
+    return (size_t)(rows * cols / 8) + fp4_scales_bytes(format, rows, cols) + 4;
+}
+
+const char* fp4_status_str(fp4_status s) {
+    switch (s) {
+        case FP4_OK: return "ok";
+        case FP4_ERR_ARG: return "invalid argument";
+        case FP4_ERR_SHAPE: return "invalid shape";
+        case FP4_ERR_ALIGN: return "misaligned pointer or stride";
+        case FP4_ERR_UNSUPPORTED: return "unsupported combination";
+        case FP4_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* fp4_last_error(void) { return g_err; }
+
+fp4_status fp4_tensor_scale(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
+                            int64_t ld, float* tensor_scale_out, hipStream_t stream) {
+    FP4Q_TRY(check_cfg(cfg));
+    uint64_t ng = 0;
+    FP4Q_TRY(check_matrix(rows, cols, ld, 16, x_bf16, &ng));
+    FP4Q_TRY(need(tensor_scale_out, 4, "tensor_scale_out"));
+    fp4q::AmaxParams p{};
+    p.x = static_cast<const uint16_t*>(x_bf16);
+    p.ld = ld;
+    p.ngroups = (uint32_t)ng;
+    p.gpr = fp4q::make_fastdiv(cols > 0 ? (uint32_t)(cols / 16) : 1u);
+    p.rht_seed = cfg->rht_seed;
+    p.acc = tensor_scale_out;
+    return hip_status(fp4q::launch_tensor_scale(cfg->grid, cfg->rht16 != 0, ld == cols, p, stream),
+                      "fp4_tensor_scale launch");
+}
+
+static fp4_status quantize_common(const fp4_cfg* cfg, int mode, const void* x_bf16, int64_t rows,
+                                  int64_t cols, int64_t ld, const float* ts, void* codes, void* scales,
+                                  void* bits_out, const void* gbits, const void* gscales,
+                                  hipStream_t stream) {
+    FP4Q_TRY(check_cfg(cfg));
+    uint64_t ng = 0;
+    FP4Q_TRY(check_matrix(rows, cols, ld, block_of(cfg->format), x_bf16, &ng));
+    if (ng == 0) return ok();
+    FP4Q_TRY(need(codes, 16, "codes"));
+    FP4Q_TRY(need(scales, 1, "scales"));
+    if (cfg->format == FP4_NVFP4) FP4Q_TRY(need(ts, 4, "tensor_scale"));
+    if (bits_out) FP4Q_TRY(need(bits_out, 16, "guide_bits_out"));
+    if (mode == fp4q::MODE_GUIDED) {
+        FP4Q_TRY(need(gbits, 16, "guide_bits"));
+        FP4Q_TRY(need(gscales, 1, "guide_scales"));
+    }
+    fp4q::QuantParams p{};
+    p.x = static_cast<const uint16_t*>(x_bf16);
+    p.ld = ld;
+    p.ngroups = (uint32_t)ng;
+    p.gpr = fp4q::make_fastdiv((uint32_t)(cols / 16));
+    p.ts = ts;
+    p.codes = static_cast<uint8_t*>(codes);
+    p.scales = static_cast<uint8_t*>(scales);
+    p.bits_out = static_cast<uint8_t*>(bits_out);
+    p.gbits = static_cast<const uint8_t*>(gbits);
+    p.gscales = static_cast<const uint8_t*>(gscales);
+    p.key0 = (uint32_t)cfg->sr_seed;
+    p.key1 = (uint32_t)(cfg->sr_seed >> 32);
+    p.sr_offset = cfg->sr_offset;
+    p.rht_seed = cfg->rht_seed;
+    return hip_status(fp4q::launch_quantize(cfg->format, cfg->grid, mode, cfg->rht16 != 0,
+                                            bits_out != nullptr, ld == cols, p, stream),
+                      "quantize launch");
+}
+
+fp4_status fp4_quantize(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
+                        int64_t ld, const float* tensor_scale, void* codes, void* scales,
+                        void* guide_bits_out, hipStream_t stream) {
+    FP4Q_TRY(check_cfg(cfg));
+    const int mode = cfg->rounding == FP4_SR ? fp4q::MODE_SR : fp4q::MODE_RTN;
+    return quantize_common(cfg, mode, x_bf16, rows, cols, ld, tensor_scale, codes, scales,
+                           guide_bits_out, nullptr, nullptr, stream);
+}
+
+fp4_status fp4_quantize_guided(const fp4_cfg* cfg, const void* x_bf16, int64_t rows,
+                               int64_t cols, int64_t ld, const void* guide_bits,
+                               const void* guide_scales, const float* guide_tensor_scale,
+                               void* codes, void* scales, hipStream_t stream) {
+    return quantize_common(cfg, fp4q::MODE_GUIDED, x_bf16, rows, cols, ld, guide_tensor_scale,
+                           codes, scales, nullptr, guide_bits, guide_scales, stream);
+}
+
+fp4_status fp4_dequantize(const fp4_cfg* cfg, const void* codes, const void* scales,
+                          const float* tensor_scale, int64_t rows, int64_t cols, void* out,
+                          int64_t ld_out, fp4_dtype dtype, hipStream_t stream) {
+    FP4Q_TRY(check_cfg(cfg));
+    if (dtype != FP4_OUT_F32 && dtype != FP4_OUT_BF16) return fail(FP4_ERR_ARG, "unknown dtype %d", (int)dtype);
+    uint64_t ng = 0;
+    FP4Q_TRY(check_matrix(rows, cols, cols, block_of(cfg->format), codes ? codes : (const void*)16, &ng));
+    if (ng == 0) return ok();
+    FP4Q_TRY(need(codes, 16, "codes"));
+    FP4Q_TRY(need(scales, 1, "scales"));
+    FP4Q_TRY(need(out, 16, "out"));
+    if (cfg->format == FP4_NVFP4) FP4Q_TRY(need(tensor_scale, 4, "tensor_scale"));
+    if (ld_out < cols) return fail(FP4_ERR_SHAPE, "ld_out=%lld < cols=%lld", (long long)ld_out, (long long)cols);
+    const int64_t esz = dtype == FP4_OUT_BF16 ? 2 : 4;
+    if ((ld_out * esz) % 16 != 0) return fail(FP4_ERR_ALIGN, "output row stride is not a multiple of 16 bytes");
+    fp4q::DequantParams p{};
+    p.codes = static_cast<const uint8_t*>(codes);
+    p.scales = static_cast<const uint8_t*>(scales);
+    p.ts = tensor_scale;
+    p.out = out;
+    p.ld_out = ld_out;
+    p.ngroups = (uint32_t)ng;
+    p.gpr = fp4q::make_fastdiv((uint32_t)(cols / 16));
+    return hip_status(fp4q::launch_dequantize(cfg->format, cfg->grid, dtype == FP4_OUT_BF16, p, stream),
+                      "dequantize launch");
+}
+
+static fp4_status guide_common(const fp4_cfg* cfg, int64_t rows, int64_t cols, const void* in,
+                               const void* scales_in, void* out, void* scales_out, uint64_t* ng) {
+    FP4Q_TRY(check_cfg(cfg));
+    FP4Q_TRY(check_matrix(rows, cols, cols, block_of(cfg->format), in ? in : (const void*)16, ng));
+    if (*ng == 0) return ok();
+    FP4Q_TRY(need(in, 16, "input"));
+    FP4Q_TRY(need(scales_in, 1, "scales input"));
+    FP4Q_TRY(need(out, 16, "output"));
+    FP4Q_TRY(need(scales_out, 1, "scales output"));
+    return FP4_OK;
+}
+
+fp4_status guide_pack(const fp4_cfg* cfg, const void* codes, const void* scales, int64_t rows,
+                      int64_t cols, void* guide_bits, void* guide_scales, hipStream_t stream) {
+    uint64_t ng = 0;
+    FP4Q_TRY(guide_common(cfg, rows, cols, codes, scales, guide_bits, guide_scales, &ng));
+    if (ng == 0) return ok();
+    fp4q::GuideParams p{static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
+                        static_cast<uint8_t*>(guide_bits), static_cast<uint8_t*>(guide_scales),
+                        (uint32_t)ng};
+    return hip_status(fp4q::launch_guide_pack(cfg->format, p, stream), "guide_pack launch");
+}
+
+fp4_status guide_unpack(const fp4_cfg* cfg, const void* guide_bits, const void* guide_scales,
+                        int64_t rows, int64_t cols, void* mant_u8, void* scales_out,
+                        hipStream_t stream) {
+    uint64_t ng = 0;
+    FP4Q_TRY(guide_common(cfg, rows, cols, guide_bits, guide_scales, mant_u8, scales_out, &ng));
+    if (ng == 0) return ok();
+    fp4q::GuideParams p{static_cast<const uint8_t*>(guide_bits), static_cast<const uint8_t*>(guide_scales),
+                        static_cast<uint8_t*>(mant_u8), static_cast<uint8_t*>(scales_out), (uint32_t)ng};
+    return hip_status(fp4q::launch_guide_unpack(cfg->format, p, stream), "guide_unpack launch");
+}
+
+fp4_status fp4_rht16(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
+                     int inverse, void* out, fp4_dtype dtype, hipStream_t stream) {
+    if (dtype != FP4_OUT_F32 && dtype != FP4_OUT_BF16) return fail(FP4_ERR_ARG, "unknown dtype %d", (int)dtype);
+    uint64_t ng = 0;
+    FP4Q_TRY(check_matrix(rows, cols, ld, 16, x_bf16, &ng));
+    if (ng == 0) return ok();
+    FP4Q_TRY(need(out, 16, "out"));
+    fp4q::RhtParams p{};
+    p.x = static_cast<const uint16_t*>(x_bf16);
+    p.ld = ld;
+    p.out = out;
+    p.ngroups = (uint32_t)ng;
+    p.gpr = fp4q::make_fastdiv((uint32_t)(cols / 16));
+    p.seed = seed;
+    return hip_status(fp4q::launch_rht16(inverse != 0, dtype == FP4_OUT_BF16, ld == cols, p, stream),
+                      "rht16 launch");
+}
+
+fp4_status fp4_encode_values(int grid, int mode, const float* v, const uint8_t* aux, int64_t n,
+                             uint8_t* out, hipStream_t stream) {
+    if (grid != FP4_GRID_E2M1 && grid != FP4_GRID_UNIFORM) return fail(FP4_ERR_ARG, "unknown grid %d", grid);
+    if (mode != FP4_MODE_RTN && mode != FP4_MODE_SR && mode != FP4_MODE_GUIDED)
+        return fail(FP4_ERR_ARG, "unknown mode %d", mode);
+    if (n < 0 || n % 8 != 0) return fail(FP4_ERR_SHAPE, "n=%lld must be a non-negative multiple of 8", (long long)n);
+    if (n / 8 >= (1ll << 31)) return fail(FP4_ERR_SHAPE, "n too large");
+    if (n == 0) return ok();
+    FP4Q_TRY(need(v, 16, "v"));
+    FP4Q_TRY(need(out, 8, "out"));
+    if (mode != FP4_MODE_RTN) FP4Q_TRY(need(aux, 8, "aux"));
+    if (aux && !aligned(aux, 8)) return fail(FP4_ERR_ALIGN, "aux is not 8-byte aligned");
+    fp4q::EncodeParams p{v, aux, out, (uint32_t)(n / 8)};
+    return hip_status(fp4q::launch_encode_values(grid, mode, p, stream), "encode_values launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,278 @@
+// device.h -- gfx950 device helpers for block-scaled FP4 quantization.
+//
+// Element encoders work on 8 elements at a time and return one packed dword
+// (element j in nibble j), the unit the kernels store.  E2M1 rounding uses
+// the gfx950 scaled-convert instructions:
+//   v_cvt_scalef32_pk_fp4_f32     round to nearest even, saturating at 6
+//   v_cvt_scalef32_sr_pk_fp4_f32  with a zero random word: truncation, i.e.
+//                                 the lower bracketing codeword
+// both called with scale 1.0, so the instruction sees the already scaled
+// value RN(y * inv).  Stochastic rounding and the uniform grid are computed
+// with plain fp32/integer arithmetic.  Per-block work (scale codes and
+// reciprocals) is written in ordinary IEEE fp32 (correctly rounded division,
+// denormals kept).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------- E4M3 / E8M0
+
+// E4M3FN code of t in [0, 448] (callers clamp), round to nearest even.
+__device__ __forceinline__ uint32_t e4m3_encode_rne(float t) {
+    uint32_t b = __float_as_uint(t);
+    if (t < 0.015625f) {                        // below 2^-6: step 2^-9
+        return (uint32_t)__builtin_rintf(t * 512.0f);  // 0..8; 8 is the smallest normal
+    }
+    b += 0x7FFFFu + ((b >> 20) & 1u);           // keep 3 mantissa bits, ties to even
+    return (b >> 20) - (120u << 3);             // rebias exponent 127 -> 7
+}
+
+// Exact fp32 value of an E4M3FN magnitude code (sign bit ignored, 0x7F not special).
+__device__ __forceinline__ float e4m3_decode(uint32_t code) {
+    code &= 0x7Fu;
+    uint32_t e = code >> 3;
+    float sub = (float)(code & 7u) * 0.001953125f;   // m * 2^-9
+    float nrm = __uint_as_float((code << 20) + (120u << 23));
+    return e == 0 ? sub : nrm;
+}
+
+// NVFP4 block reciprocal from a scale code: inv = RN(1/RN(dec*s_t)), 0 when the
+// product is 0, FLT_MAX when the reciprocal overflows.
+__device__ __forceinline__ float nvfp4_inv(uint32_t code, float ts) {
+    float S = e4m3_decode(code) * ts;
+    float inv = 1.0f / S;
+    inv = __builtin_isinf(inv) ? kFltMax : inv;
+    return S == 0.0f ? 0.0f : inv;
+}
+
+// MXFP4: 2^-e from the E8M0 code (code = e + 127, 0..254); code 254 gives the
+// subnormal 2^-127.
+__device__ __forceinline__ float mx_inv(uint32_t code) {
+    return __uint_as_float(code < 254u ? (254u - code) << 23 : 0x00400000u);
+}
+
+// ---------------------------------------------------------------- Philox4x32-10
+// Salmon et al., SC'11: ten rounds of two 32x32->64 products with the published
+// multipliers, Weyl-sequence key schedule.
+struct u32x4 { uint32_t w[4]; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                               uint32_t key0, uint32_t key1) {
+    #pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t a = (uint64_t)x0 * 0xD2511F53u;
+        const uint64_t b = (uint64_t)x2 * 0xCD9E8D57u;
+        const uint32_t y0 = (uint32_t)(b >> 32) ^ x1 ^ key0;
+        const uint32_t y2 = (uint32_t)(a >> 32) ^ x3 ^ key1;
+        x1 = (uint32_t)b;
+        x3 = (uint32_t)a;
+        x0 = y0;
+        x2 = y2;
+        key0 += 0x9E3779B9u;
+        key1 += 0xBB67AE85u;
+    }
+    u32x4 r;
+    r.w[0] = x0; r.w[1] = x1; r.w[2] = x2; r.w[3] = x3;
+    return r;
+}
+
+// ---------------------------------------------------------------- bit helpers
+
+// 8 bits -> bit 4j of a dword (nibble LSBs).
+__device__ __forceinline__ uint32_t spread8_to_nibbles(uint32_t b) {
+    b &= 0xFFu;
+    b = (b | (b << 12)) & 0x000F000Fu;
+    b = (b | (b << 6)) & 0x03030303u;
+    b = (b | (b << 3)) & 0x11111111u;
+    return b;
+}
+
+// bit 4j of a dword -> 8 contiguous bits.
+__device__ __forceinline__ uint32_t gather_nibble_lsbs(uint32_t w) {
+    uint32_t x = w & 0x11111111u;
+    x = (x | (x >> 3)) & 0x03030303u;
+    x = (x | (x >> 6)) & 0x000F000Fu;
+    x = (x | (x >> 12)) & 0xFFu;
+    return x;
+}
+
+// ---------------------------------------------------------------- E2M1 converts
+
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_rne2(uint32_t old, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Truncating convert of two values; only byte 0 of the result is defined (the
+// builtin does not merge into an old destination value, unlike the RNE form).
+__device__ __forceinline__ uint32_t cvt_trunc2_b0(float a, float b) {
+    v2f x = {a, b};
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, 0u, 1.0f, 0) & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t pack_rne8(const float v[8]) {
+    uint32_t w = 0;
+    w = cvt_rne2<0>(w, v[0], v[1]);
+    w = cvt_rne2<1>(w, v[2], v[3]);
+    w = cvt_rne2<2>(w, v[4], v[5]);
+    w = cvt_rne2<3>(w, v[6], v[7]);
+    return w;
+}
+
+__device__ __forceinline__ uint32_t pack_trunc8(const float v[8]) {
+    return cvt_trunc2_b0(v[0], v[1]) | (cvt_trunc2_b0(v[2], v[3]) << 8) |
+           (cvt_trunc2_b0(v[4], v[5]) << 16) | (cvt_trunc2_b0(v[6], v[7]) << 24);
+}
+
+__device__ __forceinline__ uint32_t sign_nibble(float v) { return (__float_as_uint(v) >> 28) & 8u; }
+
+// ---------------------------------------------------------------- encoders
+// v[j]: signed scaled values RN(y_j * inv).  Grid 0 = E2M1, 1 = uniform.
+
+enum { MODE_RTN = 0, MODE_SR = 1, MODE_GUIDED = 2 };
+
+// Guided E2M1: L = truncation codes (lower bracket member, with sign).  A
+// value lies on a codeword exactly when truncating the next smaller magnitude
+// gives a different code (for +-0 that value is a NaN pattern, which the
+// convert maps to a saturated code, also different).  Off the grid, the upper
+// member is L+1 (never carries into the sign: k_lo <= 6 there); it is taken
+// when the LSB of L differs from the guide bit.
+__device__ __forceinline__ uint32_t encode8_guided_e2m1(const float v[8], uint32_t gbits) {
+    float vd[8];
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float c = __builtin_amdgcn_fmed3f(v[j], -6.0f, 6.0f);
+        vd[j] = __uint_as_float(__float_as_uint(c) - 1u);
+    }
+    const uint32_t L = pack_trunc8(v);
+    const uint32_t Ld = pack_trunc8(vd);
+    uint32_t d = L ^ Ld;
+    d |= d >> 1;
+    d |= d >> 2;
+    const uint32_t on_grid = d & 0x11111111u;
+    const uint32_t mism = (L ^ spread8_to_nibbles(gbits)) & 0x11111111u;
+    return L + (mism & ~on_grid);
+}
+
+// SR E2M1: the grid is uniform with step 0.5, 1, 2 on [0,2), [2,4), [4,6].
+// r = vc / step (exact) and the element rounds up iff frac(r) > c with
+// c = (2u+1)/512; equivalently k = base + ceil(r - c) (r - c is exact
+// wherever it matters).
+__device__ __forceinline__ uint32_t encode1_sr_e2m1(float v, uint32_t u) {
+    const float vc = fminf(fabsf(v), 6.0f);
+    const int e = (int)(__float_as_uint(vc) >> 23);
+    const int q = min(max(e - 127, 0), 2);            // 0, 1, 2 for the three step sizes
+    const float r = __builtin_ldexpf(vc, 1 - q);
+    const float c = __builtin_fmaf((float)u, 0.00390625f, 0.001953125f);
+    const int k = (int)__builtin_ceilf(r - c) + 2 * q;
+    return (uint32_t)k | sign_nibble(v);
+}
+
+__device__ __forceinline__ uint32_t encode1_rtn_uniform(float v) {
+    const float vc = fminf(fabsf(v), 7.0f);
+    const uint32_t k = __float_as_uint(vc + 8388608.0f) - 0x4B000000u;   // RNE to integer
+    return k | sign_nibble(v);
+}
+
+__device__ __forceinline__ uint32_t encode1_sr_uniform(float v, uint32_t u) {
+    const float vc = fminf(fabsf(v), 7.0f);
+    const float c = __builtin_fmaf((float)u, 0.00390625f, 0.001953125f);
+    const int k = (int)__builtin_ceilf(vc - c);
+    return (uint32_t)k | sign_nibble(v);
+}
+
+__device__ __forceinline__ uint32_t encode1_guided_uniform(float v, uint32_t b) {
+    const float vc = fminf(fabsf(v), 7.0f);
+    const float fl = __builtin_floorf(vc);
+    const uint32_t klo = (uint32_t)fl;
+    const uint32_t off = vc != fl ? 1u : 0u;
+    const uint32_t k = klo + (((klo ^ b) & 1u) & off);
+    return k | sign_nibble(v);
+}
+
+// rnd: 8 random bytes for SR (rnd0 bytes 0..3 -> elements 0..3, rnd1 -> 4..7);
+// gbits: 8 guide bits for guided.
+template <int GRID, int MODE>
+__device__ __forceinline__ uint32_t encode8(const float v[8], uint32_t rnd0, uint32_t rnd1,
+                                            uint32_t gbits) {
+    if constexpr (GRID == 0 && MODE == MODE_RTN) {
+        return pack_rne8(v);
+    } else if constexpr (GRID == 0 && MODE == MODE_GUIDED) {
+        return encode8_guided_e2m1(v, gbits);
+    } else {
+        uint32_t w = 0;
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t u = ((j < 4 ? rnd0 : rnd1) >> (8 * (j & 3))) & 0xFFu;
+            uint32_t nib;
+            if constexpr (GRID == 0) nib = encode1_sr_e2m1(v[j], u);
+            else if constexpr (MODE == MODE_RTN) nib = encode1_rtn_uniform(v[j]);
+            else if constexpr (MODE == MODE_SR) nib = encode1_sr_uniform(v[j], u);
+            else nib = encode1_guided_uniform(v[j], (gbits >> j) & 1u);
+            w |= nib << (4 * j);
+        }
+        return w;
+    }
+}
+
+// ---------------------------------------------------------------- RHT16
+// Sylvester-ordered butterfly, stages h = 1, 2, 4, 8, each sum rounded to fp32.
+__device__ __forceinline__ void butterfly16(float a[16]) {
+    #pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+        #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i & h) continue;
+            const float s = a[i] + a[i + h];
+            const float d = a[i] - a[i + h];
+            a[i] = s;
+            a[i + h] = d;
+        }
+    }
+}
+
+// Sign mask of the RHT diagonal: bit j of word 0 of Philox(key = seed, counter (0,0,1,0)).
+__device__ __forceinline__ uint32_t rht_sign_mask(uint64_t seed) {
+    return philox4x32_10(0u, 0u, 1u, 0u, (uint32_t)seed, (uint32_t)(seed >> 32)).w[0] & 0xFFFFu;
+}
+
+// 16 bf16 (8 dwords) -> fp32, with optional forward RHT (signs first).
+template <bool RHT>
+__device__ __forceinline__ void widen16(const uint32_t w[8], uint32_t signs, float y[16]) {
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        y[2 * j] = bf16_lo(w[j]);
+        y[2 * j + 1] = bf16_hi(w[j]);
+    }
+    if constexpr (RHT) {
+        #pragma unroll
+        for (int j = 0; j < 16; ++j)
+            y[j] = __uint_as_float(__float_as_uint(y[j]) ^ (((signs >> j) & 1u) << 31));
+        butterfly16(y);
+        #pragma unroll
+        for (int j = 0; j < 16; ++j) y[j] = y[j] * 0.25f;
+    }
+}
+
+// Largest |bf16| bit pattern of 16 values (8 dwords) with sign bits cleared;
+// >= 0x7F80 means the group holds a non-finite value.  Packed 16-bit max.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t amax_bits16(const uint32_t w[8]) {
+    u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+    #pragma unroll
+    for (int j = 1; j < 8; ++j)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu));
+    return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+}  // namespace fp4q

@@ -1,0 +1,102 @@
+// internal.h -- kernel parameter blocks and launchers shared between the C ABI
+// (abi.hip) and the kernel translation units.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+// Threads per workgroup for every kernel of the library.
+constexpr int kThreads = 256;
+
+// Unsigned division by a runtime constant d (1 <= d < 2^31):
+// q = (mulhi(n, m) + n) >> l with l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    uint64_t m = ((((1ull << l) - d) << 32) / d) + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
+    uint64_t t = __umulhi(n, f.m);
+    return (uint32_t)((t + n) >> f.l);
+}
+
+// 16-element groups are the work unit: group g covers elements 16g..16g+15 of
+// the logical row-major order (rows*cols/16 groups; a row holds cols/16).
+struct QuantParams {
+    const uint16_t* x;          // bf16 input, row stride ld elements
+    int64_t ld;
+    uint32_t ngroups;
+    FastDiv gpr;                // groups per row
+    const float* ts;            // NVFP4 tensor scale (device), or guide tensor scale
+    uint8_t* codes;
+    uint8_t* scales;
+    uint8_t* bits_out;          // fused guide emission (RTN / SR), may be null
+    const uint8_t* gbits;       // guided: guide bitplane
+    const uint8_t* gscales;     // guided: guide scales
+    uint32_t key0, key1;        // SR Philox key
+    uint64_t sr_offset;         // SR counter offset (groups)
+    uint64_t rht_seed;          // RHT: Philox key of the sign diagonal
+};
+
+struct DequantParams {
+    const uint8_t* codes;
+    const uint8_t* scales;
+    const float* ts;
+    void* out;
+    int64_t ld_out;
+    uint32_t ngroups;
+    FastDiv gpr;
+};
+
+struct GuideParams {
+    const uint8_t* in;          // pack: codes;  unpack: guide bits
+    const uint8_t* scales_in;
+    uint8_t* out;               // pack: guide bits;  unpack: 0/1 bytes
+    uint8_t* scales_out;
+    uint32_t ngroups;
+};
+
+struct RhtParams {
+    const uint16_t* x;
+    int64_t ld;
+    void* out;
+    uint32_t ngroups;
+    FastDiv gpr;
+    uint64_t seed;              // Philox key of the sign diagonal
+};
+
+struct AmaxParams {
+    const uint16_t* x;
+    int64_t ld;
+    uint32_t ngroups;
+    FastDiv gpr;
+    uint64_t rht_seed;
+    float* acc;                 // receives max finite |y| (as bits, atomic max)
+};
+
+struct EncodeParams {
+    const float* v;
+    const uint8_t* aux;
+    uint8_t* out;
+    uint32_t n8;                // number of 8-element units
+};
+
+// Launchers (return hipGetLastError() of the launch).
+hipError_t launch_quantize(int format, int grid, int mode, bool rht, bool emit, bool contig,
+                           const QuantParams& p, hipStream_t s);
+hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams& p, hipStream_t s);
+hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantParams& p,
+                             hipStream_t s);
+hipError_t launch_guide_pack(int format, const GuideParams& p, hipStream_t s);
+hipError_t launch_guide_unpack(int format, const GuideParams& p, hipStream_t s);
+hipError_t launch_rht16(bool inverse, bool bf16_out, bool contig, const RhtParams& p, hipStream_t s);
+hipError_t launch_encode_values(int grid, int mode, const EncodeParams& p, hipStream_t s);
+
+}  // namespace fp4q

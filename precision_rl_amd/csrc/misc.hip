@@ -1,0 +1,294 @@
+// misc.hip -- tensor scale, dequantization, guide pack/unpack, standalone RHT16
+// and the element-encode entry, for gfx950.  Same work unit as quantize.hip:
+// one lane per 16-element group.
+#include "device.h"
+#include "internal.h"
+
+namespace fp4q {
+
+namespace {
+
+__device__ __forceinline__ int64_t row_offset(uint32_t g, FastDiv gpr, int64_t ld) {
+    const uint32_t row = fastdiv(g, gpr);
+    const uint32_t cg = g - row * gpr.d;
+    return (int64_t)row * ld + (int64_t)cg * 16;
+}
+
+// ---------------------------------------------------------------- tensor scale
+// amax over finite |y| as fp32 bits (order-preserving for non-negative values),
+// reduced per wave and merged with one atomic max per wave.
+
+__global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
+
+template <bool RHT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
+    uint32_t m = 0;
+    const uint32_t signs = RHT ? rht_sign_mask(p.rht_seed) : 0u;
+    const uint32_t stride = gridDim.x * kThreads;
+    for (uint32_t g = blockIdx.x * kThreads + threadIdx.x; g < p.ngroups; g += stride) {
+        const int64_t off = CONTIG ? (int64_t)g * 16 : row_offset(g, p.gpr, p.ld);
+        const uint4* src = reinterpret_cast<const uint4*>(p.x + off);
+        const uint4 a = src[0], b = src[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        if constexpr (RHT) {
+            float y[16];
+            widen16<true>(w, signs, y);
+            #pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t k = __float_as_uint(y[j]) & 0x7FFFFFFFu;
+                m = k < 0x7F800000u ? max(m, k) : m;
+            }
+        } else {
+            #pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+                m = lo < 0x7F80u ? max(m, lo << 16) : m;
+                m = hi < 0x7F80u ? max(m, hi << 16) : m;
+            }
+        }
+    }
+    #pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(reinterpret_cast<unsigned int*>(p.acc), m);
+}
+
+__global__ void k_ts_finalize(float* acc, float gmax448) {
+    const float a = *acc;                     // amax (bits were accumulated in place)
+    *acc = a == 0.0f ? 1.0f : a / gmax448;
+}
+
+// ---------------------------------------------------------------- dequantize
+// G[k] with sign: E2M1 via the hardware decode (exact), uniform via integers.
+template <int GRID>
+__device__ __forceinline__ void decode8(uint32_t w, float g[8]) {
+    if constexpr (GRID == 0) {
+        v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+        v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+        v2f c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+        v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        g[0] = a[0]; g[1] = a[1]; g[2] = b[0]; g[3] = b[1];
+        g[4] = c[0]; g[5] = c[1]; g[6] = d[0]; g[7] = d[1];
+    } else {
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t nib = (w >> (4 * j)) & 0xFu;
+            g[j] = __uint_as_float(__float_as_uint((float)(nib & 7u)) | ((nib & 8u) << 28));
+        }
+    }
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT, int GRID, bool BF16>
+__global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) {
+    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+    if (g >= p.ngroups) return;
+    const uint2 c = reinterpret_cast<const uint2*>(p.codes)[g];
+    const uint32_t sc = p.scales[FMT == 0 ? g : (g >> 1)];
+    float v[16];
+    decode8<GRID>(c.x, v);
+    decode8<GRID>(c.y, v + 8);
+    bool nan;
+    if constexpr (FMT == 0) {
+        nan = (sc & 0x7Fu) == 0x7Fu;
+        const float d = e4m3_decode(sc);
+        const float ts = *p.ts;
+        #pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = (v[j] * d) * ts;   // G*d is exact
+    } else {
+        nan = sc == 0xFFu;
+        const float s2 = __uint_as_float(sc ? sc << 23 : 0x00400000u);  // 2^(sc-127)
+        #pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = v[j] * s2;
+    }
+    const int64_t off = row_offset(g, p.gpr, p.ld_out);
+    if constexpr (BF16) {
+        uint32_t o[8];
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            bf16x2 h = __builtin_convertvector((v2f){v[2 * j], v[2 * j + 1]}, bf16x2);
+            o[j] = nan ? 0x7FC07FC0u : __builtin_bit_cast(uint32_t, h);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + off);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+        uint32_t o[16];
+        #pragma unroll
+        for (int j = 0; j < 16; ++j) o[j] = nan ? 0x7FC00000u : __float_as_uint(v[j]);
+        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<float*>(p.out) + off);
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    }
+}
+
+// ---------------------------------------------------------------- guide pack / unpack
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_guide_pack(const GuideParams p) {
+    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+    if (g >= p.ngroups) return;
+    const uint2 c = reinterpret_cast<const uint2*>(p.in)[g];
+    reinterpret_cast<uint16_t*>(p.out)[g] =
+        (uint16_t)(gather_nibble_lsbs(c.x) | (gather_nibble_lsbs(c.y) << 8));
+    if (FMT == 0) p.scales_out[g] = p.scales_in[g];
+    else if ((g & 1u) == 0) p.scales_out[g >> 1] = p.scales_in[g >> 1];
+}
+
+__device__ __forceinline__ uint32_t bits4_to_bytes(uint32_t b) {
+    return ((b & 0xFu) * 0x00204081u) & 0x01010101u;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_guide_unpack(const GuideParams p) {
+    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+    if (g >= p.ngroups) return;
+    const uint32_t b = reinterpret_cast<const uint16_t*>(p.in)[g];
+    reinterpret_cast<uint4*>(p.out)[g] =
+        make_uint4(bits4_to_bytes(b), bits4_to_bytes(b >> 4), bits4_to_bytes(b >> 8), bits4_to_bytes(b >> 12));
+    if (FMT == 0) p.scales_out[g] = p.scales_in[g];
+    else if ((g & 1u) == 0) p.scales_out[g >> 1] = p.scales_in[g >> 1];
+}
+
+// ---------------------------------------------------------------- RHT16
+
+template <bool INVERSE, bool BF16, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void k_rht16(const RhtParams p) {
+    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+    if (g >= p.ngroups) return;
+    const uint32_t signs = rht_sign_mask(p.seed);
+    const int64_t off = CONTIG ? (int64_t)g * 16 : row_offset(g, p.gpr, p.ld);
+    const uint4* src = reinterpret_cast<const uint4*>(p.x + off);
+    const uint4 a = src[0], b = src[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float y[16];
+    if constexpr (INVERSE) {
+        widen16<false>(w, 0u, y);
+        butterfly16(y);
+        #pragma unroll
+        for (int j = 0; j < 16; ++j)
+            y[j] = __uint_as_float(__float_as_uint(y[j] * 0.25f) ^ (((signs >> j) & 1u) << 31));
+    } else {
+        widen16<true>(w, signs, y);
+    }
+    if constexpr (BF16) {
+        uint32_t o[8];
+        #pragma unroll
+        for (int j = 0; j < 8; ++j)
+            o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){y[2 * j], y[2 * j + 1]}, bf16x2));
+        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (int64_t)g * 16);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<float*>(p.out) + (int64_t)g * 16);
+        #pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dst[q] = make_uint4(__float_as_uint(y[4 * q]), __float_as_uint(y[4 * q + 1]),
+                                __float_as_uint(y[4 * q + 2]), __float_as_uint(y[4 * q + 3]));
+    }
+}
+
+// ---------------------------------------------------------------- element encode
+
+template <int GRID, int MODE>
+__global__ __launch_bounds__(kThreads) void k_encode_values(const EncodeParams p) {
+    const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
+    if (t >= p.n8) return;
+    const float4* src = reinterpret_cast<const float4*>(p.v) + 2 * (int64_t)t;
+    const float4 a = src[0], b = src[1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t r0 = 0, r1 = 0, gbits = 0;
+    if (p.aux) {
+        const uint2 x = reinterpret_cast<const uint2*>(p.aux)[t];
+        r0 = x.x;
+        r1 = x.y;
+        // the LSB of each of the 8 aux bytes -> bits 0..7
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) gbits |= (((j < 4 ? x.x : x.y) >> (8 * (j & 3))) & 1u) << j;
+    }
+    const uint32_t w = encode8<GRID, MODE>(v, r0, r1, gbits);
+    const uint32_t lo = (w & 0xFu) | ((w >> 4) & 0xFu) << 8 | ((w >> 8) & 0xFu) << 16 | ((w >> 12) & 0xFu) << 24;
+    const uint32_t hi = ((w >> 16) & 0xFu) | ((w >> 20) & 0xFu) << 8 | ((w >> 24) & 0xFu) << 16 | ((w >> 28) & 0xFu) << 24;
+    reinterpret_cast<uint2*>(p.out)[t] = make_uint2(lo, hi);
+}
+
+inline uint32_t blocks_for(uint32_t n) { return (n + kThreads - 1) / kThreads; }
+
+}  // namespace
+
+hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, reinterpret_cast<uint32_t*>(p.acc), 0u);
+    uint32_t blocks = blocks_for(p.ngroups);
+    if (blocks > 4096) blocks = 4096;
+    if (blocks > 0) {
+        if (rht) {
+            if (contig) hipLaunchKernelGGL((k_amax<true, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((k_amax<true, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+        } else {
+            if (contig) hipLaunchKernelGGL((k_amax<false, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((k_amax<false, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+        }
+    }
+    hipLaunchKernelGGL(k_ts_finalize, dim3(1), dim3(1), 0, s, p.acc, grid == 0 ? 2688.0f : 3136.0f);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantParams& p, hipStream_t s) {
+    const dim3 b(blocks_for(p.ngroups)), t(kThreads);
+#define FP4Q_DQ(F, G, B) hipLaunchKernelGGL((k_dequantize<F, G, B>), b, t, 0, s, p)
+    if (format == 0) {
+        if (grid == 0) { if (bf16_out) FP4Q_DQ(0, 0, true); else FP4Q_DQ(0, 0, false); }
+        else { if (bf16_out) FP4Q_DQ(0, 1, true); else FP4Q_DQ(0, 1, false); }
+    } else {
+        if (grid == 0) { if (bf16_out) FP4Q_DQ(1, 0, true); else FP4Q_DQ(1, 0, false); }
+        else { if (bf16_out) FP4Q_DQ(1, 1, true); else FP4Q_DQ(1, 1, false); }
+    }
+#undef FP4Q_DQ
+    return hipGetLastError();
+}
+
+hipError_t launch_guide_pack(int format, const GuideParams& p, hipStream_t s) {
+    const dim3 b(blocks_for(p.ngroups)), t(kThreads);
+    if (format == 0) hipLaunchKernelGGL(k_guide_pack<0>, b, t, 0, s, p);
+    else hipLaunchKernelGGL(k_guide_pack<1>, b, t, 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_guide_unpack(int format, const GuideParams& p, hipStream_t s) {
+    const dim3 b(blocks_for(p.ngroups)), t(kThreads);
+    if (format == 0) hipLaunchKernelGGL(k_guide_unpack<0>, b, t, 0, s, p);
+    else hipLaunchKernelGGL(k_guide_unpack<1>, b, t, 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_rht16(bool inverse, bool bf16_out, bool contig, const RhtParams& p, hipStream_t s) {
+    const dim3 b(blocks_for(p.ngroups)), t(kThreads);
+#define FP4Q_RH(I, B, C) hipLaunchKernelGGL((k_rht16<I, B, C>), b, t, 0, s, p)
+    if (inverse) {
+        if (bf16_out) { if (contig) FP4Q_RH(true, true, true); else FP4Q_RH(true, true, false); }
+        else { if (contig) FP4Q_RH(true, false, true); else FP4Q_RH(true, false, false); }
+    } else {
+        if (bf16_out) { if (contig) FP4Q_RH(false, true, true); else FP4Q_RH(false, true, false); }
+        else { if (contig) FP4Q_RH(false, false, true); else FP4Q_RH(false, false, false); }
+    }
+#undef FP4Q_RH
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_values(int grid, int mode, const EncodeParams& p, hipStream_t s) {
+    const dim3 b(blocks_for(p.n8)), t(kThreads);
+#define FP4Q_EV(G, M) hipLaunchKernelGGL((k_encode_values<G, M>), b, t, 0, s, p)
+    if (grid == 0) {
+        if (mode == MODE_RTN) FP4Q_EV(0, MODE_RTN);
+        else if (mode == MODE_SR) FP4Q_EV(0, MODE_SR);
+        else FP4Q_EV(0, MODE_GUIDED);
+    } else {
+        if (mode == MODE_RTN) FP4Q_EV(1, MODE_RTN);
+        else if (mode == MODE_SR) FP4Q_EV(1, MODE_SR);
+        else FP4Q_EV(1, MODE_GUIDED);
+    }
+#undef FP4Q_EV
+    return hipGetLastError();
+}
+
+}  // namespace fp4q

@@ -1,0 +1,256 @@
+"""Thin ctypes binding of libfp4q (include/fp4q.h) over torch device tensors.
+
+Argument marshalling only: shapes, strides, pointers and the current HIP
+stream are passed to the C ABI, outputs are allocated with torch when the
+caller does not provide them, and every computation runs in the library's
+gfx950 kernels.  There is no fallback: if the library is missing or the
+tensors are not on a GPU, the call raises.
+
+Function names follow the C ABI (fp4_quantize, fp4_quantize_guided,
+fp4_dequantize, guide_pack, guide_unpack, fp4_rht16, fp4_tensor_scale,
+fp4_encode_values).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4q.so")
+
+NVFP4, MXFP4 = 0, 1
+E2M1, UNIFORM = 0, 1
+RTN, SR = 0, 1
+MODE_RTN, MODE_SR, MODE_GUIDED = 0, 1, 2
+OUT_F32, OUT_BF16 = 0, 1
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: status {status}: {msg}")
+        self.status = status
+
+
+class _CCfg(C.Structure):
+    _fields_ = [("format", C.c_int32), ("grid", C.c_int32), ("rounding", C.c_int32),
+                ("rht16", C.c_int32), ("sr_seed", C.c_uint64), ("sr_offset", C.c_uint64),
+                ("rht_seed", C.c_uint64)]
+
+
+@dataclass
+class Fp4Config:
+    """Mirror of fp4_cfg."""
+    format: int = NVFP4
+    grid: int = E2M1
+    rounding: int = RTN
+    rht16: bool = False
+    sr_seed: int = 0
+    sr_offset: int = 0
+    rht_seed: int = 0
+
+    @property
+    def block(self) -> int:
+        return 32 if self.format == MXFP4 else 16
+
+    def c(self) -> _CCfg:
+        return _CCfg(self.format, self.grid, self.rounding, int(bool(self.rht16)), self.sr_seed,
+                     self.sr_offset, self.rht_seed)
+
+
+_lib = None
+EXPORTS = ("fp4_tensor_scale", "fp4_quantize", "fp4_quantize_guided", "fp4_dequantize", "guide_pack",
+           "guide_unpack", "fp4_rht16", "fp4_encode_values", "fp4_codes_bytes", "fp4_scales_bytes",
+           "fp4_guide_bytes", "fp4_status_str", "fp4_last_error")
+
+
+def lib():
+    """Load libfp4q.so (built in-tree by ``precision_rl_amd/build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python precision_rl_amd/build.py` "
+                          "(there is no CPU fallback)")
+    L = C.CDLL(LIB_PATH)
+    P, I64, I = C.c_void_p, C.c_int64, C.c_int
+    CP = C.POINTER(_CCfg)
+    sigs = {
+        "fp4_tensor_scale": [CP, P, I64, I64, I64, P, P],
+        "fp4_quantize": [CP, P, I64, I64, I64, P, P, P, P, P],
+        "fp4_quantize_guided": [CP, P, I64, I64, I64, P, P, P, P, P, P],
+        "fp4_dequantize": [CP, P, P, P, I64, I64, P, I64, I, P],
+        "guide_pack": [CP, P, P, I64, I64, P, P, P],
+        "guide_unpack": [CP, P, P, I64, I64, P, P, P],
+        "fp4_rht16": [P, I64, I64, I64, C.c_uint64, I, P, I, P],
+        "fp4_encode_values": [I, I, P, P, I64, P, P],
+    }
+    for name, args in sigs.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = C.c_int
+    for name in ("fp4_codes_bytes",):
+        getattr(L, name).argtypes = [I64, I64]
+        getattr(L, name).restype = C.c_size_t
+    for name in ("fp4_scales_bytes", "fp4_guide_bytes"):
+        getattr(L, name).argtypes = [I, I64, I64]
+        getattr(L, name).restype = C.c_size_t
+    L.fp4_status_str.argtypes = [I]
+    L.fp4_status_str.restype = C.c_char_p
+    L.fp4_last_error.argtypes = []
+    L.fp4_last_error.restype = C.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise Fp4Error(status, where, lib().fp4_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _on_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("fp4q tensors must be on a GPU device (no CPU path)")
+
+
+def _matrix(x: torch.Tensor):
+    """(rows, cols, ld) of a 2-D bf16 tensor with unit column stride."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("expected a 2-D bfloat16 tensor")
+    rows, cols = x.shape
+    if cols > 1 and x.stride(1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    ld = x.stride(0) if rows > 1 else cols
+    return rows, cols, ld
+
+
+def _u8(n: int, like: torch.Tensor) -> torch.Tensor:
+    return torch.empty(n, dtype=torch.uint8, device=like.device)
+
+
+# ---------------------------------------------------------------- entry points
+def fp4_tensor_scale(x: torch.Tensor, cfg: Fp4Config, out: torch.Tensor | None = None) -> torch.Tensor:
+    _on_gpu(x, out)
+    rows, cols, ld = _matrix(x)
+    out = torch.empty(1, dtype=torch.float32, device=x.device) if out is None else out
+    c = cfg.c()
+    _check(lib().fp4_tensor_scale(C.byref(c), _ptr(x), rows, cols, ld, _ptr(out), _stream(x)),
+           "fp4_tensor_scale")
+    return out
+
+
+def fp4_quantize(x: torch.Tensor, cfg: Fp4Config, tensor_scale: torch.Tensor | None = None,
+                 emit: bool = False, codes=None, scales=None, bits=None):
+    """Returns (codes, scales) or (codes, scales, guide_bits) when ``emit``."""
+    _on_gpu(x, tensor_scale, codes, scales, bits)
+    rows, cols, ld = _matrix(x)
+    n = rows * cols
+    codes = _u8(n // 2, x) if codes is None else codes
+    scales = _u8(n // cfg.block, x) if scales is None else scales
+    if emit and bits is None:
+        bits = _u8(n // 8, x)
+    c = cfg.c()
+    _check(lib().fp4_quantize(C.byref(c), _ptr(x), rows, cols, ld, _ptr(tensor_scale), _ptr(codes),
+                              _ptr(scales), _ptr(bits) if emit else None, _stream(x)), "fp4_quantize")
+    return (codes, scales, bits) if emit else (codes, scales)
+
+
+def fp4_quantize_guided(x: torch.Tensor, cfg: Fp4Config, guide_bits: torch.Tensor,
+                        guide_scales: torch.Tensor, guide_tensor_scale: torch.Tensor | None = None,
+                        codes=None, scales=None):
+    _on_gpu(x, guide_bits, guide_scales, guide_tensor_scale, codes, scales)
+    rows, cols, ld = _matrix(x)
+    n = rows * cols
+    codes = _u8(n // 2, x) if codes is None else codes
+    scales = _u8(n // cfg.block, x) if scales is None else scales
+    c = cfg.c()
+    _check(lib().fp4_quantize_guided(C.byref(c), _ptr(x), rows, cols, ld, _ptr(guide_bits),
+                                     _ptr(guide_scales), _ptr(guide_tensor_scale), _ptr(codes),
+                                     _ptr(scales), _stream(x)), "fp4_quantize_guided")
+    return codes, scales
+
+
+def fp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, cfg: Fp4Config, rows: int, cols: int,
+                   tensor_scale: torch.Tensor | None = None, dtype=torch.bfloat16,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    _on_gpu(codes, scales, tensor_scale, out)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=dtype, device=codes.device)
+    ld_out = out.stride(0) if rows > 1 else cols
+    kind = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("dequantize output must be bfloat16 or float32")
+    c = cfg.c()
+    _check(lib().fp4_dequantize(C.byref(c), _ptr(codes), _ptr(scales), _ptr(tensor_scale), rows, cols,
+                                _ptr(out), ld_out, kind, _stream(codes)), "fp4_dequantize")
+    return out
+
+
+def guide_pack(codes: torch.Tensor, scales: torch.Tensor, cfg: Fp4Config, rows: int, cols: int,
+               bits=None, gscales=None):
+    _on_gpu(codes, scales, bits, gscales)
+    n = rows * cols
+    bits = _u8(n // 8, codes) if bits is None else bits
+    gscales = _u8(n // cfg.block, codes) if gscales is None else gscales
+    c = cfg.c()
+    _check(lib().guide_pack(C.byref(c), _ptr(codes), _ptr(scales), rows, cols, _ptr(bits), _ptr(gscales),
+                            _stream(codes)), "guide_pack")
+    return bits, gscales
+
+
+def guide_unpack(bits: torch.Tensor, gscales: torch.Tensor, cfg: Fp4Config, rows: int, cols: int,
+                 mant=None, scales_out=None):
+    _on_gpu(bits, gscales, mant, scales_out)
+    n = rows * cols
+    mant = _u8(n, bits) if mant is None else mant
+    scales_out = _u8(n // cfg.block, bits) if scales_out is None else scales_out
+    c = cfg.c()
+    _check(lib().guide_unpack(C.byref(c), _ptr(bits), _ptr(gscales), rows, cols, _ptr(mant),
+                              _ptr(scales_out), _stream(bits)), "guide_unpack")
+    return mant, scales_out
+
+
+def fp4_rht16(x: torch.Tensor, seed: int, inverse: bool = False, dtype=torch.float32,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    _on_gpu(x, out)
+    rows, cols, ld = _matrix(x)
+    out = torch.empty((rows, cols), dtype=dtype, device=x.device) if out is None else out
+    kind = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    _check(lib().fp4_rht16(_ptr(x), rows, cols, ld, seed, int(inverse), _ptr(out), kind, _stream(x)),
+           "fp4_rht16")
+    return out
+
+
+def fp4_encode_values(v: torch.Tensor, grid: int, mode: int, aux: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    _on_gpu(v, aux, out)
+    if v.dtype != torch.float32 or not v.is_contiguous():
+        raise ValueError("v must be a contiguous float32 tensor")
+    n = v.numel()
+    out = _u8(n, v) if out is None else out
+    _check(lib().fp4_encode_values(grid, mode, _ptr(v), _ptr(aux), n, _ptr(out), _stream(v)),
+           "fp4_encode_values")
+    return out
+
+
+def codes_bytes(rows: int, cols: int) -> int:
+    return lib().fp4_codes_bytes(rows, cols)
+
+
+def scales_bytes(fmt: int, rows: int, cols: int) -> int:
+    return lib().fp4_scales_bytes(fmt, rows, cols)
+
+
+def guide_bytes(fmt: int, rows: int, cols: int) -> int:
+    return lib().fp4_guide_bytes(fmt, rows, cols)

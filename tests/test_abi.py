@@ -1,0 +1,96 @@
+"""The C-ABI library loads and exports every entry point its header declares;
+argument errors are reported on the host before any launch (CPU only: none of
+these calls reaches the GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4q.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:[A-Za-z_][\w\s\*]*?)\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in {"if", "defined"}))
+
+
+@pytest.fixture(scope="module")
+def fq():
+    from precision_rl_amd import fp4q, build
+    if build.stale():
+        build.build()
+    fq_lib = fp4q.lib()
+    return fp4q
+
+
+def test_header_declares_the_expected_calls():
+    names = _declared()
+    for n in ["fp4_quantize", "fp4_quantize_guided", "fp4_dequantize", "guide_pack", "guide_unpack",
+              "fp4_rht16", "fp4_tensor_scale", "fp4_encode_values", "fp4_codes_bytes",
+              "fp4_scales_bytes", "fp4_guide_bytes", "fp4_status_str", "fp4_last_error"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(fq):
+    L = fq.lib()
+    for n in _declared():
+        assert hasattr(L, n), f"libfp4q.so does not export {n}"
+    assert set(fq.EXPORTS) <= set(_declared())
+
+
+def test_size_helpers(fq):
+    assert fq.codes_bytes(4096, 2048) == 4096 * 2048 // 2
+    assert fq.scales_bytes(fq.NVFP4, 4096, 2048) == 4096 * 2048 // 16
+    assert fq.scales_bytes(fq.MXFP4, 16384, 4096) == 16384 * 4096 // 32
+    assert fq.guide_bytes(fq.NVFP4, 16, 32) == 16 * 32 // 8 + 16 * 32 // 16 + 4
+
+
+def _call_quantize(fq, cfg, x, rows, cols, ld, ts=16, codes=16, scales=16):
+    L = fq.lib()
+    c = cfg.c() if cfg is not None else None
+    return L.fp4_quantize(C.byref(c) if c is not None else None, C.c_void_p(x), rows, cols, ld,
+                          C.c_void_p(ts), C.c_void_p(codes), C.c_void_p(scales), None, None)
+
+
+def test_host_side_argument_errors(fq):
+    L = fq.lib()
+    cfg = fq.Fp4Config()
+    A = 1 << 20  # a fake, 16-byte-aligned address: never dereferenced, validation fails first
+    assert _call_quantize(fq, None, A, 4, 32, 32) == 1
+    assert "cfg" in L.fp4_last_error().decode()
+    assert _call_quantize(fq, cfg, A, 4, 24, 24) == 2            # cols % 16
+    assert _call_quantize(fq, fq.Fp4Config(format=fq.MXFP4), A, 4, 48, 48) == 2  # cols % 32
+    assert _call_quantize(fq, cfg, A, 4, 32, 16) == 2            # ld < cols
+    assert _call_quantize(fq, cfg, A, 4, 32, 36) == 3            # ld % 8
+    assert _call_quantize(fq, cfg, A + 8, 4, 32, 32) == 3        # misaligned x
+    assert _call_quantize(fq, cfg, 0, 4, 32, 32) == 1            # null x
+    assert _call_quantize(fq, cfg, A, 4, 32, 32, ts=0) == 1      # NVFP4 needs a tensor scale
+    assert _call_quantize(fq, cfg, A, -1, 32, 32) == 1
+    assert _call_quantize(fq, fq.Fp4Config(format=7), A, 4, 32, 32) == 1
+    assert _call_quantize(fq, fq.Fp4Config(rounding=3), A, 4, 32, 32) == 1
+    assert _call_quantize(fq, cfg, A, 1 << 20, 1 << 16, 1 << 16) == 2   # too many elements
+    # empty input is a no-op that succeeds without touching the device
+    assert _call_quantize(fq, cfg, 0, 0, 32, 32) == 0
+    assert _call_quantize(fq, cfg, 0, 5, 0, 0) == 0
+    assert L.fp4_status_str(3).decode().startswith("misaligned")
+    # encode_values: n % 8
+    assert L.fp4_encode_values(0, 0, C.c_void_p(A), None, 12, C.c_void_p(A), None) == 2
+    assert L.fp4_encode_values(0, 5, C.c_void_p(A), None, 16, C.c_void_p(A), None) == 1
+    # dequantize: bad dtype and ld_out
+    c = cfg.c()
+    assert L.fp4_dequantize(C.byref(c), C.c_void_p(A), C.c_void_p(A), C.c_void_p(A), 4, 32,
+                            C.c_void_p(A), 32, 9, None) == 1
+    assert L.fp4_dequantize(C.byref(c), C.c_void_p(A), C.c_void_p(A), C.c_void_p(A), 4, 32,
+                            C.c_void_p(A), 16, 0, None) == 2
+    assert L.fp4_rht16(C.c_void_p(A), 4, 40, 40, 7, 0, C.c_void_p(A), 0, None) == 2
+
+
+def test_binding_refuses_cpu_tensors(fq):
+    import torch
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fq.fp4_quantize(x, fq.Fp4Config(), torch.ones(1))

@@ -1,0 +1,284 @@
+"""GPU parity: every output of the HIP path equals the CPU oracle bit for bit.
+
+Shapes span many workgroups (one workgroup covers 512 groups of 16 elements)
+and leave ragged tails; padded row strides, empty inputs and degenerate
+blocks are included.  Floating-point outputs (tensor scale, dequantized
+values, RHT) are compared as bit patterns: tolerance 0 ulp.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from precision_rl_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fq():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from precision_rl_amd import fp4q
+    fq_lib = fp4q.lib()
+    return fp4q
+
+
+def dev(u16: np.ndarray, pad: int = 0) -> torch.Tensor:
+    """Host bf16 bit patterns -> device bf16 matrix, optionally with padded rows (ld = cols + pad)."""
+    rows, cols = u16.shape
+    t = torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16)
+    if pad:
+        buf = torch.full((rows, cols + pad), float("nan"), dtype=torch.bfloat16)
+        buf[:, :cols] = t
+        return buf.cuda()[:, :cols]
+    return t.cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def ocfg(fqc) -> O.Cfg:
+    return O.Cfg(format=fqc.format, grid=fqc.grid, rht16=fqc.rht16, rht_seed=fqc.rht_seed,
+                 sr_seed=fqc.sr_seed, sr_offset=fqc.sr_offset)
+
+
+def f32_bits(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+SHAPES = [(256, 512), (37, 544), (1, 32), (129, 96)]
+
+
+def _data(kind, rows, cols, seed):
+    if kind == "normal":
+        return W.c1_x(rows, cols, seed=seed)
+    if kind == "student":
+        return W.c2_pair(rows, cols, seed=seed)[0]
+    return W.c5_x(rows, cols, seed=seed)
+
+
+# ---------------------------------------------------------------- element encode
+
+@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_encode_values_vs_oracle(fq, grid, mode):
+    h = np.arange(0, 0x10000, dtype=np.uint32)
+    bfv = (h << 16).view(np.float32)
+    bfv = bfv[~np.isnan(bfv)]
+    gmax = 6.0 if grid == 0 else 7.0
+    near = []
+    pts = [0, .25, .5, .75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 6.5, 7, 7.5, 8] + \
+          [k + 0.5 for k in range(8)]
+    for p in pts:
+        u = np.array([p], dtype=np.float32).view(np.uint32)[0]
+        d = np.arange(-300, 301, dtype=np.int64) + int(u)
+        d = d[d >= 0].astype(np.uint32)
+        near.append(d.view(np.float32))
+    rng = np.random.default_rng(grid * 3 + mode)
+    rnd = rng.uniform(0, gmax + 1, 200_000).astype(np.float32)
+    tiny = (rng.uniform(0, 1, 20_000) * 2.0 ** rng.integers(-149, -1, 20_000)).astype(np.float32)
+    v = np.concatenate([bfv] + near + [rnd, tiny])
+    v = np.concatenate([v, -v])
+    v = v[: v.size // 8 * 8]
+    if mode == 1:
+        aux = rng.integers(0, 256, v.size, dtype=np.uint8)
+    elif mode == 2:
+        aux = rng.integers(0, 2, v.size, dtype=np.uint8)
+    else:
+        aux = None
+    out = fq.fp4_encode_values(torch.from_numpy(v).cuda(), grid, mode,
+                               None if aux is None else torch.from_numpy(aux).cuda())
+    got = host(out)
+    k = O.encode_many(grid, mode, np.abs(v), None if aux is None else aux.astype(np.uint32))
+    want = (np.signbit(v).astype(np.uint8) << 3) | k
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(v[i]), int(aux[i]) if aux is not None else None, int(got[i]), int(want[i]))
+                           for i in bad[:10]]
+
+
+# ---------------------------------------------------------------- quantize
+
+CASES = [
+    # (format, grid, rounding/mode, rht, data)
+    (0, 0, 0, False, "normal"),
+    (0, 0, 1, False, "normal"),
+    (1, 0, 0, False, "student"),
+    (1, 0, 1, False, "student"),
+    (0, 1, 0, False, "outlier"),
+    (0, 1, 1, True, "outlier"),
+    (0, 0, 0, True, "outlier"),
+    (1, 1, 1, True, "outlier"),
+    (1, 0, 0, True, "student"),
+]
+
+
+@pytest.mark.parametrize("fmt,grid,rnd,rht,data", CASES)
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("pad", [0, 24])
+def test_quantize_vs_oracle(fq, fmt, grid, rnd, rht, data, shape, pad):
+    rows, cols = shape
+    if cols % (32 if fmt else 16):
+        pytest.skip("shape not valid for this block size")
+    xh = _data(data, rows, cols, seed=rows + cols)
+    cfg = fq.Fp4Config(format=fmt, grid=grid, rounding=rnd, rht16=rht, rht_seed=7, sr_seed=0xABCDEF0123,
+                       sr_offset=3)
+    oc = ocfg(cfg)
+    x = dev(xh, pad)
+    ts_t = None
+    ts = 1.0
+    if fmt == 0:
+        ts_t = fq.fp4_tensor_scale(x, cfg)
+        ts = O.tensor_scale(oc, xh)
+        assert f32_bits(host(ts_t))[0] == f32_bits([ts])[0]
+    codes, scales, bits = fq.fp4_quantize(x, cfg, ts_t, emit=True)
+    oc_codes, oc_scales, oc_bits = O.quantize(oc, rnd, xh, ts, emit=True)
+    assert (host(scales) == oc_scales).all()
+    assert (host(codes) == oc_codes).all()
+    assert (host(bits) == oc_bits).all()
+    # without emission the codes are the same
+    c2, s2 = fq.fp4_quantize(x, cfg, ts_t)
+    assert (host(c2) == oc_codes).all() and (host(s2) == oc_scales).all()
+
+
+@pytest.mark.parametrize("fmt,grid,rht", [(0, 0, False), (1, 0, False), (0, 1, False), (1, 1, True), (0, 0, True)])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_guided_vs_oracle(fq, fmt, grid, rht, shape):
+    rows, cols = shape
+    if cols % (32 if fmt else 16):
+        pytest.skip("shape not valid for this block size")
+    x_h = W.c1_x(rows, cols, seed=11)
+    xr_h = W.c1_rollout(rows, cols, seed=11)
+    cfg = fq.Fp4Config(format=fmt, grid=grid, rht16=rht, rht_seed=7)
+    oc = ocfg(cfg)
+    xr, x = dev(xr_h), dev(x_h, pad=8)
+    ts_t = fq.fp4_tensor_scale(xr, cfg) if fmt == 0 else None
+    ts = O.tensor_scale(oc, xr_h) if fmt == 0 else 1.0
+    rc, rs = fq.fp4_quantize(xr, cfg, ts_t)
+    gb, gs = fq.guide_pack(rc, rs, cfg, rows, cols)
+    o_rc, o_rs = O.quantize(oc, O.RTN, xr_h, ts)
+    o_gb, o_gs = O.guide_pack(oc, o_rc, o_rs, rows, cols)
+    assert (host(gb) == o_gb).all() and (host(gs) == o_gs).all()
+    gc, gsc = fq.fp4_quantize_guided(x, cfg, gb, gs, ts_t)
+    o_gc, o_gsc = O.quantize(oc, O.GUIDED, x_h, ts, guide_bits=o_gb, guide_scales=o_gs)
+    assert (host(gsc) == o_gsc).all()
+    assert (host(gc) == o_gc).all()
+    # the tensor's own RTN guide reproduces RTN bit for bit
+    own_c, own_s, own_b = fq.fp4_quantize(x, cfg, ts_t, emit=True)
+    g2c, _ = fq.fp4_quantize_guided(x, cfg, own_b, own_s, ts_t)
+    assert (host(g2c) == host(own_c)).all()
+
+
+def test_special_blocks(fq):
+    x = np.zeros((2, 96), dtype=np.float32)
+    x[0, 16:32] = -0.0
+    x[0, 32] = 1000.0
+    x[0, 48:64] = np.float32(2.0 ** -130)
+    x[0, 64:80] = [0, .5, 1, 1.5, 2, 3, 4, 6, -6, -4, -3, -2, -1.5, -1, -.5, -0.]
+    x[1] = np.linspace(-3e38, 3e38, 96)
+    xh = W.f32_to_bf16_rne(x)
+    xh[0, 85] = 0x7FC0
+    xh[0, 90] = 0xFF80
+    xh[1, 5] = 0x7F80
+    for fmt in (0, 1):
+        for rht in (False, True):
+            for rnd in (0, 1):
+                cfg = fq.Fp4Config(format=fmt, rounding=rnd, rht16=rht, rht_seed=7)
+                oc = ocfg(cfg)
+                d = dev(xh)
+                ts_t = fq.fp4_tensor_scale(d, cfg) if fmt == 0 else None
+                ts = O.tensor_scale(oc, xh) if fmt == 0 else 1.0
+                if fmt == 0:
+                    assert f32_bits(host(ts_t))[0] == f32_bits([ts])[0]
+                c, s = fq.fp4_quantize(d, cfg, ts_t)
+                oc_c, oc_s = O.quantize(oc, rnd, xh, ts)
+                assert (host(s) == oc_s).all(), (fmt, rht, rnd)
+                assert (host(c) == oc_c).all(), (fmt, rht, rnd)
+
+
+def test_guided_with_nan_guide_scales(fq):
+    rows, cols = 8, 64
+    xh = W.c1_x(rows, cols, seed=2)
+    for fmt in (0, 1):
+        cfg = fq.Fp4Config(format=fmt)
+        oc = ocfg(cfg)
+        rng = np.random.default_rng(fmt)
+        gb = rng.integers(0, 256, rows * cols // 8, dtype=np.uint8)
+        gs = rng.integers(0, 256, rows * cols // cfg.block, dtype=np.uint8)
+        gs[::3] = 0x7F if fmt == 0 else 0xFF
+        ts = np.float32(0.0123)
+        tst = torch.tensor([ts], device="cuda")
+        c, s = fq.fp4_quantize_guided(dev(xh), cfg, torch.from_numpy(gb).cuda(), torch.from_numpy(gs).cuda(), tst)
+        oc_c, oc_s = O.quantize(oc, O.GUIDED, xh, float(ts), guide_bits=gb, guide_scales=gs)
+        assert (host(s) == oc_s).all() and (host(c) == oc_c).all()
+
+
+# ---------------------------------------------------------------- dequantize, guide, rht
+
+@pytest.mark.parametrize("fmt,grid", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("shape", [(256, 512), (37, 544), (3, 32)])
+def test_dequantize_vs_oracle(fq, fmt, grid, shape):
+    rows, cols = shape
+    B = 32 if fmt else 16
+    if cols % B:
+        pytest.skip("shape not valid for this block size")
+    rng = np.random.default_rng(rows)
+    codes = rng.integers(0, 256, rows * cols // 2, dtype=np.uint8)
+    scales = rng.integers(0, 256, rows * cols // B, dtype=np.uint8)
+    ts = np.float32(rng.uniform(1e-4, 3.0))
+    cfg = fq.Fp4Config(format=fmt, grid=grid)
+    oc = ocfg(cfg)
+    ct, st = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+    tst = torch.tensor([ts], device="cuda")
+    for bf16 in (False, True):
+        want = O.dequantize(oc, codes, scales, float(ts), rows, cols, out_bf16=bf16)
+        dt = torch.bfloat16 if bf16 else torch.float32
+        got = fq.fp4_dequantize(ct, st, cfg, rows, cols, tst, dtype=dt)
+        g = host(got.view(torch.int16) if bf16 else got.view(torch.int32)).reshape(-1)
+        w = want.view(np.int16 if bf16 else np.int32)
+        assert (g == w).all(), (bf16, np.nonzero(g != w)[0][:5])
+        # padded output rows
+        out = torch.zeros((rows, cols + 64), dtype=dt, device="cuda")[:, :cols]
+        fq.fp4_dequantize(ct, st, cfg, rows, cols, tst, out=out)
+        g2 = host(out.contiguous().view(torch.int16) if bf16 else out.contiguous().view(torch.int32)).reshape(-1)
+        assert (g2 == w).all()
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_guide_pack_unpack_vs_oracle(fq, fmt):
+    rows, cols = 77, 544
+    B = 32 if fmt else 16
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, rows * cols // 2, dtype=np.uint8)
+    scales = rng.integers(0, 256, rows * cols // B, dtype=np.uint8)
+    cfg = fq.Fp4Config(format=fmt)
+    oc = ocfg(cfg)
+    gb, gs = fq.guide_pack(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), cfg, rows, cols)
+    o_gb, o_gs = O.guide_pack(oc, codes, scales, rows, cols)
+    assert (host(gb) == o_gb).all() and (host(gs) == o_gs).all()
+    m, so = fq.guide_unpack(gb, gs, cfg, rows, cols)
+    o_m, o_so = O.guide_unpack(oc, o_gb, o_gs, rows, cols)
+    assert (host(m) == o_m).all() and (host(so) == o_so).all()
+
+
+@pytest.mark.parametrize("inverse", [False, True])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("pad", [0, 40])
+def test_rht16_vs_oracle(fq, inverse, bf16, pad):
+    rows, cols = 133, 256
+    xh = W.c5_x(rows, cols, seed=9)
+    out = fq.fp4_rht16(dev(xh, pad), 7, inverse=inverse, dtype=torch.bfloat16 if bf16 else torch.float32)
+    want = O.rht16(xh, 7, inverse=inverse, out_bf16=bf16)
+    g = host(out.view(torch.int16) if bf16 else out.view(torch.int32)).reshape(-1)
+    assert (g == want.view(np.int16 if bf16 else np.int32)).all()
+
+
+def test_empty_inputs(fq):
+    cfg = fq.Fp4Config()
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    ts = fq.fp4_tensor_scale(x, cfg)
+    assert host(ts)[0] == 1.0
+    c, s = fq.fp4_quantize(x, cfg, ts)
+    assert c.numel() == 0 and s.numel() == 0
