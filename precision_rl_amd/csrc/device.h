@@ -18,6 +18,39 @@
 namespace fp4q {
 
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+
+// Streaming memory access.  Inputs are read once: non-temporal loads keep them
+// from displacing reusable lines.  Outputs use non-temporal stores when
+// FP4Q_NT_STORES is set (default off: measured slower for the write-heavy kernels).
+#ifndef FP4Q_NT_STORES
+#define FP4Q_NT_STORES 0
+#endif
+
+__device__ __forceinline__ void load32_nt(const uint16_t* p, uint32_t w[8]) {
+    const v4u32* s = reinterpret_cast<const v4u32*>(p);
+    const v4u32 a = __builtin_nontemporal_load(s);
+    const v4u32 b = __builtin_nontemporal_load(s + 1);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_out(T* p, T v) {
+    if (FP4Q_NT_STORES) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+__device__ __forceinline__ void st_out2(void* base, uint32_t idx, uint32_t a, uint32_t b) {
+    v2u32 v = {a, b};
+    st_out(reinterpret_cast<v2u32*>(base) + idx, v);
+}
+
+__device__ __forceinline__ void st_out4(void* base, int64_t idx, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    v4u32 v = {a, b, c, d};
+    st_out(reinterpret_cast<v4u32*>(base) + idx, v);
+}
 
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 

@@ -20,36 +20,63 @@ __device__ __forceinline__ int64_t row_offset(uint32_t g, FastDiv gpr, int64_t l
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
+// Each lane keeps kAmaxU groups in flight per iteration of a grid-stride loop;
+// the workgroup reduces in LDS and issues one atomic max, so a launch of at
+// most kAmaxBlocks workgroups makes at most that many same-address atomics.
+constexpr int kAmaxU = 4;
+constexpr uint32_t kAmaxBlocks = 1024;
+
 template <bool RHT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
+    __shared__ uint32_t red[kThreads / 64];
     uint32_t m = 0;
     const uint32_t signs = RHT ? rht_sign_mask(p.rht_seed) : 0u;
-    const uint32_t stride = gridDim.x * kThreads;
-    for (uint32_t g = blockIdx.x * kThreads + threadIdx.x; g < p.ngroups; g += stride) {
-        const int64_t off = CONTIG ? (int64_t)g * 16 : row_offset(g, p.gpr, p.ld);
-        const uint4* src = reinterpret_cast<const uint4*>(p.x + off);
-        const uint4 a = src[0], b = src[1];
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        if constexpr (RHT) {
-            float y[16];
-            widen16<true>(w, signs, y);
-            #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t k = __float_as_uint(y[j]) & 0x7FFFFFFFu;
-                m = k < 0x7F800000u ? max(m, k) : m;
+    const uint32_t chunk = kThreads * kAmaxU;
+    for (uint32_t base = blockIdx.x * chunk; base < p.ngroups; base += gridDim.x * chunk) {
+        uint32_t w[kAmaxU][8];
+        #pragma unroll
+        for (int u = 0; u < kAmaxU; ++u) {
+            const uint32_t g = base + u * kThreads + threadIdx.x;
+            if (g < p.ngroups) {
+                const int64_t off = CONTIG ? (int64_t)g * 16 : row_offset(g, p.gpr, p.ld);
+                const uint4* src = reinterpret_cast<const uint4*>(p.x + off);
+                const uint4 a = src[0], b = src[1];
+                w[u][0] = a.x; w[u][1] = a.y; w[u][2] = a.z; w[u][3] = a.w;
+                w[u][4] = b.x; w[u][5] = b.y; w[u][6] = b.z; w[u][7] = b.w;
+            } else {
+                #pragma unroll
+                for (int j = 0; j < 8; ++j) w[u][j] = 0;
             }
-        } else {
-            #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
-                m = lo < 0x7F80u ? max(m, lo << 16) : m;
-                m = hi < 0x7F80u ? max(m, hi << 16) : m;
+        }
+        #pragma unroll
+        for (int u = 0; u < kAmaxU; ++u) {
+            if constexpr (RHT) {
+                float y[16];
+                widen16<true>(w[u], signs, y);
+                #pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t k = __float_as_uint(y[j]) & 0x7FFFFFFFu;
+                    m = k < 0x7F800000u ? max(m, k) : m;
+                }
+            } else {
+                #pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t lo = w[u][j] & 0x7FFFu, hi = (w[u][j] >> 16) & 0x7FFFu;
+                    m = lo < 0x7F80u ? max(m, lo << 16) : m;
+                    m = hi < 0x7F80u ? max(m, hi << 16) : m;
+                }
             }
         }
     }
     #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(reinterpret_cast<unsigned int*>(p.acc), m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        #pragma unroll
+        for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
+        if (m != 0) atomicMax(reinterpret_cast<unsigned int*>(p.acc), m);
+    }
 }
 
 __global__ void k_ts_finalize(float* acc, float gmax448) {
@@ -83,7 +110,7 @@ template <int FMT, int GRID, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) {
     const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
     if (g >= p.ngroups) return;
-    const uint2 c = reinterpret_cast<const uint2*>(p.codes)[g];
+    const v2u32 c = __builtin_nontemporal_load(reinterpret_cast<const v2u32*>(p.codes) + g);
     const uint32_t sc = p.scales[FMT == 0 ? g : (g >> 1)];
     float v[16];
     decode8<GRID>(c.x, v);
@@ -109,30 +136,53 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) 
             bf16x2 h = __builtin_convertvector((v2f){v[2 * j], v[2 * j + 1]}, bf16x2);
             o[j] = nan ? 0x7FC07FC0u : __builtin_bit_cast(uint32_t, h);
         }
-        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + off);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + off;
+        st_out4(dst, 0, o[0], o[1], o[2], o[3]);
+        st_out4(dst, 1, o[4], o[5], o[6], o[7]);
     } else {
         uint32_t o[16];
         #pragma unroll
         for (int j = 0; j < 16; ++j) o[j] = nan ? 0x7FC00000u : __float_as_uint(v[j]);
-        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<float*>(p.out) + off);
+        float* dst = reinterpret_cast<float*>(p.out) + off;
         #pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        for (int q = 0; q < 4; ++q) st_out4(dst, q, o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
     }
 }
 
 // ---------------------------------------------------------------- guide pack / unpack
 
+// Four consecutive groups per lane: 32 bytes of codes in, 8 bytes of bits out.
+constexpr uint32_t kGuideG = 4;
+
+template <int FMT>
+__device__ __forceinline__ void copy_scales(const GuideParams& p, uint32_t g) {
+    if (FMT == 0) st_out(p.scales_out + g, p.scales_in[g]);
+    else if ((g & 1u) == 0) st_out(p.scales_out + (g >> 1), p.scales_in[g >> 1]);
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_guide_pack(const GuideParams p) {
-    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
-    if (g >= p.ngroups) return;
-    const uint2 c = reinterpret_cast<const uint2*>(p.in)[g];
-    reinterpret_cast<uint16_t*>(p.out)[g] =
-        (uint16_t)(gather_nibble_lsbs(c.x) | (gather_nibble_lsbs(c.y) << 8));
-    if (FMT == 0) p.scales_out[g] = p.scales_in[g];
-    else if ((g & 1u) == 0) p.scales_out[g >> 1] = p.scales_in[g >> 1];
+    const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t g0 = t * kGuideG;
+    if (g0 >= p.ngroups) return;
+    if (g0 + kGuideG <= p.ngroups) {
+        const v4u32* src = reinterpret_cast<const v4u32*>(p.in) + 2 * (int64_t)t;
+        const v4u32 a = __builtin_nontemporal_load(src), b = __builtin_nontemporal_load(src + 1);
+        const uint32_t lo = gather_nibble_lsbs(a.x) | (gather_nibble_lsbs(a.y) << 8) |
+                            (gather_nibble_lsbs(a.z) << 16) | (gather_nibble_lsbs(a.w) << 24);
+        const uint32_t hi = gather_nibble_lsbs(b.x) | (gather_nibble_lsbs(b.y) << 8) |
+                            (gather_nibble_lsbs(b.z) << 16) | (gather_nibble_lsbs(b.w) << 24);
+        st_out2(p.out, t, lo, hi);
+        #pragma unroll
+        for (uint32_t k = 0; k < kGuideG; ++k) copy_scales<FMT>(p, g0 + k);
+    } else {
+        for (uint32_t g = g0; g < p.ngroups; ++g) {
+            const uint2 c = reinterpret_cast<const uint2*>(p.in)[g];
+            reinterpret_cast<uint16_t*>(p.out)[g] =
+                (uint16_t)(gather_nibble_lsbs(c.x) | (gather_nibble_lsbs(c.y) << 8));
+            copy_scales<FMT>(p, g);
+        }
+    }
 }
 
 __device__ __forceinline__ uint32_t bits4_to_bytes(uint32_t b) {
@@ -141,13 +191,16 @@ __device__ __forceinline__ uint32_t bits4_to_bytes(uint32_t b) {
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_guide_unpack(const GuideParams p) {
-    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
-    if (g >= p.ngroups) return;
-    const uint32_t b = reinterpret_cast<const uint16_t*>(p.in)[g];
-    reinterpret_cast<uint4*>(p.out)[g] =
-        make_uint4(bits4_to_bytes(b), bits4_to_bytes(b >> 4), bits4_to_bytes(b >> 8), bits4_to_bytes(b >> 12));
-    if (FMT == 0) p.scales_out[g] = p.scales_in[g];
-    else if ((g & 1u) == 0) p.scales_out[g >> 1] = p.scales_in[g >> 1];
+    const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t g0 = t * kGuideG;
+    if (g0 >= p.ngroups) return;
+    const uint32_t gend = g0 + kGuideG <= p.ngroups ? g0 + kGuideG : p.ngroups;
+    for (uint32_t g = g0; g < gend; ++g) {
+        const uint32_t b = reinterpret_cast<const uint16_t*>(p.in)[g];
+        st_out4(p.out, g, bits4_to_bytes(b), bits4_to_bytes(b >> 4), bits4_to_bytes(b >> 8),
+                bits4_to_bytes(b >> 12));
+        copy_scales<FMT>(p, g);
+    }
 }
 
 // ---------------------------------------------------------------- RHT16
@@ -218,8 +271,8 @@ inline uint32_t blocks_for(uint32_t n) { return (n + kThreads - 1) / kThreads; }
 
 hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams& p, hipStream_t s) {
     hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, reinterpret_cast<uint32_t*>(p.acc), 0u);
-    uint32_t blocks = blocks_for(p.ngroups);
-    if (blocks > 4096) blocks = 4096;
+    uint32_t blocks = (p.ngroups + kThreads * kAmaxU - 1) / (kThreads * kAmaxU);
+    if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
     if (blocks > 0) {
         if (rht) {
             if (contig) hipLaunchKernelGGL((k_amax<true, true>), dim3(blocks), dim3(kThreads), 0, s, p);
@@ -248,14 +301,14 @@ hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantP
 }
 
 hipError_t launch_guide_pack(int format, const GuideParams& p, hipStream_t s) {
-    const dim3 b(blocks_for(p.ngroups)), t(kThreads);
+    const dim3 b(blocks_for((p.ngroups + kGuideG - 1) / kGuideG)), t(kThreads);
     if (format == 0) hipLaunchKernelGGL(k_guide_pack<0>, b, t, 0, s, p);
     else hipLaunchKernelGGL(k_guide_pack<1>, b, t, 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_guide_unpack(int format, const GuideParams& p, hipStream_t s) {
-    const dim3 b(blocks_for(p.ngroups)), t(kThreads);
+    const dim3 b(blocks_for((p.ngroups + kGuideG - 1) / kGuideG)), t(kThreads);
     if (format == 0) hipLaunchKernelGGL(k_guide_unpack<0>, b, t, 0, s, p);
     else hipLaunchKernelGGL(k_guide_unpack<1>, b, t, 0, s, p);
     return hipGetLastError();

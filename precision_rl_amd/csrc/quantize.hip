@@ -23,7 +23,10 @@ namespace fp4q {
 
 namespace {
 
-constexpr int kGroupsPerLane = 2;
+#ifndef FP4Q_GROUPS_PER_LANE
+#define FP4Q_GROUPS_PER_LANE 1
+#endif
+constexpr int kGroupsPerLane = FP4Q_GROUPS_PER_LANE;
 
 template <bool CONTIG>
 __device__ __forceinline__ int64_t group_offset(uint32_t g, const QuantParams& p) {
@@ -54,11 +57,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const QuantParams p) {
     for (int u = 0; u < U; ++u) {
         const uint32_t g = g0 + u * kThreads;
         if (g < p.ngroups) {
-            const uint4* src = reinterpret_cast<const uint4*>(p.x + group_offset<CONTIG>(g, p));
-            const uint4 a = src[0];
-            const uint4 b = src[1];
-            w[u][0] = a.x; w[u][1] = a.y; w[u][2] = a.z; w[u][3] = a.w;
-            w[u][4] = b.x; w[u][5] = b.y; w[u][6] = b.z; w[u][7] = b.w;
+            load32_nt(p.x + group_offset<CONTIG>(g, p), w[u]);
             if constexpr (MODE == MODE_GUIDED) {
                 gb[u] = reinterpret_cast<const uint16_t*>(p.gbits)[g];
                 gs[u] = p.gscales[FMT == 0 ? g : (g >> 1)];
@@ -133,15 +132,15 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const QuantParams p) {
         uint32_t c1 = encode8<GRID, MODE>(v + 8, r2, r3, gbits >> 8);
         if (!finite) { c0 = 0; c1 = 0; }
 
-        reinterpret_cast<uint2*>(p.codes)[g] = make_uint2(c0, c1);
+        st_out2(p.codes, g, c0, c1);
         if constexpr (FMT == 0) {
-            p.scales[g] = (uint8_t)sc;
+            st_out(p.scales + g, (uint8_t)sc);
         } else {
-            if ((g & 1u) == 0) p.scales[g >> 1] = (uint8_t)sc;
+            if ((g & 1u) == 0) st_out(p.scales + (g >> 1), (uint8_t)sc);
         }
         if constexpr (EMIT) {
-            reinterpret_cast<uint16_t*>(p.bits_out)[g] =
-                (uint16_t)(gather_nibble_lsbs(c0) | (gather_nibble_lsbs(c1) << 8));
+            st_out(reinterpret_cast<uint16_t*>(p.bits_out) + g,
+                   (uint16_t)(gather_nibble_lsbs(c0) | (gather_nibble_lsbs(c1) << 8)));
         }
     }
 }
