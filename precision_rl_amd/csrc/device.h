@@ -28,10 +28,14 @@ typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
 #define FP4Q_NT_STORES 0
 #endif
 
+#ifndef FP4Q_NT_LOADS
+#define FP4Q_NT_LOADS 1
+#endif
+
 __device__ __forceinline__ void load32_nt(const uint16_t* p, uint32_t w[8]) {
     const v4u32* s = reinterpret_cast<const v4u32*>(p);
-    const v4u32 a = __builtin_nontemporal_load(s);
-    const v4u32 b = __builtin_nontemporal_load(s + 1);
+    const v4u32 a = FP4Q_NT_LOADS ? __builtin_nontemporal_load(s) : s[0];
+    const v4u32 b = FP4Q_NT_LOADS ? __builtin_nontemporal_load(s + 1) : s[1];
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
