@@ -122,6 +122,50 @@ fp4_status fp4_quantize_guided(const fp4_cfg* cfg, const void* x_bf16, int64_t r
                                const void* guide_scales, const float* guide_tensor_scale,
                                void* codes, void* scales, hipStream_t stream);
 
+/* One tensor of a grouped call (fields as in fp4_quantize / fp4_quantize_guided). */
+typedef struct {
+    const void* x;              /* bf16 [rows, cols], row stride ld elements */
+    int64_t rows;
+    int64_t cols;
+    int64_t ld;
+    const float* tensor_scale;  /* NVFP4: s_t, or the guide's s_t when guided; else ignored */
+    void* codes;                /* output codes */
+    void* scales;               /* output scales */
+    void* guide_bits;           /* RTN/SR: fused emission output or NULL; guided: guide bits input */
+    const void* guide_scales;   /* guided: guide scales input; otherwise ignored */
+} fp4_tensor;
+
+#define FP4_MAX_GROUP 16
+
+/* Several tensors sharing one configuration in a single launch, e.g. the routed
+ * experts' weight slices and the activations of one MoE layer [TRACE-JA
+ * 実験結果: MoE models; TRACE-JA 量子化情報キャッシュ: every quantization
+ * point of a deep layer].  Equivalent to calling fp4_quantize (guided == 0,
+ * rounding from cfg) or fp4_quantize_guided (guided != 0) on each tensor in
+ * turn with the same cfg: each tensor's element index, and so its
+ * stochastic-rounding counter, starts at 0.
+ *   n        1 .. FP4_MAX_GROUP
+ *   tensors  HOST array of n descriptors; validated like the single calls.
+ * With guided == 0 either every tensor gives guide_bits (fused emission) or
+ * none does. */
+fp4_status fp4_quantize_grouped(const fp4_cfg* cfg, int guided, int n, const fp4_tensor* tensors,
+                                hipStream_t stream);
+
+/* Fake quantization for quantization-aware training [TRACE-JA "TRACEの仕組み":
+ * the trainer's forward pass uses the chosen quantized value; FQT-FP4 §3]:
+ * out = bf16 dequantization of the codes that fp4_quantize (guided == 0,
+ * rounding from cfg) or fp4_quantize_guided (guided != 0) would produce,
+ * computed in one pass without writing codes.  Bit for bit equal to calling
+ * the quantize entry point and then fp4_dequantize with FP4_OUT_BF16.
+ *   tensor_scale  NVFP4: s_t (guided: the guide's s_t); MXFP4: ignored
+ *   guide_bits, guide_scales  guided only (may be NULL otherwise)
+ *   out_bf16      [rows, cols] with row stride ld_out (>= cols, % 8 == 0),
+ *                 16-byte aligned. */
+fp4_status fp4_fake_quantize(const fp4_cfg* cfg, int guided, const void* x_bf16, int64_t rows,
+                             int64_t cols, int64_t ld, const float* tensor_scale,
+                             const void* guide_bits, const void* guide_scales, void* out_bf16,
+                             int64_t ld_out, hipStream_t stream);
+
 /* Dequantization [TRACE-KO: shared block scale, 4-bit values]:
  * NVFP4 val = RN(RN(G[k]*dec(scale))*s_t); MXFP4 val = G[k]*2^e; the code's
  * sign applied; fp32 output, or bf16 by round-to-nearest-even of that fp32.

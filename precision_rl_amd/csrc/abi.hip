@@ -167,12 +167,103 @@ fp4_status fp4_quantize(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, in
                            guide_bits_out, nullptr, nullptr, stream);
 }
 
+fp4_status fp4_quantize_grouped(const fp4_cfg* cfg, int guided, int n, const fp4_tensor* tensors,
+                                hipStream_t stream) {
+    FP4Q_TRY(check_cfg(cfg));
+    if (n < 1 || n > FP4_MAX_GROUP) return fail(FP4_ERR_ARG, "n=%d outside 1..%d", n, FP4_MAX_GROUP);
+    if (!tensors) return fail(FP4_ERR_ARG, "tensors is NULL");
+    static_assert(FP4_MAX_GROUP == fp4q::kMaxGroup, "group size limits differ");
+    const int mode = guided ? fp4q::MODE_GUIDED : (cfg->rounding == FP4_SR ? fp4q::MODE_SR : fp4q::MODE_RTN);
+    const bool emit = !guided && tensors[0].guide_bits != nullptr;
+    fp4q::GroupedQuantParams gp{};
+    gp.n = (uint32_t)n;
+    uint64_t wg = 0;
+    for (int t = 0; t < n; ++t) {
+        const fp4_tensor& d = tensors[t];
+        uint64_t ng = 0;
+        fp4_status st = check_matrix(d.rows, d.cols, d.ld, block_of(cfg->format), d.x, &ng);
+        if (st != FP4_OK) {
+            char msg[sizeof g_err];
+            snprintf(msg, sizeof msg, "%s", g_err);
+            return fail(st, "tensor %d: %s", t, msg);
+        }
+        gp.wg_start[t] = (uint32_t)wg;
+        if (ng == 0) continue;
+        const char* what = nullptr;
+        if (!d.codes || !aligned(d.codes, 16)) what = "codes";
+        else if (!d.scales) what = "scales";
+        else if (cfg->format == FP4_NVFP4 && (!d.tensor_scale || !aligned(d.tensor_scale, 4))) what = "tensor_scale";
+        else if (guided && (!d.guide_bits || !aligned(d.guide_bits, 16))) what = "guide_bits";
+        else if (guided && !d.guide_scales) what = "guide_scales";
+        else if (!guided && (d.guide_bits != nullptr) != emit) what = "guide_bits (emission must be all or none)";
+        else if (!guided && emit && !aligned(d.guide_bits, 16)) what = "guide_bits";
+        if (what) return fail(FP4_ERR_ARG, "tensor %d: %s missing or misaligned", t, what);
+        fp4q::QuantParams& p = gp.t[t];
+        p.x = static_cast<const uint16_t*>(d.x);
+        p.ld = d.ld;
+        p.ngroups = (uint32_t)ng;
+        p.gpr = fp4q::make_fastdiv((uint32_t)(d.cols / 16));
+        p.ts = d.tensor_scale;
+        p.codes = static_cast<uint8_t*>(d.codes);
+        p.scales = static_cast<uint8_t*>(d.scales);
+        p.bits_out = guided ? nullptr : static_cast<uint8_t*>(d.guide_bits);
+        p.gbits = guided ? static_cast<const uint8_t*>(d.guide_bits) : nullptr;
+        p.gscales = guided ? static_cast<const uint8_t*>(d.guide_scales) : nullptr;
+        p.key0 = (uint32_t)cfg->sr_seed;
+        p.key1 = (uint32_t)(cfg->sr_seed >> 32);
+        p.sr_offset = cfg->sr_offset;
+        p.rht_seed = cfg->rht_seed;
+        if (d.ld == d.cols) gp.contig_mask |= 1u << t;
+        wg += fp4q::quantize_chunks((uint32_t)ng);
+        if (wg >= (1ull << 31)) return fail(FP4_ERR_SHAPE, "grouped call too large");
+    }
+    gp.wg_start[n] = (uint32_t)wg;
+    if (wg == 0) return ok();
+    return hip_status(fp4q::launch_quantize_grouped(cfg->format, cfg->grid, mode, cfg->rht16 != 0, emit, gp, stream),
+                      "grouped quantize launch");
+}
+
 fp4_status fp4_quantize_guided(const fp4_cfg* cfg, const void* x_bf16, int64_t rows,
                                int64_t cols, int64_t ld, const void* guide_bits,
                                const void* guide_scales, const float* guide_tensor_scale,
                                void* codes, void* scales, hipStream_t stream) {
     return quantize_common(cfg, fp4q::MODE_GUIDED, x_bf16, rows, cols, ld, guide_tensor_scale,
                            codes, scales, nullptr, guide_bits, guide_scales, stream);
+}
+
+fp4_status fp4_fake_quantize(const fp4_cfg* cfg, int guided, const void* x_bf16, int64_t rows,
+                             int64_t cols, int64_t ld, const float* tensor_scale,
+                             const void* guide_bits, const void* guide_scales, void* out_bf16,
+                             int64_t ld_out, hipStream_t stream) {
+    FP4Q_TRY(check_cfg(cfg));
+    uint64_t ng = 0;
+    FP4Q_TRY(check_matrix(rows, cols, ld, block_of(cfg->format), x_bf16, &ng));
+    if (ng == 0) return ok();
+    FP4Q_TRY(need(out_bf16, 16, "out_bf16"));
+    if (ld_out < cols) return fail(FP4_ERR_SHAPE, "ld_out=%lld < cols=%lld", (long long)ld_out, (long long)cols);
+    if (ld_out % 8 != 0) return fail(FP4_ERR_ALIGN, "ld_out=%lld is not a multiple of 8", (long long)ld_out);
+    if (cfg->format == FP4_NVFP4) FP4Q_TRY(need(tensor_scale, 4, "tensor_scale"));
+    if (guided) {
+        FP4Q_TRY(need(guide_bits, 16, "guide_bits"));
+        FP4Q_TRY(need(guide_scales, 1, "guide_scales"));
+    }
+    fp4q::QuantParams p{};
+    p.x = static_cast<const uint16_t*>(x_bf16);
+    p.ld = ld;
+    p.ngroups = (uint32_t)ng;
+    p.gpr = fp4q::make_fastdiv((uint32_t)(cols / 16));
+    p.ts = tensor_scale;
+    p.gbits = static_cast<const uint8_t*>(guide_bits);
+    p.gscales = static_cast<const uint8_t*>(guide_scales);
+    p.key0 = (uint32_t)cfg->sr_seed;
+    p.key1 = (uint32_t)(cfg->sr_seed >> 32);
+    p.sr_offset = cfg->sr_offset;
+    p.rht_seed = cfg->rht_seed;
+    p.fq_out = static_cast<uint16_t*>(out_bf16);
+    p.ld_out = ld_out;
+    const int mode = guided ? fp4q::MODE_GUIDED : (cfg->rounding == FP4_SR ? fp4q::MODE_SR : fp4q::MODE_RTN);
+    return hip_status(fp4q::launch_fake_quantize(cfg->format, cfg->grid, mode, cfg->rht16 != 0, ld == cols, p, stream),
+                      "fake quantize launch");
 }
 
 fp4_status fp4_dequantize(const fp4_cfg* cfg, const void* codes, const void* scales,

@@ -261,6 +261,58 @@ __device__ __forceinline__ uint32_t encode8(const float v[8], uint32_t rnd0, uin
     }
 }
 
+// ---------------------------------------------------------------- decode
+// G[k] with sign for 8 packed codes: E2M1 via the hardware decode (exact),
+// uniform via integers.
+template <int GRID>
+__device__ __forceinline__ void decode8(uint32_t w, float g[8]) {
+    if constexpr (GRID == 0) {
+        v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+        v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+        v2f c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+        v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        g[0] = a[0]; g[1] = a[1]; g[2] = b[0]; g[3] = b[1];
+        g[4] = c[0]; g[5] = c[1]; g[6] = d[0]; g[7] = d[1];
+    } else {
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t nib = (w >> (4 * j)) & 0xFu;
+            g[j] = __uint_as_float(__float_as_uint((float)(nib & 7u)) | ((nib & 8u) << 28));
+        }
+    }
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Dequantized values of one 16-group from its codes and block scale code:
+// NVFP4 RN(RN(G*d)*s_t) (G*d exact), MXFP4 G*2^(code-127); returns false for a
+// NaN scale code.
+template <int FMT, int GRID>
+__device__ __forceinline__ bool dequant16(uint32_t c0, uint32_t c1, uint32_t sc, float ts, float v[16]) {
+    decode8<GRID>(c0, v);
+    decode8<GRID>(c1, v + 8);
+    if constexpr (FMT == 0) {
+        const float d = e4m3_decode(sc);
+        #pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = (v[j] * d) * ts;
+        return (sc & 0x7Fu) != 0x7Fu;
+    } else {
+        const float s2 = __uint_as_float(sc ? sc << 23 : 0x00400000u);  // 2^(sc-127)
+        #pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = v[j] * s2;
+        return sc != 0xFFu;
+    }
+}
+
+// 16 fp32 -> 16 bf16 (RNE) as 8 dwords; canonical quiet NaN when !ok.
+__device__ __forceinline__ void to_bf16x16(const float v[16], bool ok, uint32_t o[8]) {
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        bf16x2 h = __builtin_convertvector((v2f){v[2 * j], v[2 * j + 1]}, bf16x2);
+        o[j] = ok ? __builtin_bit_cast(uint32_t, h) : 0x7FC07FC0u;
+    }
+}
+
 // ---------------------------------------------------------------- RHT16
 // Sylvester-ordered butterfly, stages h = 1, 2, 4, 8, each sum rounded to fp32.
 __device__ __forceinline__ void butterfly16(float a[16]) {

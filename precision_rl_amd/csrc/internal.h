@@ -43,6 +43,18 @@ struct QuantParams {
     uint32_t key0, key1;        // SR Philox key
     uint64_t sr_offset;         // SR counter offset (groups)
     uint64_t rht_seed;          // RHT: Philox key of the sign diagonal
+    uint16_t* fq_out;           // fake quantization: bf16 output (dequantized codes)
+    int64_t ld_out;             // its row stride in elements
+};
+
+// Up to kMaxGroup tensors sharing one configuration, quantized by one launch.
+constexpr int kMaxGroup = 16;
+
+struct GroupedQuantParams {
+    QuantParams t[kMaxGroup];
+    uint32_t wg_start[kMaxGroup + 1];   // prefix sums of per-tensor workgroup counts
+    uint32_t n;
+    uint32_t contig_mask;               // bit t: tensor t has ld == cols
 };
 
 struct DequantParams {
@@ -91,6 +103,13 @@ struct EncodeParams {
 // Launchers (return hipGetLastError() of the launch).
 hipError_t launch_quantize(int format, int grid, int mode, bool rht, bool emit, bool contig,
                            const QuantParams& p, hipStream_t s);
+// Quantize then dequantize to bf16 in one pass (p.fq_out, p.ld_out); no codes written.
+hipError_t launch_fake_quantize(int format, int grid, int mode, bool rht, bool contig,
+                                const QuantParams& p, hipStream_t s);
+// Workgroups needed to quantize `ngroups` 16-element groups.
+uint32_t quantize_chunks(uint32_t ngroups);
+hipError_t launch_quantize_grouped(int format, int grid, int mode, bool rht, bool emit,
+                                   const GroupedQuantParams& gp, hipStream_t s);
 hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams& p, hipStream_t s);
 hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantParams& p,
                              hipStream_t s);

@@ -85,26 +85,6 @@ __global__ void k_ts_finalize(float* acc, float gmax448) {
 }
 
 // ---------------------------------------------------------------- dequantize
-// G[k] with sign: E2M1 via the hardware decode (exact), uniform via integers.
-template <int GRID>
-__device__ __forceinline__ void decode8(uint32_t w, float g[8]) {
-    if constexpr (GRID == 0) {
-        v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-        v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-        v2f c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-        v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-        g[0] = a[0]; g[1] = a[1]; g[2] = b[0]; g[3] = b[1];
-        g[4] = c[0]; g[5] = c[1]; g[6] = d[0]; g[7] = d[1];
-    } else {
-        #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t nib = (w >> (4 * j)) & 0xFu;
-            g[j] = __uint_as_float(__float_as_uint((float)(nib & 7u)) | ((nib & 8u) << 28));
-        }
-    }
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int FMT, int GRID, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) {
@@ -113,29 +93,12 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) 
     const v2u32 c = __builtin_nontemporal_load(reinterpret_cast<const v2u32*>(p.codes) + g);
     const uint32_t sc = p.scales[FMT == 0 ? g : (g >> 1)];
     float v[16];
-    decode8<GRID>(c.x, v);
-    decode8<GRID>(c.y, v + 8);
-    bool nan;
-    if constexpr (FMT == 0) {
-        nan = (sc & 0x7Fu) == 0x7Fu;
-        const float d = e4m3_decode(sc);
-        const float ts = *p.ts;
-        #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = (v[j] * d) * ts;   // G*d is exact
-    } else {
-        nan = sc == 0xFFu;
-        const float s2 = __uint_as_float(sc ? sc << 23 : 0x00400000u);  // 2^(sc-127)
-        #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = v[j] * s2;
-    }
+    const bool ok = dequant16<FMT, GRID>(c.x, c.y, sc, FMT == 0 ? *p.ts : 1.0f, v);
+    const bool nan = !ok;
     const int64_t off = row_offset(g, p.gpr, p.ld_out);
     if constexpr (BF16) {
         uint32_t o[8];
-        #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            bf16x2 h = __builtin_convertvector((v2f){v[2 * j], v[2 * j + 1]}, bf16x2);
-            o[j] = nan ? 0x7FC07FC0u : __builtin_bit_cast(uint32_t, h);
-        }
+        to_bf16x16(v, ok, o);
         uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + off;
         st_out4(dst, 0, o[0], o[1], o[2], o[3]);
         st_out4(dst, 1, o[4], o[5], o[6], o[7]);

@@ -44,11 +44,14 @@ __device__ __forceinline__ uint32_t dpp_swap_pair(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
 }
 
-template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG>
-__global__ __launch_bounds__(kThreads) void k_quantize(const QuantParams p) {
+// One workgroup's share (kThreads * U groups starting at chunk `wg`) of one tensor.
+// OUT = 0 stores codes, scales (and emitted guide bits); OUT = 1 stores the
+// dequantized bf16 values instead (fake quantization).
+template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG, int OUT = 0>
+__device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg) {
     constexpr int U = kGroupsPerLane;
     constexpr float kGmax = GRID == 0 ? 6.0f : 7.0f;
-    const uint32_t g0 = blockIdx.x * (kThreads * U) + threadIdx.x;
+    const uint32_t g0 = wg * (kThreads * U) + threadIdx.x;
 
     uint32_t w[U][8];
     uint32_t gb[U];
@@ -132,16 +135,83 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const QuantParams p) {
         uint32_t c1 = encode8<GRID, MODE>(v + 8, r2, r3, gbits >> 8);
         if (!finite) { c0 = 0; c1 = 0; }
 
-        st_out2(p.codes, g, c0, c1);
-        if constexpr (FMT == 0) {
-            st_out(p.scales + g, (uint8_t)sc);
+        if constexpr (OUT == 1) {
+            float dv[16];
+            const bool ok = dequant16<FMT, GRID>(c0, c1, sc, ts, dv);
+            uint32_t o[8];
+            to_bf16x16(dv, ok, o);
+            const uint32_t row = fastdiv(g, p.gpr);
+            uint16_t* dst = p.fq_out + (int64_t)row * p.ld_out + (int64_t)(g - row * p.gpr.d) * 16;
+            st_out4(dst, 0, o[0], o[1], o[2], o[3]);
+            st_out4(dst, 1, o[4], o[5], o[6], o[7]);
         } else {
-            if ((g & 1u) == 0) st_out(p.scales + (g >> 1), (uint8_t)sc);
+            st_out2(p.codes, g, c0, c1);
+            if constexpr (FMT == 0) {
+                st_out(p.scales + g, (uint8_t)sc);
+            } else {
+                if ((g & 1u) == 0) st_out(p.scales + (g >> 1), (uint8_t)sc);
+            }
+            if constexpr (EMIT) {
+                st_out(reinterpret_cast<uint16_t*>(p.bits_out) + g,
+                       (uint16_t)(gather_nibble_lsbs(c0) | (gather_nibble_lsbs(c1) << 8)));
+            }
         }
-        if constexpr (EMIT) {
-            st_out(reinterpret_cast<uint16_t*>(p.bits_out) + g,
-                   (uint16_t)(gather_nibble_lsbs(c0) | (gather_nibble_lsbs(c1) << 8)));
-        }
+    }
+}
+
+template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void k_quantize(const QuantParams p) {
+    quantize_chunk<FMT, GRID, MODE, RHT, EMIT, CONTIG>(p, blockIdx.x);
+}
+
+// Several tensors with one configuration in one launch: workgroup b belongs to
+// the tensor t with wg_start[t] <= b < wg_start[t+1] (a uniform scan of at most
+// kMaxGroup entries), and processes that tensor's chunk b - wg_start[t].
+template <int FMT, int GRID, int MODE, bool RHT, bool EMIT>
+__global__ __launch_bounds__(kThreads) void k_quantize_grouped(const GroupedQuantParams gp) {
+    const uint32_t b = blockIdx.x;
+    uint32_t t = 0;
+    while (t + 1 < gp.n && b >= gp.wg_start[t + 1]) ++t;
+    const uint32_t wg = b - gp.wg_start[t];
+    if ((gp.contig_mask >> t) & 1u)
+        quantize_chunk<FMT, GRID, MODE, RHT, EMIT, true>(gp.t[t], wg);
+    else
+        quantize_chunk<FMT, GRID, MODE, RHT, EMIT, false>(gp.t[t], wg);
+}
+
+template <int FMT, int GRID, int MODE, bool RHT, bool EMIT>
+hipError_t launch_grouped_t(const GroupedQuantParams& gp, hipStream_t s) {
+    const uint32_t blocks = gp.wg_start[gp.n];
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_quantize_grouped<FMT, GRID, MODE, RHT, EMIT>), dim3(blocks), dim3(kThreads), 0, s, gp);
+    return hipGetLastError();
+}
+
+template <int FMT, int GRID, int MODE, bool RHT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void k_fake_quantize(const QuantParams p) {
+    quantize_chunk<FMT, GRID, MODE, RHT, false, CONTIG, 1>(p, blockIdx.x);
+}
+
+template <int FMT, int GRID, int MODE>
+hipError_t launch_fake_m(bool rht, bool contig, const QuantParams& p, hipStream_t s) {
+    const uint32_t per_block = kThreads * kGroupsPerLane;
+    const dim3 b((p.ngroups + per_block - 1) / per_block), t(kThreads);
+    if (rht) {
+        if (contig) hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, true, true>), b, t, 0, s, p);
+        else hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, true, false>), b, t, 0, s, p);
+    } else {
+        if (contig) hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, false, true>), b, t, 0, s, p);
+        else hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, false, false>), b, t, 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+template <int FMT, int GRID>
+hipError_t launch_fake_g(int mode, bool rht, bool contig, const QuantParams& p, hipStream_t s) {
+    switch (mode) {
+        case MODE_RTN: return launch_fake_m<FMT, GRID, MODE_RTN>(rht, contig, p, s);
+        case MODE_SR: return launch_fake_m<FMT, GRID, MODE_SR>(rht, contig, p, s);
+        default: return launch_fake_m<FMT, GRID, MODE_GUIDED>(rht, contig, p, s);
     }
 }
 
@@ -185,7 +255,57 @@ hipError_t launch_m(int mode, bool rht, bool emit, bool contig, const QuantParam
     }
 }
 
+template <int FMT, int GRID, int MODE, bool RHT>
+hipError_t launch_grouped_e(bool emit, const GroupedQuantParams& gp, hipStream_t s) {
+    if constexpr (MODE == MODE_GUIDED) {
+        return launch_grouped_t<FMT, GRID, MODE, RHT, false>(gp, s);
+    } else {
+        return emit ? launch_grouped_t<FMT, GRID, MODE, RHT, true>(gp, s)
+                    : launch_grouped_t<FMT, GRID, MODE, RHT, false>(gp, s);
+    }
+}
+
+template <int FMT, int GRID>
+hipError_t launch_grouped_m(int mode, bool rht, bool emit, const GroupedQuantParams& gp, hipStream_t s) {
+    switch (mode) {
+        case MODE_RTN:
+            return rht ? launch_grouped_e<FMT, GRID, MODE_RTN, true>(emit, gp, s)
+                       : launch_grouped_e<FMT, GRID, MODE_RTN, false>(emit, gp, s);
+        case MODE_SR:
+            return rht ? launch_grouped_e<FMT, GRID, MODE_SR, true>(emit, gp, s)
+                       : launch_grouped_e<FMT, GRID, MODE_SR, false>(emit, gp, s);
+        default:
+            return rht ? launch_grouped_e<FMT, GRID, MODE_GUIDED, true>(emit, gp, s)
+                       : launch_grouped_e<FMT, GRID, MODE_GUIDED, false>(emit, gp, s);
+    }
+}
+
 }  // namespace
+
+uint32_t quantize_chunks(uint32_t ngroups) {
+    const uint32_t per = kThreads * kGroupsPerLane;
+    return (ngroups + per - 1) / per;
+}
+
+hipError_t launch_quantize_grouped(int format, int grid, int mode, bool rht, bool emit,
+                                   const GroupedQuantParams& gp, hipStream_t s) {
+    if (format == 0) {
+        return grid == 0 ? launch_grouped_m<0, 0>(mode, rht, emit, gp, s)
+                         : launch_grouped_m<0, 1>(mode, rht, emit, gp, s);
+    }
+    return grid == 0 ? launch_grouped_m<1, 0>(mode, rht, emit, gp, s)
+                     : launch_grouped_m<1, 1>(mode, rht, emit, gp, s);
+}
+
+hipError_t launch_fake_quantize(int format, int grid, int mode, bool rht, bool contig,
+                                const QuantParams& p, hipStream_t s) {
+    if (format == 0) {
+        return grid == 0 ? launch_fake_g<0, 0>(mode, rht, contig, p, s)
+                         : launch_fake_g<0, 1>(mode, rht, contig, p, s);
+    }
+    return grid == 0 ? launch_fake_g<1, 0>(mode, rht, contig, p, s)
+                     : launch_fake_g<1, 1>(mode, rht, contig, p, s);
+}
 
 hipError_t launch_quantize(int format, int grid, int mode, bool rht, bool emit, bool contig,
                            const QuantParams& p, hipStream_t s) {

@@ -60,10 +60,19 @@ class Fp4Config:
                      self.sr_offset, self.rht_seed)
 
 
+class _CTensor(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("rows", C.c_int64), ("cols", C.c_int64), ("ld", C.c_int64),
+                ("tensor_scale", C.c_void_p), ("codes", C.c_void_p), ("scales", C.c_void_p),
+                ("guide_bits", C.c_void_p), ("guide_scales", C.c_void_p)]
+
+
+MAX_GROUP = 16
+
 _lib = None
-EXPORTS = ("fp4_tensor_scale", "fp4_quantize", "fp4_quantize_guided", "fp4_dequantize", "guide_pack",
-           "guide_unpack", "fp4_rht16", "fp4_encode_values", "fp4_codes_bytes", "fp4_scales_bytes",
-           "fp4_guide_bytes", "fp4_status_str", "fp4_last_error")
+EXPORTS = ("fp4_tensor_scale", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
+           "fp4_fake_quantize", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_rht16",
+           "fp4_encode_values", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
+           "fp4_status_str", "fp4_last_error")
 
 
 def lib():
@@ -81,6 +90,8 @@ def lib():
         "fp4_tensor_scale": [CP, P, I64, I64, I64, P, P],
         "fp4_quantize": [CP, P, I64, I64, I64, P, P, P, P, P],
         "fp4_quantize_guided": [CP, P, I64, I64, I64, P, P, P, P, P, P],
+        "fp4_quantize_grouped": [CP, I, I, C.POINTER(_CTensor), P],
+        "fp4_fake_quantize": [CP, I, P, I64, I64, I64, P, P, P, P, I64, P],
         "fp4_dequantize": [CP, P, P, P, I64, I64, P, I64, I, P],
         "guide_pack": [CP, P, P, I64, I64, P, P, P],
         "guide_unpack": [CP, P, P, I64, I64, P, P, P],
@@ -179,6 +190,66 @@ def fp4_quantize_guided(x: torch.Tensor, cfg: Fp4Config, guide_bits: torch.Tenso
                                      _ptr(guide_scales), _ptr(guide_tensor_scale), _ptr(codes),
                                      _ptr(scales), _stream(x)), "fp4_quantize_guided")
     return codes, scales
+
+
+def fp4_quantize_grouped(xs, cfg: Fp4Config, tensor_scales=None, emit: bool = False, guides=None,
+                         outs=None):
+    """Quantize up to MAX_GROUP tensors with one configuration in one launch.
+
+    xs            list of 2-D bf16 device tensors
+    tensor_scales list of f32[1] tensors (NVFP4; for guided, the guides' tensor scales)
+    emit          RTN/SR: also return each tensor's guide bitplane
+    guides        list of (guide_bits, guide_scales): guided quantization
+    outs          optional list of (codes, scales[, bits]) output tensors
+    Returns a list of (codes, scales) or (codes, scales, bits)."""
+    n = len(xs)
+    if not 1 <= n <= MAX_GROUP:
+        raise ValueError(f"1..{MAX_GROUP} tensors per grouped call, got {n}")
+    arr = (_CTensor * n)()
+    results = []
+    for t, x in enumerate(xs):
+        _on_gpu(x)
+        rows, cols, ld = _matrix(x)
+        m = rows * cols
+        if outs is not None:
+            o = outs[t]
+            codes, scales = o[0], o[1]
+            bits = o[2] if len(o) > 2 else None
+        else:
+            codes, scales, bits = _u8(m // 2, x), _u8(m // cfg.block, x), None
+        if emit and bits is None:
+            bits = _u8(m // 8, x)
+        ts = tensor_scales[t] if tensor_scales is not None else None
+        gb = gs = None
+        if guides is not None:
+            gb, gs = guides[t]
+        _on_gpu(codes, scales, bits, ts, gb, gs)
+        arr[t] = _CTensor(x.data_ptr(), rows, cols, ld, ts.data_ptr() if ts is not None else None,
+                          codes.data_ptr(), scales.data_ptr(),
+                          (gb.data_ptr() if gb is not None else (bits.data_ptr() if emit else None)),
+                          gs.data_ptr() if gs is not None else None)
+        results.append((codes, scales, bits) if emit else (codes, scales))
+    c = cfg.c()
+    _check(lib().fp4_quantize_grouped(C.byref(c), int(guides is not None), n, arr, _stream(xs[0])),
+           "fp4_quantize_grouped")
+    return results
+
+
+def fp4_fake_quantize(x: torch.Tensor, cfg: Fp4Config, tensor_scale: torch.Tensor | None = None,
+                      guide_bits: torch.Tensor | None = None, guide_scales: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 dequantization of the quantized x in one pass (guided when a guide is given)."""
+    _on_gpu(x, tensor_scale, guide_bits, guide_scales, out)
+    rows, cols, ld = _matrix(x)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+    ld_out = out.stride(0) if rows > 1 else cols
+    guided = guide_bits is not None
+    c = cfg.c()
+    _check(lib().fp4_fake_quantize(C.byref(c), int(guided), _ptr(x), rows, cols, ld, _ptr(tensor_scale),
+                                   _ptr(guide_bits), _ptr(guide_scales), _ptr(out), ld_out, _stream(x)),
+           "fp4_fake_quantize")
+    return out
 
 
 def fp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, cfg: Fp4Config, rows: int, cols: int,

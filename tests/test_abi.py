@@ -94,3 +94,22 @@ def test_binding_refuses_cpu_tensors(fq):
     x = torch.zeros(4, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fq.fp4_quantize(x, fq.Fp4Config(), torch.ones(1))
+
+
+def test_grouped_host_side_errors(fq):
+    L = fq.lib()
+    A = 1 << 20
+    cfg = fq.Fp4Config().c()
+    arr = (fq._CTensor * 17)()
+    for t in range(17):
+        arr[t] = fq._CTensor(A, 4, 32, 32, A, A, A, None, None)
+    assert L.fp4_quantize_grouped(C.byref(cfg), 0, 0, arr, None) == 1
+    assert L.fp4_quantize_grouped(C.byref(cfg), 0, 17, arr, None) == 1
+    assert L.fp4_quantize_grouped(C.byref(cfg), 0, 2, None, None) == 1
+    arr[1] = fq._CTensor(A, 4, 24, 24, A, A, A, None, None)          # cols % 16
+    assert L.fp4_quantize_grouped(C.byref(cfg), 0, 2, arr, None) == 2
+    assert "tensor 1" in L.fp4_last_error().decode()
+    arr[1] = fq._CTensor(A, 4, 32, 32, A, A, A, A, None)             # emission on one tensor only
+    assert L.fp4_quantize_grouped(C.byref(cfg), 0, 2, arr, None) == 1
+    arr[1] = fq._CTensor(A, 4, 32, 32, A, A, A, None, None)
+    assert L.fp4_quantize_grouped(C.byref(cfg), 1, 2, arr, None) == 1  # guided needs guides
