@@ -7,22 +7,28 @@ bf16 Student-t(4) values, 32-element blocks with E8M0 scales:
   1. rollout side: RTN quantize of the rollout copy x_r,
   2. guide_pack of its codes and scales (1 mantissa bit + block scale),
   3. trainer side: guided quantize of x with that guide,
-  4. stochastic rounding (Philox, key 1) of an activation batch of the same
+  4. dequantize of the guided codes to bf16,
+  5. stochastic rounding (Philox, key 1) of an activation batch of the same
      shape (the previous batch's x, so no input is re-read from the last-level
-     cache within a step),
-  5. dequantize of the guided codes to bf16.
-``value`` = algorithmic bytes of the step / step time, in GB/s.  Inputs are
-resident in HBM before timing; a rotating pool of input sets (>= 768 MiB)
-keeps the 256 MB Infinity Cache from serving re-reads across steps.
+     cache within a step).
+Kernels 1-4 form a dependent chain on one stream; kernel 5 depends on none of
+them and runs on a second stream (default priority), so its ALU-heavy rounding
+overlaps the memory-bound chain.  ``--streams 1`` serializes all five.
+``value`` = algorithmic bytes of the step / step time, in GB/s, measured with
+HIP events around K whole steps.  Inputs are resident in HBM before timing; a
+rotating pool of input sets (768 MiB) keeps the 256 MB Infinity Cache from
+serving re-reads across steps.
 
-The other workloads (NVFP4 activation 4096x2048 with RTN/guided, the KV cache
-at 131072 tokens, one deep guidance-cache layer, the uniform grid with RHT16
-and SR on a 65536x8192 GEMM operand) are timed after it and reported under
-"workloads".  Per-kernel durations come from HIP events recorded on the
-stream the kernels run on.  The CPU baseline is the oracle timed on a
-bounded row sample of the headline step.
+Per kernel, two durations are reported: with events around every launch inside
+the steps, and as back-to-back launches of that kernel alone (events around
+the loop); the latter is the roofline figure and compares directly with
+rocprofv3's kernel durations.  The other workloads (NVFP4 activation 4096x2048,
+KV cache at 131072 tokens, one deep guidance-cache layer, uniform grid + RHT16
++ SR on a 65536x8192 GEMM operand) are timed back to back and reported under
+"workloads".  The CPU baseline is the oracle timed on a bounded row sample of
+the headline step.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--streams 1|2]
 """
 from __future__ import annotations
 
@@ -50,6 +56,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--streams", type=int, default=2, choices=(1, 2))
     ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the CPU-baseline sample")
@@ -87,6 +94,21 @@ class KernelTimer:
         return {k: (tot[k] / cnt[k], cnt[k]) for k in tot}
 
 
+def back_to_back(torch, fn, reps, warm=2):
+    """Average ms of `fn(i)` over `reps` consecutive launches on the current stream."""
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def source_sha():
     h = hashlib.sha256()
     for f in ["device.h", "internal.h", "quantize.hip", "misc.hip", "abi.hip"]:
@@ -111,8 +133,28 @@ def read_traffic(kernel_key: str, sha: str):
     return None
 
 
+def report(ms, nbytes, n, ceiling=None):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    r = {"us": round(ms * 1e3, 2), "bytes": int(nbytes), "GBps": round(gbs, 1),
+         "Gelem_per_s": round(n / (ms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    if ceiling:
+        r["frac_copy_ceiling"] = round(gbs / ceiling, 4)
+    return r
+
+
+# ---------------------------------------------------------------- copy ceiling
+def copy_ceiling(torch, fq, mib=256, reps=20):
+    """The library's plain streaming copy (16 B per lane): the practical bandwidth reference."""
+    n = mib * (1 << 20)
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    for b in bufs:
+        b.fill_(1)
+    ms = back_to_back(torch, lambda i: fq.fp4_stream_copy(bufs[(2 * i) % 4], bufs[(2 * i + 1) % 4]), reps)
+    return {"bytes_per_launch": 2 * n, "us": round(ms * 1e3, 2), "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
 # ---------------------------------------------------------------- headline step
-def headline(args, fq, torch, W):
+def headline(args, fq, torch, W, ceiling):
     rows, cols = W.c2_shape()
     n = rows * cols
     log(f"generating C2 {rows}x{cols} Student-t(4) ...")
@@ -128,6 +170,7 @@ def headline(args, fq, torch, W):
     outs = [dict(rc=u8(n // 2), rs=u8(n // B), gb=u8(n // 8), gs=u8(n // B), gc=u8(n // 2), gsc=u8(n // B),
                  sc=u8(n // 2), ss=u8(n // B), dq=torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda"))
             for _ in range(P)]
+    chain = ["quantize_rtn", "guide_pack", "quantize_guided", "dequantize_bf16"]
 
     def step_fns(k):
         s = k % P
@@ -137,100 +180,76 @@ def headline(args, fq, torch, W):
             "guide_pack": lambda: fq.guide_pack(o["rc"], o["rs"], cfg_rtn, rows, cols, bits=o["gb"], gscales=o["gs"]),
             "quantize_guided": lambda: fq.fp4_quantize_guided(xs[s], cfg_rtn, o["gb"], o["gs"], None,
                                                               codes=o["gc"], scales=o["gsc"]),
-            "quantize_sr": lambda: fq.fp4_quantize(xs[(s + 2) % P], cfg_sr, None, codes=o["sc"], scales=o["ss"]),
             "dequantize_bf16": lambda: fq.fp4_dequantize(o["gc"], o["gsc"], cfg_rtn, rows, cols, None, out=o["dq"]),
+            "quantize_sr": lambda: fq.fp4_quantize(xs[(s + 2) % P], cfg_sr, None, codes=o["sc"], scales=o["ss"]),
         }
-
-    def one(fn):
-        fn()
-
-    def step(k, timer=None):
-        for name, fn in step_fns(k).items():
-            if timer:
-                timer.run(name, fn)
-            else:
-                fn()
 
     bytes_per = {  # algorithmic bytes per element of each kernel (MXFP4, B = 32)
         "quantize_rtn": 2 + 0.5 + 1 / 32,
         "guide_pack": 0.5 + 1 / 32 + 1 / 8 + 1 / 32,
         "quantize_guided": 2 + 1 / 8 + 1 / 32 + 0.5 + 1 / 32,
-        "quantize_sr": 2 + 0.5 + 1 / 32,
         "dequantize_bf16": 0.5 + 1 / 32 + 2,
+        "quantize_sr": 2 + 0.5 + 1 / 32,
     }
     step_bytes = sum(bytes_per.values()) * n
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # default priority
 
-    log("warmup ...")
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    # timed region 1: whole steps, no per-kernel events
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record()
-    for k in range(args.steps):
-        step(k)
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t0.elapsed_time(t1) / args.steps
-    # timed region 2: the same steps with events around every kernel
+    def step(k, streams):
+        f = step_fns(k)
+        if streams == 2:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                f["quantize_sr"]()
+            for name in chain:
+                f[name]()
+            main.wait_stream(side)
+        else:
+            for name in chain + ["quantize_sr"]:
+                f[name]()
+
+    def timed_steps(streams):
+        for k in range(args.warmup):
+            step(k, streams)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for k in range(args.steps):
+            step(k, streams)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    log("timing steps ...")
+    ms_serial = timed_steps(1)
+    ms_step = timed_steps(args.streams) if args.streams == 2 else ms_serial
+    # events around every kernel inside serialized steps
     timer = KernelTimer()
-    torch.cuda.synchronize()
     for k in range(args.steps):
-        step(k, timer)
+        for name, fn in step_fns(k).items():
+            timer.run(name, fn)
     torch.cuda.synchronize()
-    ks = timer.summary()
     kernels = {}
-    for name, (ms, cnt) in ks.items():
-        b = bytes_per[name] * n
-        kernels[name] = {"us": round(ms * 1e3, 2), "launches": cnt, "bytes": int(b),
-                         "GBps": round(b / (ms * 1e-3) / 1e9, 1), "Gelem_per_s": round(n / (ms * 1e-3) / 1e9, 1),
-                         "frac_hbm_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    # back-to-back launches of each kernel alone (events around the loop): the average
-    # launch duration used for the roofline, comparable with rocprofv3's kernel durations
-    single = {}
+    for name, (ms, cnt) in timer.summary().items():
+        kernels[name] = dict(report(ms, bytes_per[name] * n, n, ceiling), launches=cnt)
+    # back-to-back launches of each kernel alone: the roofline figure
     for name in kernels:
-        t_a = torch.cuda.Event(enable_timing=True)
-        t_b = torch.cuda.Event(enable_timing=True)
-        reps = args.steps
-        for k in range(2):
-            one(step_fns(k)[name])
-        torch.cuda.synchronize()
-        t_a.record()
-        for k in range(reps):
-            step_fns(k)[name]()
-        t_b.record()
-        torch.cuda.synchronize()
-        single[name] = t_a.elapsed_time(t_b) / reps
-    for name, ms in single.items():
-        b = bytes_per[name] * n
-        kernels[name]["us_back_to_back"] = round(ms * 1e3, 2)
-        kernels[name]["GBps_back_to_back"] = round(b / (ms * 1e-3) / 1e9, 1)
-    return dict(rows=rows, cols=cols, n=n, ms_step=ms_step, wall=wall, step_bytes=step_bytes,
-                kernels=kernels, bytes_per=bytes_per, x_h=x_h, xr_h=xr_h, outs=outs[0], cfg_rtn=cfg_rtn,
-                cfg_sr=cfg_sr, xs=xs)
+        ms = back_to_back(torch, lambda i: step_fns(i)[name](), args.steps)
+        r = report(ms, bytes_per[name] * n, n, ceiling)
+        kernels[name]["us_back_to_back"] = r["us"]
+        kernels[name]["GBps_back_to_back"] = r["GBps"]
+        kernels[name]["frac_hbm_peak_back_to_back"] = r["frac_hbm_peak"]
+    # guided fake quantization (quantize -> bf16 in one pass), the QAT forward op
+    fqo = [torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    ms = back_to_back(torch, lambda i: fq.fp4_fake_quantize(xs[i % P], cfg_rtn, None, outs[i % P]["gb"],
+                                                            outs[i % P]["gs"], out=fqo[i % P]), args.steps)
+    fake = report(ms, (2 + 1 / 8 + 1 / 32 + 2) * n, n, ceiling)
+    return dict(rows=rows, cols=cols, n=n, ms_step=ms_step, ms_serial=ms_serial, step_bytes=step_bytes,
+                kernels=kernels, bytes_per=bytes_per, x_h=x_h, xr_h=xr_h, outs=outs[0], fake=fake)
 
 
-def copy_ceiling(torch, mib=256, iters=20):
-    """A plain streaming read+write of known size (torch's vectorized elementwise kernel,
-    y = -x in fp32): the practical streaming ceiling next to the quantize kernels."""
-    n = mib * (1 << 20) // 4
-    bufs = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(4)]
-    for b in bufs:
-        b.fill_(1.0)
-    timer = KernelTimer()
-    for i in range(iters):
-        timer.run("copy", lambda: torch.neg(bufs[(2 * i) % 4], out=bufs[(2 * i + 1) % 4]))
-    torch.cuda.synchronize()
-    ms = timer.summary()["copy"][0]
-    return {"bytes_per_launch": 2 * n * 4, "us": round(ms * 1e3, 2),
-            "GBps": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}
-
-
-def parity_sample(fq, torch, W, h, oracle_mod, rows_s=64):
+def parity_sample(torch, h, oracle_mod, rows_s=64):
     """Compare the headline step's slot-0 outputs with the oracle on the first rows."""
     O = oracle_mod
     cols = h["cols"]
@@ -259,8 +278,8 @@ def cpu_baseline(args, W, oracle_mod, h):
     rc, rs = O.quantize(oc, O.RTN, xr)
     gb, gs = O.guide_pack(oc, rc, rs, R, cols)
     gc, gsc = O.quantize(oc, O.GUIDED, x, guide_bits=gb, guide_scales=gs)
-    O.quantize(osr, O.SR, x)
     O.dequantize(oc, gc, gsc, 1.0, R, cols, out_bf16=True)
+    O.quantize(osr, O.SR, x)
     dt = time.perf_counter() - t
     b = sum(h["bytes_per"].values()) * R * cols
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -269,26 +288,7 @@ def cpu_baseline(args, W, oracle_mod, h):
 
 
 # ---------------------------------------------------------------- other workloads
-def time_loop(torch, fns, iters):
-    """Average ms of each named callable over `iters` rounds, events around each call."""
-    timer = KernelTimer()
-    for name, fn in fns:  # warm
-        fn()
-    torch.cuda.synchronize()
-    for _ in range(iters):
-        for name, fn in fns:
-            timer.run(name, fn)
-    torch.cuda.synchronize()
-    return {k: v[0] for k, v in timer.summary().items()}
-
-
-def report(ms, nbytes, n):
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"us": round(ms * 1e3, 2), "bytes": int(nbytes), "GBps": round(gbs, 1),
-            "Gelem_per_s": round(n / (ms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
-
-
-def other_workloads(args, fq, torch, W):
+def other_workloads(args, fq, torch, W, ceiling):
     res = {}
     it = args.config_iters
     u8 = lambda k: torch.empty(k, dtype=torch.uint8, device="cuda")
@@ -296,7 +296,7 @@ def other_workloads(args, fq, torch, W):
     # NVFP4 activation 4096x2048 (16 MiB): a pool of 32 copies keeps it out of the caches
     rows, cols = W.c1_shape()
     n = rows * cols
-    log("C1 ...")
+    log("NVFP4 activation 4096x2048 ...")
     x0, xr0 = to_dev(W.c1_x(rows, cols)), to_dev(W.c1_rollout(rows, cols))
     cfg = fq.Fp4Config()
     P = 32
@@ -305,100 +305,79 @@ def other_workloads(args, fq, torch, W):
     tss = [fq.fp4_tensor_scale(xr, cfg) for xr in xrs]
     guides = [fq.fp4_quantize(xrs[s], cfg, tss[s], emit=True) for s in range(P)]
     oc, os_, ob = u8(n // 2), u8(n // 16), u8(n // 8)
-    k = [0]
-
-    def nxt():
-        k[0] = (k[0] + 1) % P
-        return k[0]
-    ms = time_loop(torch, [
-        ("tensor_scale", lambda: fq.fp4_tensor_scale(xs[nxt()], cfg, out=tss[k[0]])),
-        ("quantize_rtn", lambda: fq.fp4_quantize(xs[nxt()], cfg, tss[k[0]], codes=oc, scales=os_)),
-        ("quantize_rtn_emit", lambda: fq.fp4_quantize(xs[nxt()], cfg, tss[k[0]], emit=True, codes=oc, scales=os_, bits=ob)),
-        ("quantize_guided", lambda: fq.fp4_quantize_guided(xs[nxt()], cfg, guides[k[0]][2], guides[k[0]][1], tss[k[0]], codes=oc, scales=os_)),
-    ], it)
-    res["nvfp4_act_4096x2048"] = {
-        "tensor_scale": report(ms["tensor_scale"], 2 * n, n),
-        "quantize_rtn": report(ms["quantize_rtn"], 2.5625 * n, n),
-        "quantize_rtn_emit": report(ms["quantize_rtn_emit"], 2.6875 * n, n),
-        "quantize_guided": report(ms["quantize_guided"], 2.75 * n, n),
-    }
+    tso = torch.empty(1, dtype=torch.float32, device="cuda")
+    r = {}
+    r["tensor_scale"] = report(back_to_back(torch, lambda i: fq.fp4_tensor_scale(xs[i % P], cfg, out=tso), it), 2 * n, n, ceiling)
+    r["quantize_rtn"] = report(back_to_back(torch, lambda i: fq.fp4_quantize(xs[i % P], cfg, tss[i % P], codes=oc, scales=os_), it), 2.5625 * n, n, ceiling)
+    r["quantize_rtn_emit"] = report(back_to_back(torch, lambda i: fq.fp4_quantize(xs[i % P], cfg, tss[i % P], emit=True, codes=oc, scales=os_, bits=ob), it), 2.6875 * n, n, ceiling)
+    r["quantize_guided"] = report(back_to_back(torch, lambda i: fq.fp4_quantize_guided(xs[i % P], cfg, guides[i % P][2], guides[i % P][1], tss[i % P], codes=oc, scales=os_), it), 2.75 * n, n, ceiling)
+    res["nvfp4_act_4096x2048"] = r
     del xs, xrs, guides
 
-    # KV cache: K and V each (131072*8) x 128, NVFP4 along head_dim
+    # KV cache: K and V each (131072*8) x 128, NVFP4 along head_dim; K and V in one grouped launch
     rows, cols = W.c3_shape()
     n = rows * cols
-    log("C3 ...")
+    log("KV cache 131072 tokens ...")
     K, V = to_dev(W.c3_kv(0)), to_dev(W.c3_kv(1))
     tk, tv = fq.fp4_tensor_scale(K, cfg), fq.fp4_tensor_scale(V, cfg)
-    kc, ks_, vc, vs = u8(n // 2), u8(n // 16), u8(n // 2), u8(n // 16)
+    kv_out = [(u8(n // 2), u8(n // 16)), (u8(n // 2), u8(n // 16))]
     kd = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
     vd = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
-    ms = time_loop(torch, [
-        ("quantize_k", lambda: fq.fp4_quantize(K, cfg, tk, codes=kc, scales=ks_)),
-        ("quantize_v", lambda: fq.fp4_quantize(V, cfg, tv, codes=vc, scales=vs)),
-        ("dequantize_k", lambda: fq.fp4_dequantize(kc, ks_, cfg, rows, cols, tk, out=kd)),
-        ("dequantize_v", lambda: fq.fp4_dequantize(vc, vs, cfg, rows, cols, tv, out=vd)),
-    ], it)
-    res["nvfp4_kv_131072x8x128"] = {
-        "quantize_kv": report(ms["quantize_k"] + ms["quantize_v"], 2 * 2.5625 * n, 2 * n),
-        "dequantize_kv_bf16": report(ms["dequantize_k"] + ms["dequantize_v"], 2 * 2.5625 * n, 2 * n),
-    }
+    r = {}
+    r["quantize_kv_grouped"] = report(back_to_back(torch, lambda i: fq.fp4_quantize_grouped([K, V], cfg, [tk, tv], outs=kv_out), it), 2 * 2.5625 * n, 2 * n, ceiling)
+
+    def deq(i):
+        fq.fp4_dequantize(kv_out[0][0], kv_out[0][1], cfg, rows, cols, tk, out=kd)
+        fq.fp4_dequantize(kv_out[1][0], kv_out[1][1], cfg, rows, cols, tv, out=vd)
+    r["dequantize_kv_bf16"] = report(back_to_back(torch, deq, it), 2 * 2.5625 * n, 2 * n, ceiling)
+    res["nvfp4_kv_131072x8x128"] = r
     del K, V, kd, vd
 
-    # one deep guidance-cache layer: 8 experts 4096x1536 + activations 8192x4096
-    log("C4 ...")
-    tens = []
-    for name, r, c, sigma, seed, stream in W.c4_tensors(20):
-        xh, xrh = W.c4_pair(r, c, sigma, seed, stream)
-        tens.append((to_dev(xh), to_dev(xrh), r, c))
-    n_layer = sum(r * c for _, _, r, c in tens)
-    bufs = []
-    for x, xr, r, c in tens:
-        m = r * c
-        ts = fq.fp4_tensor_scale(xr, cfg)
-        bufs.append(dict(x=x, xr=xr, r=r, c=c, ts=ts, rc=u8(m // 2), rs=u8(m // 16), gb=u8(m // 8),
-                         gs=u8(m // 16), gc=u8(m // 2), gsc=u8(m // 16)))
+    # one deep guidance-cache layer: 8 expert slices 4096x1536 + activations 8192x4096, grouped
+    log("guidance-cache layer ...")
+    xs, xrs, shapes = [], [], []
+    for name, rr, cc, sigma, seed, stream in W.c4_tensors(20):
+        xh, xrh = W.c4_pair(rr, cc, sigma, seed, stream)
+        xs.append(to_dev(xh))
+        xrs.append(to_dev(xrh))
+        shapes.append((rr, cc))
+    n_layer = sum(rr * cc for rr, cc in shapes)
+    tss = [fq.fp4_tensor_scale(x, cfg) for x in xrs]
+    roll = [(u8(rr * cc // 2), u8(rr * cc // 16), u8(rr * cc // 8)) for rr, cc in shapes]
+    tr = [(u8(rr * cc // 2), u8(rr * cc // 16)) for rr, cc in shapes]
+    fq.fp4_quantize_grouped(xrs, cfg, tss, emit=True, outs=roll)
+    guides = [(o[2], o[1]) for o in roll]
+    pk = [(u8(rr * cc // 8), u8(rr * cc // 16)) for rr, cc in shapes]
 
-    def rollout():
-        for b in bufs:
-            fq.fp4_quantize(b["xr"], cfg, b["ts"], codes=b["rc"], scales=b["rs"])
-
-    def pack():
-        for b in bufs:
-            fq.guide_pack(b["rc"], b["rs"], cfg, b["r"], b["c"], bits=b["gb"], gscales=b["gs"])
-
-    def trainer():
-        for b in bufs:
-            fq.fp4_quantize_guided(b["x"], cfg, b["gb"], b["gs"], b["ts"], codes=b["gc"], scales=b["gsc"])
-    ms = time_loop(torch, [("rollout_rtn", rollout), ("guide_pack", pack), ("trainer_guided", trainer)], it)
+    def pack(i):
+        for (rr, cc), o, p in zip(shapes, roll, pk):
+            fq.guide_pack(o[0], o[1], cfg, rr, cc, bits=p[0], gscales=p[1])
+    r = {}
+    r["rollout_rtn_emit_grouped"] = report(back_to_back(torch, lambda i: fq.fp4_quantize_grouped(xrs, cfg, tss, emit=True, outs=roll), it), 2.6875 * n_layer, n_layer, ceiling)
+    r["trainer_guided_grouped"] = report(back_to_back(torch, lambda i: fq.fp4_quantize_grouped(xs, cfg, tss, guides=guides, outs=tr), it), 2.75 * n_layer, n_layer, ceiling)
+    r["guide_pack_9_launches"] = report(back_to_back(torch, pack, it), 0.75 * n_layer, n_layer, ceiling)
     per_layer_guide = n_layer // 8 + n_layer // 16
     per_layer_full = n_layer // 2 + n_layer // 16
-    res["guide_cache_layer_8x4096x1536_plus_8192x4096"] = {
-        "rollout_rtn": report(ms["rollout_rtn"], 2.5625 * n_layer, n_layer),
-        "guide_pack": report(ms["guide_pack"], 0.75 * n_layer, n_layer),
-        "trainer_guided": report(ms["trainer_guided"], 2.75 * n_layer, n_layer),
-        "cache_bytes_20_deep_layers": per_layer_guide * 20,
-        "full_codes_scales_40_layers": per_layer_full * 40,
-        "cache_ratio": round(per_layer_guide * 20 / (per_layer_full * 40), 6),
-    }
-    del tens, bufs
+    r["cache_bytes_20_deep_layers"] = per_layer_guide * 20
+    r["full_codes_scales_40_layers"] = per_layer_full * 40
+    r["cache_ratio"] = round(per_layer_guide * 20 / (per_layer_full * 40), 6)
+    res["guide_cache_layer_8x4096x1536_plus_8192x4096"] = r
+    del xs, xrs, roll, tr, guides, pk
 
     # uniform grid + RHT16 + SR on a 65536x8192 GEMM operand (1 GiB)
     rows, cols = W.c5_shape()
     n = rows * cols
-    log("C5 (generating 1 GiB) ...")
+    log("uniform + RHT16 + SR 65536x8192 (generating 1 GiB) ...")
     x = to_dev(W.c5_x(rows, cols))
     cfg5 = fq.Fp4Config(grid=fq.UNIFORM, rounding=fq.SR, rht16=True, rht_seed=W.C5_RHT_SEED, sr_seed=W.C5_SR_SEED)
     ts = fq.fp4_tensor_scale(x, cfg5)
     c5c, c5s = u8(n // 2), u8(n // 16)
-    ms = time_loop(torch, [
-        ("tensor_scale_rht", lambda: fq.fp4_tensor_scale(x, cfg5, out=ts)),
-        ("quantize_rht_sr_uniform", lambda: fq.fp4_quantize(x, cfg5, ts, codes=c5c, scales=c5s)),
-    ], max(5, it // 2))
-    res["uniform_rht16_sr_65536x8192"] = {
-        "tensor_scale_rht": report(ms["tensor_scale_rht"], 2 * n, n),
-        "quantize_rht_sr_uniform": report(ms["quantize_rht_sr_uniform"], 2.5625 * n, n),
-    }
+    tso = torch.empty(1, dtype=torch.float32, device="cuda")
+    k5 = max(5, it // 2)
+    r = {}
+    r["tensor_scale_rht"] = report(back_to_back(torch, lambda i: fq.fp4_tensor_scale(x, cfg5, out=tso), k5), 2 * n, n, ceiling)
+    r["quantize_rht_sr_uniform"] = report(back_to_back(torch, lambda i: fq.fp4_quantize(x, cfg5, ts, codes=c5c, scales=c5s), k5), 2.5625 * n, n, ceiling)
+    res["uniform_rht16_sr_65536x8192"] = r
     del x
     return res
 
@@ -406,8 +385,8 @@ def other_workloads(args, fq, torch, W):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part "
-              "of this path", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); runs on several GPUs are not "
+              "part of this path", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -417,19 +396,17 @@ def main():
     fq.lib()
     torch.cuda.set_device(0)
 
-    h = headline(args, fq, torch, W)
-    ceiling = copy_ceiling(torch)
-    for k in h["kernels"].values():
-        k["frac_copy_ceiling"] = round(k["GBps"] / ceiling["GBps"], 4)
+    ceiling = copy_ceiling(torch, fq)
+    h = headline(args, fq, torch, W, ceiling["GBps"])
     import oracle as oracle_mod  # CPU baseline and the parity sample only
-    parity = parity_sample(fq, torch, W, h, oracle_mod)
+    parity = parity_sample(torch, h, oracle_mod)
     if not parity:
         log("PARITY FAILURE on the headline sample")
     cpu = None
     if not (args.quick or args.no_cpu_baseline):
         log("CPU baseline (oracle) ...")
         cpu = cpu_baseline(args, W, oracle_mod, h)
-    workloads = {} if args.quick else other_workloads(args, fq, torch, W)
+    workloads = {} if args.quick else other_workloads(args, fq, torch, W, ceiling["GBps"])
 
     n = h["n"]
     value = h["step_bytes"] / (h["ms_step"] * 1e-3) / 1e9
@@ -437,7 +414,6 @@ def main():
     dk = h["kernels"][dom]
     ach = dk["GBps_back_to_back"]
     sha = source_sha()
-    traffic = read_traffic(f"{dom}@c2", sha)
     out = {
         "metric": "FP4 quantize GB/s and Gelem/s (RTN & guided) as % of MI355X HBM peak",
         "value": round(value, 1),
@@ -446,26 +422,31 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(h["ms_step"], 4),
+        "ms_per_step_serial": round(h["ms_serial"], 4),
+        "streams": args.streams,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "MXFP4 MoE expert activations 16384x4096 bf16 Student-t(4): rollout RTN "
-                               "quantize + guide_pack, trainer guided quantize, SR quantize (Philox key 1), "
-                               "dequantize to bf16",
+                               "quantize + guide_pack, trainer guided quantize, dequantize to bf16, SR "
+                               "quantize (Philox key 1) of the previous batch",
                    "rows": h["rows"], "cols": h["cols"], "block": 32, "scale": "E8M0",
-                   "elements_per_step": n, "bytes_per_step": int(h["step_bytes"])},
+                   "elements_per_kernel": n, "bytes_per_step": int(h["step_bytes"])},
         "gelem_per_s": round(5 * n / (h["ms_step"] * 1e-3) / 1e9, 1),
         "frac_hbm_peak": round(value / PEAK_HBM_GBS, 4),
+        "frac_copy_ceiling": round(value / ceiling["GBps"], 4),
         "parity_sample_ok": parity,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "traffic": read_traffic(f"{dom}@c2", sha),
                      "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": dk["us_back_to_back"],
                      "avg_launch_us_in_step": dk["us"]},
         "cpu_baseline": cpu,
         "copy_ceiling": ceiling,
         "kernels": h["kernels"],
+        "fake_quantize_guided_bf16": h["fake"],
         "workloads": workloads,
         "source_sha": sha,
     }

@@ -203,6 +203,12 @@ fp4_status fp4_rht16(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld,
 fp4_status fp4_encode_values(int grid, int mode, const float* v, const uint8_t* aux, int64_t n,
                              uint8_t* out, hipStream_t stream);
 
+/* Plain streaming copy of `bytes` (a multiple of 16) from src to dst, one
+ * 16-byte load and store per lane: the practical HBM bandwidth reference the
+ * quantize kernels are measured against.  Both pointers 16-byte aligned;
+ * the ranges must not overlap. */
+fp4_status fp4_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
 /* Buffer sizes in bytes. */
 size_t fp4_codes_bytes(int64_t rows, int64_t cols);
 size_t fp4_scales_bytes(int format, int64_t rows, int64_t cols);

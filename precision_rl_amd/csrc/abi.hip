@@ -345,6 +345,17 @@ fp4_status fp4_rht16(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld,
                       "rht16 launch");
 }
 
+fp4_status fp4_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return ok();
+    if (bytes % 16 != 0) return fail(FP4_ERR_SHAPE, "bytes=%zu is not a multiple of 16", bytes);
+    if (bytes / 16 / fp4q::kThreads >= (1ull << 31)) return fail(FP4_ERR_SHAPE, "copy too large");
+    FP4Q_TRY(need(src, 16, "src"));
+    FP4Q_TRY(need(dst, 16, "dst"));
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + bytes && b < a + bytes) return fail(FP4_ERR_ARG, "src and dst overlap");
+    return hip_status(fp4q::launch_stream_copy(src, dst, bytes / 16, stream), "stream copy launch");
+}
+
 fp4_status fp4_encode_values(int grid, int mode, const float* v, const uint8_t* aux, int64_t n,
                              uint8_t* out, hipStream_t stream) {
     if (grid != FP4_GRID_E2M1 && grid != FP4_GRID_UNIFORM) return fail(FP4_ERR_ARG, "unknown grid %d", grid);

@@ -228,6 +228,14 @@ __global__ __launch_bounds__(kThreads) void k_encode_values(const EncodeParams p
     reinterpret_cast<uint2*>(p.out)[t] = make_uint2(lo, hi);
 }
 
+// ---------------------------------------------------------------- reference copy
+
+__global__ __launch_bounds__(kThreads) void k_stream_copy(const v4u32* __restrict__ src,
+                                                          v4u32* __restrict__ dst, uint64_t n16) {
+    const uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n16) dst[i] = __builtin_nontemporal_load(src + i);
+}
+
 inline uint32_t blocks_for(uint32_t n) { return (n + kThreads - 1) / kThreads; }
 
 }  // namespace
@@ -288,6 +296,13 @@ hipError_t launch_rht16(bool inverse, bool bf16_out, bool contig, const RhtParam
         else { if (contig) FP4Q_RH(false, false, true); else FP4Q_RH(false, false, false); }
     }
 #undef FP4Q_RH
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n16, hipStream_t s) {
+    const uint64_t blocks = (n16 + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(k_stream_copy, dim3((uint32_t)blocks), dim3(kThreads), 0, s,
+                       static_cast<const v4u32*>(src), static_cast<v4u32*>(dst), n16);
     return hipGetLastError();
 }
 

@@ -71,7 +71,7 @@ MAX_GROUP = 16
 _lib = None
 EXPORTS = ("fp4_tensor_scale", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
            "fp4_fake_quantize", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_rht16",
-           "fp4_encode_values", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
+           "fp4_encode_values", "fp4_stream_copy", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
            "fp4_status_str", "fp4_last_error")
 
 
@@ -97,6 +97,7 @@ def lib():
         "guide_unpack": [CP, P, P, I64, I64, P, P, P],
         "fp4_rht16": [P, I64, I64, I64, C.c_uint64, I, P, I, P],
         "fp4_encode_values": [I, I, P, P, I64, P, P],
+        "fp4_stream_copy": [P, P, C.c_size_t, P],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -313,6 +314,16 @@ def fp4_encode_values(v: torch.Tensor, grid: int, mode: int, aux: torch.Tensor |
     _check(lib().fp4_encode_values(grid, mode, _ptr(v), _ptr(aux), n, _ptr(out), _stream(v)),
            "fp4_encode_values")
     return out
+
+
+def fp4_stream_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """Reference streaming copy of src's bytes into dst (same byte size, contiguous)."""
+    _on_gpu(src, dst)
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("stream copy needs contiguous tensors of equal byte size")
+    _check(lib().fp4_stream_copy(_ptr(src), _ptr(dst), nb, _stream(src)), "fp4_stream_copy")
+    return dst
 
 
 def codes_bytes(rows: int, cols: int) -> int:
