@@ -55,9 +55,14 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB) or os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC):
-            _build.build()
-        L = C.CDLL(_build.LIB)
+        # FP4Q_ORACLE_LIB names another build of the same source; the mutation
+        # tests point it at copies with a planted mistake to show the pins fail.
+        path = os.environ.get("FP4Q_ORACLE_LIB")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+                _build.build()
+        L = C.CDLL(path)
         P = C.c_void_p
         I64 = C.c_int64
         F = C.c_float

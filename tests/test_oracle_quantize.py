@@ -108,7 +108,8 @@ def test_nvfp4_rtn_matches_independent_pipeline(orc, grid):
 @pytest.mark.parametrize("ts", [1.0, 0.37, 1e-3, 2.0 ** -120, 7.5e37 / 2688])
 def test_nvfp4_scale_rule_at_extreme_tensor_scales(orc, ts):
     rng = np.random.default_rng(9)
-    x = (rng.standard_normal((16, 64)) * rng.choice([1e-30, 1e-3, 1, 1e3], (16, 1))).astype(np.float32)
+    # 1e-38 rows at ts = 2^-120 give block scales S = d*ts below 2^-128, where 1/S overflows
+    x = (rng.standard_normal((16, 64)) * rng.choice([1e-38, 1e-30, 1e-3, 1, 1e3], (16, 1))).astype(np.float32)
     xh = _bf16(x)
     cfg = orc.Cfg(format=orc.NVFP4)
     codes, scales = orc.quantize(cfg, orc.RTN, xh, np.float32(ts))
@@ -123,6 +124,22 @@ def test_mxfp4_rtn_matches_frexp_pipeline(orc, grid):
     codes, scales = orc.quantize(cfg, orc.RTN, xh)
     rc, rs = numpy_mxfp4_rtn(xh, grid)
     assert (scales == rs).all() and (codes == rc).all()
+
+
+@pytest.mark.parametrize("grid", [0, 1])
+def test_mxfp4_rtn_at_extreme_magnitudes(orc, grid):
+    # block amax from the smallest bf16 subnormal (2^-133, exponent clamped at -127)
+    # up to the largest finite bf16 value
+    rng = np.random.default_rng(11)
+    mags = np.float32([2.0 ** -133, 2.0 ** -130, 2.0 ** -127, 2.0 ** -125, 1e-30, 1.0, 1e30, 3.0e38])
+    x = (rng.uniform(-1, 1, (8, 64)) * mags[:, None]).astype(np.float32)
+    x[:, 0] = mags  # each row's amax is its magnitude
+    xh = _bf16(x)
+    cfg = orc.Cfg(format=orc.MXFP4, grid=grid)
+    codes, scales = orc.quantize(cfg, orc.RTN, xh)
+    rc, rs = numpy_mxfp4_rtn(xh, grid)
+    assert (scales == rs).all() and (codes == rc).all()
+    assert scales[0] == 0 and scales[-1] == 125 + 127
 
 
 def test_tensor_scale_is_amax_over_2688(orc):
@@ -179,6 +196,60 @@ def test_guided_invariants_against_a_perturbed_rollout(orc):
     own, _ = orc.quantize(cfg, orc.RTN, x, ts_r)
     ok = _unpack(own) & 7
     assert (k == rk).mean() >= (ok == rk).mean()
+
+
+def test_guided_takes_block_scales_from_the_guide(orc):
+    # the rollout is the tensor scaled by 1.7 (bf16), so its block scales differ from
+    # the ones the tensor would get on its own; guided output must keep the guide's
+    R, C = 32, 256
+    x = W.c5_x(R, C, seed=6)
+    xr = _bf16(_f32(x) * np.float32(1.7))
+    for fmt in (orc.NVFP4, orc.MXFP4):
+        cfg = orc.Cfg(format=fmt)
+        B = cfg.block
+        ts = orc.tensor_scale(cfg, xr) if fmt == orc.NVFP4 else 1.0
+        rc, rs = orc.quantize(cfg, orc.RTN, xr, ts)
+        own_c, own_s = orc.quantize(cfg, orc.RTN, x, ts)
+        assert (own_s != rs).mean() > 0.5
+        gb, gs = orc.guide_pack(cfg, rc, rs, R, C)
+        gc, gsc = orc.quantize(cfg, orc.GUIDED, x, ts, guide_bits=gb, guide_scales=gs)
+        assert (gsc == rs).all()
+        xf = torch.from_numpy(_f32(x).reshape(R, C // B, B).copy())
+        if fmt == orc.NVFP4:
+            d = torch.from_numpy(gs.copy()).view(torch.float8_e4m3fn).to(torch.float32).reshape(R, C // B)
+            S = d * torch.tensor(ts, dtype=torch.float32)
+            inv = torch.where(S == 0, torch.zeros_like(S), 1.0 / S)
+        else:
+            e = torch.from_numpy(gs.astype(np.int64)).reshape(R, C // B) - 127
+            inv = torch.pow(2.0, -e.to(torch.float64)).to(torch.float32)
+        v = np.minimum((xf.abs() * inv[..., None]).numpy().astype(np.float64).reshape(-1), 6.0)
+        klo = np.searchsorted(E2M1, v, side="right") - 1
+        khi = np.searchsorted(E2M1, v, side="left")
+        k = (_unpack(gc) & 7).astype(int)
+        bit = np.unpackbits(gb, bitorder="little").astype(int)
+        assert ((k == klo) | (k == khi)).all()
+        assert ((k[klo != khi] & 1) == bit[klo != khi]).all()
+
+
+def test_guided_nan_guide_scale_gives_zero_codes(orc):
+    # E4M3FN NaN is S.1111.111 (0x7F and 0xFF); E8M0 NaN is 0xFF
+    R, C = 1, 128
+    x = _bf16(np.linspace(-5, 5, C, dtype=np.float32)[None, :])
+    gb = np.full(C // 8, 0xFF, dtype=np.uint8)  # guide bit 1 everywhere: never the zero code
+    gs = np.array([0x7F, 0x38, 0xFF, 0x38, 0x40, 0x7F, 0x30, 0xFF], dtype=np.uint8)
+    cfg = orc.Cfg()
+    gc, gsc = orc.quantize(cfg, orc.GUIDED, x, 1.0, guide_bits=gb, guide_scales=gs)
+    nib = _unpack(gc).reshape(8, 16)
+    assert (gsc == gs).all()
+    for b in range(8):
+        nan = gs[b] & 0x7F == 0x7F
+        assert (nib[b] == 0).all() == nan, b
+    cfgm = orc.Cfg(format=orc.MXFP4)
+    gsm = np.array([0xFF, 127, 0xFE, 0xFF], dtype=np.uint8)
+    gc, gsc = orc.quantize(cfgm, orc.GUIDED, x, 1.0, guide_bits=gb, guide_scales=gsm)
+    nib = _unpack(gc).reshape(4, 32)
+    assert (gsc == gsm).all()
+    assert (nib[0] == 0).all() and (nib[3] == 0).all() and (nib[1] != 0).any()
 
 
 def test_sr_random_bytes_follow_the_group_counter(orc):
@@ -284,6 +355,21 @@ def test_dequant_bf16_is_rne_of_fp32(orc):
     assert (b == W.f32_to_bf16_rne(f)).all()
 
 
+def test_dequant_bf16_ties_go_to_even(orc):
+    # with d = 1, ts = 1 + 2^-8 and 1 + 3*2^-8 put the fp32 results of the power-of-two
+    # codewords exactly halfway between two bf16 values; torch's fp32 -> bf16 cast
+    # rounds half to even
+    codes = np.arange(256, dtype=np.uint8)  # every pair of codes
+    cfg = orc.Cfg()
+    for ts in (1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8):  # ties below an even / an odd bf16 value
+        sc = np.full(32, 0x38, dtype=np.uint8)  # d = 1
+        f = orc.dequantize(cfg, codes, sc, ts, 1, 512)
+        b = orc.dequantize(cfg, codes, sc, ts, 1, 512, out_bf16=True)
+        want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert (b == want).all()
+        assert ((f.view(np.uint32) & 0xFFFF) == 0x8000).sum() >= 64  # ties are really there
+
+
 def test_special_blocks(orc):
     cfg = orc.Cfg()
     x = np.zeros((1, 96), dtype=np.float32)
@@ -294,8 +380,15 @@ def test_special_blocks(orc):
     xh = _bf16(x)
     xh[0, 80:96] = _bf16(np.ones(16, dtype=np.float32))
     xh[0, 85] = 0x7FC0                       # block 5: NaN inside
+    xh = np.concatenate([xh, _bf16(np.ones((1, 32), dtype=np.float32))], axis=1)
+    xh[0, 100] = 0x7F80                      # block 6: +Inf inside
+    xh[0, 127] = 0xFF80                      # block 7: -Inf inside
     codes, scales = orc.quantize(cfg, orc.RTN, xh, 1.0)
     nib = _unpack(codes)
+    assert scales[6] == 0x7F and scales[7] == 0x7F and (nib[96:128] == 0).all()
+    deq = orc.dequantize(cfg, codes, scales, 1.0, 1, 128)
+    assert (deq.view(np.uint32)[80:] == 0x7FC00000).all()   # canonical quiet NaN for the whole block
+    assert (orc.dequantize(cfg, codes, scales, 1.0, 1, 128, out_bf16=True)[80:] == 0x7FC0).all()
     assert scales[0] == 0 and (nib[:16] == 0).all()          # all-zero block: zero scale and codes
     assert scales[1] == 0 and (nib[16:32] == 8).all()        # -0 keeps its sign
     assert nib[32] == 7 and (nib[33:48] == 0).all()          # outlier at the max, rest zero
@@ -306,8 +399,10 @@ def test_special_blocks(orc):
     assert list(nib[64:80]) == [0, 1, 2, 3, 4, 5, 6, 7, 15, 14, 13, 12, 11, 10, 9, 8]
     cfgm = orc.Cfg(format=orc.MXFP4)
     cm, sm = orc.quantize(cfgm, orc.RTN, xh, 1.0)
-    assert sm[0] == 0 and sm[2] == 0xFF                      # MX: zero block -> 2^-127, NaN block -> 0xFF
-    assert (_unpack(cm)[64:96] == 0).all()
+    assert sm[0] == 0 and sm[2] == 0xFF and sm[3] == 0xFF    # MX: zero block -> 2^-127, NaN/Inf -> 0xFF
+    assert (_unpack(cm)[64:128] == 0).all()
+    dm = orc.dequantize(cfgm, cm, sm, 1.0, 1, 128)
+    assert (dm.view(np.uint32)[64:] == 0x7FC00000).all()
 
 
 def test_guide_pack_unpack_roundtrip(orc):
