@@ -215,6 +215,79 @@ def test_guided_with_nan_guide_scales(fq):
         assert (host(s) == oc_s).all() and (host(c) == oc_c).all()
 
 
+@pytest.mark.parametrize("ts", [1.0, 0.37, 1e-3, 2.0 ** -120, 7.5e37 / 2688])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_nvfp4_extreme_tensor_scales(fq, ts, rnd):
+    # 1e-38 rows at ts = 2^-120: block scales S below 2^-128, where 1/S saturates to FLT_MAX
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((16, 64)) * rng.choice([1e-38, 1e-30, 1e-3, 1, 1e3], (16, 1))).astype(np.float32)
+    xh = W.f32_to_bf16_rne(x)
+    cfg = fq.Fp4Config(rounding=rnd, sr_seed=21)
+    oc = ocfg(cfg)
+    ts = np.float32(ts)
+    tst = torch.tensor([ts], device="cuda")
+    c, s = fq.fp4_quantize(dev(xh), cfg, tst)
+    oc_c, oc_s = O.quantize(oc, rnd, xh, float(ts))
+    assert (host(s) == oc_s).all() and (host(c) == oc_c).all()
+    fqo = fq.fp4_fake_quantize(dev(xh), cfg, tst)
+    want = O.dequantize(oc, oc_c, oc_s, float(ts), 16, 64, out_bf16=True)
+    assert (host(fqo.view(torch.int16)).reshape(-1) == want.view(np.int16)).all()
+
+
+@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_mxfp4_extreme_magnitudes(fq, grid, rnd):
+    rng = np.random.default_rng(11)
+    mags = np.float32([2.0 ** -133, 2.0 ** -130, 2.0 ** -127, 2.0 ** -125, 1e-30, 1.0, 1e30, 3.0e38])
+    x = (rng.uniform(-1, 1, (8, 64)) * mags[:, None]).astype(np.float32)
+    x[:, 0] = mags
+    xh = W.f32_to_bf16_rne(x)
+    cfg = fq.Fp4Config(format=1, grid=grid, rounding=rnd, sr_seed=4)
+    oc = ocfg(cfg)
+    c, s = fq.fp4_quantize(dev(xh), cfg)
+    oc_c, oc_s = O.quantize(oc, rnd, xh)
+    assert oc_s[0] == 0
+    assert (host(s) == oc_s).all() and (host(c) == oc_c).all()
+    fqo = fq.fp4_fake_quantize(dev(xh), cfg)
+    want = O.dequantize(oc, oc_c, oc_s, 1.0, 8, 64, out_bf16=True)
+    assert (host(fqo.view(torch.int16)).reshape(-1) == want.view(np.int16)).all()
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_guided_with_a_rescaled_rollout(fq, fmt):
+    # the rollout is 1.7x the tensor, so most guide block scales differ from the tensor's own
+    rows, cols = 96, 512
+    x_h = W.c5_x(rows, cols, seed=6)
+    xr_h = W.f32_to_bf16_rne(W.bf16_to_f32(x_h) * np.float32(1.7))
+    cfg = fq.Fp4Config(format=fmt)
+    oc = ocfg(cfg)
+    xr = dev(xr_h)
+    ts_t = fq.fp4_tensor_scale(xr, cfg) if fmt == 0 else None
+    ts = O.tensor_scale(oc, xr_h) if fmt == 0 else 1.0
+    _, rs, rb = fq.fp4_quantize(xr, cfg, ts_t, emit=True)
+    o_rc, o_rs, o_rb = O.quantize(oc, O.RTN, xr_h, ts, emit=True)
+    assert (host(rs) == o_rs).all() and (host(rb) == o_rb).all()
+    gc, gsc = fq.fp4_quantize_guided(dev(x_h), cfg, rb, rs, ts_t)
+    o_gc, o_gsc = O.quantize(oc, O.GUIDED, x_h, ts, guide_bits=o_rb, guide_scales=o_rs)
+    assert (host(gsc) == o_gsc).all() and (host(gc) == o_gc).all()
+    fqo = fq.fp4_fake_quantize(dev(x_h), cfg, ts_t, rb, rs)
+    want = O.dequantize(oc, o_gc, o_gsc, ts, rows, cols, out_bf16=True)
+    assert (host(fqo.view(torch.int16)).reshape(-1) == want.view(np.int16)).all()
+
+
+def test_dequant_bf16_ties(fq):
+    codes = np.arange(256, dtype=np.uint8)
+    cfg = fq.Fp4Config()
+    oc = ocfg(cfg)
+    sc = np.full(32, 0x38, dtype=np.uint8)
+    for ts in (1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8):
+        ts = np.float32(ts)
+        want = O.dequantize(oc, codes, sc, float(ts), 1, 512, out_bf16=True)
+        got = fq.fp4_dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(sc).cuda(), cfg, 1, 512,
+                                torch.tensor([ts], device="cuda"), dtype=torch.bfloat16)
+        assert (host(got.view(torch.int16)).reshape(-1) == want.view(np.int16)).all()
+
+
 # ---------------------------------------------------------------- dequantize, guide, rht
 
 @pytest.mark.parametrize("fmt,grid", [(0, 0), (1, 0), (0, 1), (1, 1)])
