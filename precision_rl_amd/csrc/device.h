@@ -5,10 +5,13 @@
 // the gfx950 scaled-convert instructions:
 //   v_cvt_scalef32_pk_fp4_f32     round to nearest even, saturating at 6
 //   v_cvt_scalef32_sr_pk_fp4_f32  with a zero random word: truncation, i.e.
-//                                 the lower bracketing codeword
-// both called with scale 1.0, so the instruction sees the already scaled
-// value RN(y * inv).  Stochastic rounding and the uniform grid are computed
-// with plain fp32/integer arithmetic.  Per-block work (scale codes and
+//                                 the lower bracketing codeword; with a word
+//                                 built from the random byte: stochastic
+//                                 rounding, exact for values with at most 14
+//                                 significant bits (MXFP4 without the RHT)
+// all called with scale 1.0, so the instruction sees the already scaled
+// value RN(y * inv).  Stochastic rounding of other values and the uniform
+// grid are computed with plain fp32/integer arithmetic.  Per-block work (scale codes and
 // reciprocals) is written in ordinary IEEE fp32 (correctly rounded division,
 // denormals kept).
 #pragma once
@@ -32,12 +35,10 @@ typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
 #define FP4Q_NT_LOADS 1
 #endif
 
-__device__ __forceinline__ void load32_nt(const uint16_t* p, uint32_t w[8]) {
+__device__ __forceinline__ void load16_nt(const uint16_t* p, uint32_t w[4]) {
     const v4u32* s = reinterpret_cast<const v4u32*>(p);
     const v4u32 a = FP4Q_NT_LOADS ? __builtin_nontemporal_load(s) : s[0];
-    const v4u32 b = FP4Q_NT_LOADS ? __builtin_nontemporal_load(s + 1) : s[1];
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
 template <typename T>
@@ -102,14 +103,19 @@ __device__ __forceinline__ float mx_inv(uint32_t code) {
 // multipliers, Weyl-sequence key schedule.
 struct u32x4 { uint32_t w[4]; };
 
+// a ^ b ^ c in one instruction (truth table 0x96 = odd parity of the three bits)
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
                                                uint32_t key0, uint32_t key1) {
     #pragma unroll
     for (int round = 0; round < 10; ++round) {
         const uint64_t a = (uint64_t)x0 * 0xD2511F53u;
         const uint64_t b = (uint64_t)x2 * 0xCD9E8D57u;
-        const uint32_t y0 = (uint32_t)(b >> 32) ^ x1 ^ key0;
-        const uint32_t y2 = (uint32_t)(a >> 32) ^ x3 ^ key1;
+        const uint32_t y0 = xor3((uint32_t)(b >> 32), x1, key0);
+        const uint32_t y2 = xor3((uint32_t)(a >> 32), x3, key1);
         x1 = (uint32_t)b;
         x3 = (uint32_t)a;
         x0 = y0;
@@ -214,6 +220,42 @@ __device__ __forceinline__ uint32_t encode1_sr_e2m1(float v, uint32_t u) {
     return (uint32_t)k | sign_nibble(v);
 }
 
+// SR E2M1 through the hardware convert, one element per instruction (slot 0;
+// slot 1 converts +0).  The convert rounds up iff D + R >= 2^32, with D the
+// discarded fraction of the bracket as a 32-bit fixed-point number; the word
+// R = (~u << 24) | 0x7FFFFF makes that "D > (2u+1) * 2^23", i.e. 2u+1 < 512 f.
+// It is exact except below 1.0, where it keeps 23 fraction bits: a value with
+// at most 14 significant bits never lies strictly within 2^-23 above a
+// threshold (thresholds are multiples of 2^-10 and v >= 2^-10 there), so it is
+// exact for such values.  Checked on the GPU against encode1_sr_e2m1 over every
+// fp32 value in [-8, 8] and every u: the only differences are values with 15
+// or more significant bits.  MXFP4 without the RHT scales bf16 inputs by a
+// power of two, so its v has at most 8 significant bits.
+// nw = ~(four random bytes); byte j of nw becomes the top byte of R.
+__device__ __forceinline__ uint32_t sr_word(uint32_t nw, int j) {
+    return __builtin_amdgcn_perm(nw, 0x007FFFFFu, ((4u + (uint32_t)j) << 24) | 0x020100u);
+}
+
+// Slot 1 of the convert uses its random word shifted left by one, so a pair
+// (v[2i], v[2i+1]) is converted twice from one register pair: with R for
+// element 2i (low nibble kept) and with R' >> 1 for element 2i+1 (high nibble
+// kept; bit 0 of R' is below the convert's resolution).  Same exhaustive check
+// as slot 0.  The four pair bytes are then gathered with two byte permutes.
+__device__ __forceinline__ uint32_t encode8_sr_e2m1_short(const float v[8], uint32_t rnd0, uint32_t rnd1) {
+    const uint32_t n0 = ~rnd0, n1 = ~rnd1;
+    uint32_t b[4];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t nw = i < 2 ? n0 : n1;
+        v2f x = {v[2 * i], v[2 * i + 1]};
+        const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, sr_word(nw, (2 * i) & 3), 1.0f, 0);
+        const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, sr_word(nw, (2 * i + 1) & 3) >> 1,
+                                                                        1.0f, 0);
+        b[i] = (lo & 0x0Fu) | (hi & 0xF0u);   // byte 0 valid
+    }
+    return __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+}
+
 __device__ __forceinline__ uint32_t encode1_rtn_uniform(float v) {
     const float vc = fminf(fabsf(v), 7.0f);
     const uint32_t k = __float_as_uint(vc + 8388608.0f) - 0x4B000000u;   // RNE to integer
@@ -237,14 +279,17 @@ __device__ __forceinline__ uint32_t encode1_guided_uniform(float v, uint32_t b) 
 }
 
 // rnd: 8 random bytes for SR (rnd0 bytes 0..3 -> elements 0..3, rnd1 -> 4..7);
-// gbits: 8 guide bits for guided.
-template <int GRID, int MODE>
+// gbits: 8 guide bits for guided.  SHORT: every |v| has at most 14
+// significant bits (lets SR use the hardware convert).
+template <int GRID, int MODE, bool SHORT = false>
 __device__ __forceinline__ uint32_t encode8(const float v[8], uint32_t rnd0, uint32_t rnd1,
                                             uint32_t gbits) {
     if constexpr (GRID == 0 && MODE == MODE_RTN) {
         return pack_rne8(v);
     } else if constexpr (GRID == 0 && MODE == MODE_GUIDED) {
         return encode8_guided_e2m1(v, gbits);
+    } else if constexpr (GRID == 0 && MODE == MODE_SR && SHORT) {
+        return encode8_sr_e2m1_short(v, rnd0, rnd1);
     } else {
         uint32_t w = 0;
         #pragma unroll
@@ -304,6 +349,32 @@ __device__ __forceinline__ bool dequant16(uint32_t c0, uint32_t c1, uint32_t sc,
     }
 }
 
+// Same for one half-group (8 codes in one dword).
+template <int FMT, int GRID>
+__device__ __forceinline__ bool dequant8(uint32_t c, uint32_t sc, float ts, float v[8]) {
+    decode8<GRID>(c, v);
+    if constexpr (FMT == 0) {
+        const float d = e4m3_decode(sc);
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (v[j] * d) * ts;
+        return (sc & 0x7Fu) != 0x7Fu;
+    } else {
+        const float s2 = __uint_as_float(sc ? sc << 23 : 0x00400000u);  // 2^(sc-127)
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = v[j] * s2;
+        return sc != 0xFFu;
+    }
+}
+
+// 8 fp32 -> 8 bf16 (RNE) as 4 dwords; canonical quiet NaN when !ok.
+__device__ __forceinline__ void to_bf16x8(const float v[8], bool ok, uint32_t o[4]) {
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        bf16x2 h = __builtin_convertvector((v2f){v[2 * j], v[2 * j + 1]}, bf16x2);
+        o[j] = ok ? __builtin_bit_cast(uint32_t, h) : 0x7FC07FC0u;
+    }
+}
+
 // 16 fp32 -> 16 bf16 (RNE) as 8 dwords; canonical quiet NaN when !ok.
 __device__ __forceinline__ void to_bf16x16(const float v[16], bool ok, uint32_t o[8]) {
     #pragma unroll
@@ -352,9 +423,21 @@ __device__ __forceinline__ void widen16(const uint32_t w[8], uint32_t signs, flo
     }
 }
 
+// ---------------------------------------------------------------- lane exchange
+// quad_perm DPP moves within each row of four lanes: [1,0,3,2] swaps pair
+// partners, [2,3,0,1] swaps the two pairs.  Callers make every lane execute
+// them (a lane reading an inactive partner gets 0).
+__device__ __forceinline__ uint32_t dpp_swap1(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t dpp_swap2(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 // Largest |bf16| bit pattern of 16 values (8 dwords) with sign bits cleared;
 // >= 0x7F80 means the group holds a non-finite value.  Packed 16-bit max.
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t amax_bits16(const uint32_t w[8]) {
     u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
