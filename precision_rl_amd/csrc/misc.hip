@@ -1,6 +1,5 @@
 // misc.hip -- tensor scale, dequantization, guide pack/unpack, standalone RHT16
-// and the element-encode entry, for gfx950.  Same work unit as quantize.hip:
-// one lane per 16-element group.
+// and the element-encode entry, for gfx950.
 #include "device.h"
 #include "internal.h"
 
@@ -85,65 +84,112 @@ __global__ void k_ts_finalize(float* acc, float gmax448) {
 }
 
 // ---------------------------------------------------------------- dequantize
+// Work unit: 16 bytes of output, i.e. 8 elements to bf16 (one dword of codes)
+// or 4 elements to fp32 (16 bits of codes).  In each of its kDqSlots slots the
+// 64 lanes of a wave handle 64 consecutive units, so every store instruction
+// of a wave writes 1 KiB contiguously (when ld_out == cols).
+
+#ifndef FP4Q_DQ_SLOTS
+#define FP4Q_DQ_SLOTS 2
+#endif
+constexpr int kDqSlots = FP4Q_DQ_SLOTS;
 
 template <int FMT, int GRID, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) {
-    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
-    if (g >= p.ngroups) return;
-    const v2u32 c = __builtin_nontemporal_load(reinterpret_cast<const v2u32*>(p.codes) + g);
-    const uint32_t sc = p.scales[FMT == 0 ? g : (g >> 1)];
-    float v[16];
-    const bool ok = dequant16<FMT, GRID>(c.x, c.y, sc, FMT == 0 ? *p.ts : 1.0f, v);
-    const bool nan = !ok;
-    const int64_t off = row_offset(g, p.gpr, p.ld_out);
-    if constexpr (BF16) {
-        uint32_t o[8];
-        to_bf16x16(v, ok, o);
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + off;
-        st_out4(dst, 0, o[0], o[1], o[2], o[3]);
-        st_out4(dst, 1, o[4], o[5], o[6], o[7]);
-    } else {
-        uint32_t o[16];
-        #pragma unroll
-        for (int j = 0; j < 16; ++j) o[j] = nan ? 0x7FC00000u : __float_as_uint(v[j]);
-        float* dst = reinterpret_cast<float*>(p.out) + off;
-        #pragma unroll
-        for (int q = 0; q < 4; ++q) st_out4(dst, q, o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    constexpr uint32_t E = BF16 ? 8u : 4u;                 // elements per unit
+    const uint64_t nunits = (uint64_t)p.ngroups * (16u / E);
+    const uint64_t u0 = (uint64_t)blockIdx.x * (kThreads * kDqSlots) + (threadIdx.x >> 6) * (64u * kDqSlots) +
+                        (threadIdx.x & 63u);
+    const float ts = FMT == 0 ? *p.ts : 1.0f;
+    uint32_t c[kDqSlots], sc[kDqSlots];
+    #pragma unroll
+    for (int s = 0; s < kDqSlots; ++s) {
+        const uint64_t u = u0 + 64u * s;
+        c[s] = sc[s] = 0u;
+        if (u < nunits) {
+            if constexpr (BF16) c[s] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.codes) + u);
+            else c[s] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p.codes) + u);
+            sc[s] = p.scales[(u * E) / (FMT == 0 ? 16u : 32u)];   // u*E < 2^35: 64-bit
+        }
+    }
+    #pragma unroll
+    for (int s = 0; s < kDqSlots; ++s) {
+        const uint64_t u = u0 + 64u * s;
+        if (u >= nunits) continue;
+        float v[8];
+        const bool ok = dequant8<FMT, GRID>(c[s], sc[s], ts, v);
+        const uint32_t g = (uint32_t)(u / (16u / E));        // group of the unit
+        const uint32_t row = fastdiv(g, p.gpr);
+        const int64_t off = (int64_t)row * p.ld_out + (int64_t)(g - row * p.gpr.d) * 16 +
+                            (int64_t)((u * E) & 15u);
+        if constexpr (BF16) {
+            uint32_t o[4];
+            to_bf16x8(v, ok, o);
+            st_out4(reinterpret_cast<uint16_t*>(p.out) + off, 0, o[0], o[1], o[2], o[3]);
+        } else {
+            uint32_t o[4];
+            #pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = ok ? __float_as_uint(v[j]) : 0x7FC00000u;
+            st_out4(reinterpret_cast<float*>(p.out) + off, 0, o[0], o[1], o[2], o[3]);
+        }
     }
 }
 
 // ---------------------------------------------------------------- guide pack / unpack
+// pack: a unit is 32 elements (16 bytes of codes -> 4 bytes of bits, plus the
+// unit's scale bytes); unpack: a unit is 16 elements (2 bytes of bits -> 16
+// bytes of 0/1).  Slots as in dequantize: loads or stores of a wave are
+// contiguous per instruction.
 
-// Four consecutive groups per lane: 32 bytes of codes in, 8 bytes of bits out.
-constexpr uint32_t kGuideG = 4;
-
-template <int FMT>
-__device__ __forceinline__ void copy_scales(const GuideParams& p, uint32_t g) {
-    if (FMT == 0) st_out(p.scales_out + g, p.scales_in[g]);
-    else if ((g & 1u) == 0) st_out(p.scales_out + (g >> 1), p.scales_in[g >> 1]);
-}
+#ifndef FP4Q_GUIDE_SLOTS
+#define FP4Q_GUIDE_SLOTS 2
+#endif
+constexpr int kGuideSlots = FP4Q_GUIDE_SLOTS;
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_guide_pack(const GuideParams p) {
-    const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
-    const uint32_t g0 = t * kGuideG;
-    if (g0 >= p.ngroups) return;
-    if (g0 + kGuideG <= p.ngroups) {
-        const v4u32* src = reinterpret_cast<const v4u32*>(p.in) + 2 * (int64_t)t;
-        const v4u32 a = __builtin_nontemporal_load(src), b = __builtin_nontemporal_load(src + 1);
-        const uint32_t lo = gather_nibble_lsbs(a.x) | (gather_nibble_lsbs(a.y) << 8) |
-                            (gather_nibble_lsbs(a.z) << 16) | (gather_nibble_lsbs(a.w) << 24);
-        const uint32_t hi = gather_nibble_lsbs(b.x) | (gather_nibble_lsbs(b.y) << 8) |
-                            (gather_nibble_lsbs(b.z) << 16) | (gather_nibble_lsbs(b.w) << 24);
-        st_out2(p.out, t, lo, hi);
-        #pragma unroll
-        for (uint32_t k = 0; k < kGuideG; ++k) copy_scales<FMT>(p, g0 + k);
-    } else {
-        for (uint32_t g = g0; g < p.ngroups; ++g) {
-            const uint2 c = reinterpret_cast<const uint2*>(p.in)[g];
-            reinterpret_cast<uint16_t*>(p.out)[g] =
-                (uint16_t)(gather_nibble_lsbs(c.x) | (gather_nibble_lsbs(c.y) << 8));
-            copy_scales<FMT>(p, g);
+    // an odd NVFP4 group count leaves a last unit of one group (8 bytes of codes)
+    const uint32_t nunits = (p.ngroups + 1u) >> 1;
+    const uint32_t half_unit = (p.ngroups & 1u) ? nunits - 1u : 0xFFFFFFFFu;
+    const uint32_t u0 = blockIdx.x * (kThreads * kGuideSlots) + (threadIdx.x >> 6) * (64u * kGuideSlots) +
+                        (threadIdx.x & 63u);
+    v4u32 c[kGuideSlots];
+    uint32_t sc[kGuideSlots];
+    #pragma unroll
+    for (int s = 0; s < kGuideSlots; ++s) {
+        const uint32_t u = u0 + 64u * s;
+        c[s] = (v4u32){0u, 0u, 0u, 0u};
+        sc[s] = 0u;
+        if (u < nunits) {
+            if (u != half_unit) {
+                c[s] = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p.in) + u);
+                if constexpr (FMT == 0) sc[s] = p.scales_in[2 * u] | ((uint32_t)p.scales_in[2 * u + 1] << 8);
+                else sc[s] = p.scales_in[u];
+            } else {
+                const v2u32 h = reinterpret_cast<const v2u32*>(p.in)[2 * u];
+                c[s].x = h.x;
+                c[s].y = h.y;
+                sc[s] = p.scales_in[2 * u];
+            }
+        }
+    }
+    #pragma unroll
+    for (int s = 0; s < kGuideSlots; ++s) {
+        const uint32_t u = u0 + 64u * s;
+        if (u >= nunits) continue;
+        const uint32_t bits = gather_nibble_lsbs(c[s].x) | (gather_nibble_lsbs(c[s].y) << 8) |
+                              (gather_nibble_lsbs(c[s].z) << 16) | (gather_nibble_lsbs(c[s].w) << 24);
+        if (u != half_unit) {
+            st_out(reinterpret_cast<uint32_t*>(p.out) + u, bits);
+            if constexpr (FMT == 0) {
+                st_out(p.scales_out + 2 * u, (uint8_t)sc[s]);
+                st_out(p.scales_out + 2 * u + 1, (uint8_t)(sc[s] >> 8));
+            } else {
+                st_out(p.scales_out + u, (uint8_t)sc[s]);
+            }
+        } else {
+            st_out(reinterpret_cast<uint16_t*>(p.out) + 2 * u, (uint16_t)bits);
+            st_out(p.scales_out + 2 * u, (uint8_t)sc[s]);
         }
     }
 }
@@ -154,15 +200,26 @@ __device__ __forceinline__ uint32_t bits4_to_bytes(uint32_t b) {
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_guide_unpack(const GuideParams p) {
-    const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
-    const uint32_t g0 = t * kGuideG;
-    if (g0 >= p.ngroups) return;
-    const uint32_t gend = g0 + kGuideG <= p.ngroups ? g0 + kGuideG : p.ngroups;
-    for (uint32_t g = g0; g < gend; ++g) {
-        const uint32_t b = reinterpret_cast<const uint16_t*>(p.in)[g];
-        st_out4(p.out, g, bits4_to_bytes(b), bits4_to_bytes(b >> 4), bits4_to_bytes(b >> 8),
-                bits4_to_bytes(b >> 12));
-        copy_scales<FMT>(p, g);
+    const uint32_t u0 = blockIdx.x * (kThreads * kGuideSlots) + (threadIdx.x >> 6) * (64u * kGuideSlots) +
+                        (threadIdx.x & 63u);
+    uint32_t b[kGuideSlots], sc[kGuideSlots];
+    #pragma unroll
+    for (int s = 0; s < kGuideSlots; ++s) {
+        const uint32_t g = u0 + 64u * s;
+        b[s] = sc[s] = 0u;
+        if (g < p.ngroups) {
+            b[s] = reinterpret_cast<const uint16_t*>(p.in)[g];
+            if (FMT == 0 || (g & 1u) == 0) sc[s] = p.scales_in[FMT == 0 ? g : (g >> 1)];
+        }
+    }
+    #pragma unroll
+    for (int s = 0; s < kGuideSlots; ++s) {
+        const uint32_t g = u0 + 64u * s;
+        if (g >= p.ngroups) continue;
+        st_out4(p.out, g, bits4_to_bytes(b[s]), bits4_to_bytes(b[s] >> 4), bits4_to_bytes(b[s] >> 8),
+                bits4_to_bytes(b[s] >> 12));
+        if (FMT == 0) st_out(p.scales_out + g, (uint8_t)sc[s]);
+        else if ((g & 1u) == 0) st_out(p.scales_out + (g >> 1), (uint8_t)sc[s]);
     }
 }
 
@@ -258,7 +315,8 @@ hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams
 }
 
 hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantParams& p, hipStream_t s) {
-    const dim3 b(blocks_for(p.ngroups)), t(kThreads);
+    const uint64_t units = (uint64_t)p.ngroups * (bf16_out ? 2u : 4u);
+    const dim3 b((uint32_t)((units + kThreads * kDqSlots - 1) / (kThreads * kDqSlots))), t(kThreads);
 #define FP4Q_DQ(F, G, B) hipLaunchKernelGGL((k_dequantize<F, G, B>), b, t, 0, s, p)
     if (format == 0) {
         if (grid == 0) { if (bf16_out) FP4Q_DQ(0, 0, true); else FP4Q_DQ(0, 0, false); }
@@ -272,14 +330,15 @@ hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantP
 }
 
 hipError_t launch_guide_pack(int format, const GuideParams& p, hipStream_t s) {
-    const dim3 b(blocks_for((p.ngroups + kGuideG - 1) / kGuideG)), t(kThreads);
+    const uint32_t units = (p.ngroups + 1u) >> 1;
+    const dim3 b((units + kThreads * kGuideSlots - 1) / (kThreads * kGuideSlots)), t(kThreads);
     if (format == 0) hipLaunchKernelGGL(k_guide_pack<0>, b, t, 0, s, p);
     else hipLaunchKernelGGL(k_guide_pack<1>, b, t, 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_guide_unpack(int format, const GuideParams& p, hipStream_t s) {
-    const dim3 b(blocks_for((p.ngroups + kGuideG - 1) / kGuideG)), t(kThreads);
+    const dim3 b((p.ngroups + kThreads * kGuideSlots - 1) / (kThreads * kGuideSlots)), t(kThreads);
     if (format == 0) hipLaunchKernelGGL(k_guide_unpack<0>, b, t, 0, s, p);
     else hipLaunchKernelGGL(k_guide_unpack<1>, b, t, 0, s, p);
     return hipGetLastError();

@@ -31,7 +31,7 @@ namespace fp4q {
 namespace {
 
 #ifndef FP4Q_HALVES_PER_LANE
-#define FP4Q_HALVES_PER_LANE 2
+#define FP4Q_HALVES_PER_LANE 4
 #endif
 // Half-groups per lane (load slots); even, since slots are transposed in pairs.
 constexpr int kH = FP4Q_HALVES_PER_LANE;

@@ -234,6 +234,37 @@ def test_nvfp4_extreme_tensor_scales(fq, ts, rnd):
     assert (host(fqo.view(torch.int16)).reshape(-1) == want.view(np.int16)).all()
 
 
+def test_mxfp4_sr_every_8bit_scaled_value(fq):
+    # MXFP4 SR of E2M1 without the RHT runs through the hardware stochastic
+    # convert, exact for scaled values with at most 14 significant bits.  Every
+    # block gets an anchor 6*2^s (so e = s and v = |y|/2^s) and 31 values from
+    # the list of all 8-bit significands times 2^E, E = -11..2, both signs.  Over
+    # 4096 rows each value meets each random byte with probability 1 - 1e-7.
+    sig = 1.0 + np.arange(128) / 128.0
+    vals = np.concatenate([sig * 2.0 ** E for E in range(-11, 3)] + [[0.0, 0.5, 1.5, 3.0, 6.0]])
+    vals = np.concatenate([vals, -vals]).astype(np.float64)
+    per_row = 31 * ((vals.size + 30) // 31)
+    nblk = per_row // 31
+    rows, cols = 4096, 32 * nblk
+    rng = np.random.default_rng(17)
+    x = np.empty((rows, cols), dtype=np.float32)
+    for r in range(rows):
+        s = (r % 9) - 4
+        payload = np.resize(np.roll(vals, r * 7), per_row).reshape(nblk, 31)
+        blk = np.empty((nblk, 32))
+        blk[:, 0] = 6.0 * (1 if r % 2 else -1)
+        blk[:, 1:] = payload
+        x[r] = (blk * 2.0 ** s).reshape(-1)
+    xh = W.f32_to_bf16_rne(x)
+    assert (W.bf16_to_f32(xh) == x).all()       # exact: 8 significant bits
+    cfg = fq.Fp4Config(format=1, rounding=1, sr_seed=0x5EED, sr_offset=11)
+    oc = ocfg(cfg)
+    c, sc = fq.fp4_quantize(dev(xh), cfg)
+    oc_c, oc_s = O.quantize(oc, O.SR, xh)
+    assert (host(sc) == oc_s).all()
+    assert (host(c) == oc_c).all()
+
+
 @pytest.mark.parametrize("grid", [0, 1])
 @pytest.mark.parametrize("rnd", [0, 1])
 def test_mxfp4_extreme_magnitudes(fq, grid, rnd):
@@ -291,7 +322,7 @@ def test_dequant_bf16_ties(fq):
 # ---------------------------------------------------------------- dequantize, guide, rht
 
 @pytest.mark.parametrize("fmt,grid", [(0, 0), (1, 0), (0, 1), (1, 1)])
-@pytest.mark.parametrize("shape", [(256, 512), (37, 544), (3, 32)])
+@pytest.mark.parametrize("shape", [(256, 512), (37, 544), (3, 32), (5, 48), (1, 16), (300, 2080)])
 def test_dequantize_vs_oracle(fq, fmt, grid, shape):
     rows, cols = shape
     B = 32 if fmt else 16
@@ -320,9 +351,12 @@ def test_dequantize_vs_oracle(fq, fmt, grid, shape):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-def test_guide_pack_unpack_vs_oracle(fq, fmt):
-    rows, cols = 77, 544
+@pytest.mark.parametrize("shape", [(77, 544), (5, 48), (1, 16), (3, 16), (300, 2080)])
+def test_guide_pack_unpack_vs_oracle(fq, fmt, shape):
+    rows, cols = shape
     B = 32 if fmt else 16
+    if cols % B:
+        pytest.skip("shape not valid for this block size")
     rng = np.random.default_rng(5)
     codes = rng.integers(0, 256, rows * cols // 2, dtype=np.uint8)
     scales = rng.integers(0, 256, rows * cols // B, dtype=np.uint8)
