@@ -98,6 +98,11 @@ __device__ __forceinline__ float mx_inv(uint32_t code) {
     return __uint_as_float(code < 254u ? (254u - code) << 23 : 0x00400000u);
 }
 
+// MXFP4: 2^e from the E8M0 code (code 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float mx_scale(uint32_t code) {
+    return __uint_as_float(code ? code << 23 : 0x00400000u);
+}
+
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon et al., SC'11: ten rounds of two 32x32->64 products with the published
 // multipliers, Weyl-sequence key schedule.
@@ -150,9 +155,12 @@ __device__ __forceinline__ uint32_t gather_nibble_lsbs(uint32_t w) {
 
 // ---------------------------------------------------------------- E2M1 converts
 
+// The converts divide their inputs by the scale operand; with a power of two
+// the result equals converting the exactly scaled value (checked on the GPU for
+// every finite bf16 input, scales 2^-127..2^127, RNE and every SR word used here).
 template <int SEL>
-__device__ __forceinline__ uint32_t cvt_rne2(uint32_t old, float a, float b) {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+__device__ __forceinline__ uint32_t cvt_rne2(uint32_t old, float a, float b, float scale = 1.0f) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
 }
 
 // Truncating convert of two values; only byte 0 of the result is defined (the
@@ -162,13 +170,27 @@ __device__ __forceinline__ uint32_t cvt_trunc2_b0(float a, float b) {
     return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, 0u, 1.0f, 0) & 0xFFu;
 }
 
-__device__ __forceinline__ uint32_t pack_rne8(const float v[8]) {
+__device__ __forceinline__ uint32_t pack_rne8(const float v[8], float scale = 1.0f) {
     uint32_t w = 0;
-    w = cvt_rne2<0>(w, v[0], v[1]);
-    w = cvt_rne2<1>(w, v[2], v[3]);
-    w = cvt_rne2<2>(w, v[4], v[5]);
-    w = cvt_rne2<3>(w, v[6], v[7]);
+    w = cvt_rne2<0>(w, v[0], v[1], scale);
+    w = cvt_rne2<1>(w, v[2], v[3], scale);
+    w = cvt_rne2<2>(w, v[4], v[5], scale);
+    w = cvt_rne2<3>(w, v[6], v[7], scale);
     return w;
+}
+
+// RNE of 8 bf16 values (4 dwords, element 2j in the low half of w[j]) divided
+// by a power-of-two scale, straight from the bf16 bits: the bf16-input convert
+// equals the fp32-input one on every finite bf16 value (checked on the GPU for
+// scales 2^-127..2^127) and also merges into the old destination bytes.
+__device__ __forceinline__ uint32_t pack_rne8_bf16(const uint32_t w[4], float scale) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, w[0]), scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, w[1]), scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, w[2]), scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, w[3]), scale, 3);
+    return r;
 }
 
 __device__ __forceinline__ uint32_t pack_trunc8(const float v[8]) {
@@ -241,17 +263,18 @@ __device__ __forceinline__ uint32_t sr_word(uint32_t nw, int j) {
 // element 2i (low nibble kept) and with R' >> 1 for element 2i+1 (high nibble
 // kept; bit 0 of R' is below the convert's resolution).  Same exhaustive check
 // as slot 0.  The four pair bytes are then gathered with two byte permutes.
-__device__ __forceinline__ uint32_t encode8_sr_e2m1_short(const float v[8], uint32_t rnd0, uint32_t rnd1) {
+__device__ __forceinline__ uint32_t encode8_sr_e2m1_short(const float v[8], uint32_t rnd0, uint32_t rnd1,
+                                                          float scale = 1.0f) {
     const uint32_t n0 = ~rnd0, n1 = ~rnd1;
     uint32_t b[4];
     #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t nw = i < 2 ? n0 : n1;
         v2f x = {v[2 * i], v[2 * i + 1]};
-        const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, sr_word(nw, (2 * i) & 3), 1.0f, 0);
+        const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, sr_word(nw, (2 * i) & 3), scale, 0);
         const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, sr_word(nw, (2 * i + 1) & 3) >> 1,
-                                                                        1.0f, 0);
-        b[i] = (lo & 0x0Fu) | (hi & 0xF0u);   // byte 0 valid
+                                                                        scale, 0);
+        b[i] = (lo & 0x0Fu) | (hi & ~0x0Fu);  // one bitfield insert; byte 0 is what counts
     }
     return __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
 }
@@ -280,16 +303,18 @@ __device__ __forceinline__ uint32_t encode1_guided_uniform(float v, uint32_t b) 
 
 // rnd: 8 random bytes for SR (rnd0 bytes 0..3 -> elements 0..3, rnd1 -> 4..7);
 // gbits: 8 guide bits for guided.  SHORT: every |v| has at most 14
-// significant bits (lets SR use the hardware convert).
+// significant bits (lets SR use the hardware convert).  scale: a power of two
+// the E2M1 RTN and short SR paths divide v by inside the convert; every other
+// path takes already scaled values (scale 1).
 template <int GRID, int MODE, bool SHORT = false>
 __device__ __forceinline__ uint32_t encode8(const float v[8], uint32_t rnd0, uint32_t rnd1,
-                                            uint32_t gbits) {
+                                            uint32_t gbits, float scale = 1.0f) {
     if constexpr (GRID == 0 && MODE == MODE_RTN) {
-        return pack_rne8(v);
+        return pack_rne8(v, scale);
     } else if constexpr (GRID == 0 && MODE == MODE_GUIDED) {
         return encode8_guided_e2m1(v, gbits);
     } else if constexpr (GRID == 0 && MODE == MODE_SR && SHORT) {
-        return encode8_sr_e2m1_short(v, rnd0, rnd1);
+        return encode8_sr_e2m1_short(v, rnd0, rnd1, scale);
     } else {
         uint32_t w = 0;
         #pragma unroll
@@ -342,7 +367,7 @@ __device__ __forceinline__ bool dequant16(uint32_t c0, uint32_t c1, uint32_t sc,
         for (int j = 0; j < 16; ++j) v[j] = (v[j] * d) * ts;
         return (sc & 0x7Fu) != 0x7Fu;
     } else {
-        const float s2 = __uint_as_float(sc ? sc << 23 : 0x00400000u);  // 2^(sc-127)
+        const float s2 = mx_scale(sc);
         #pragma unroll
         for (int j = 0; j < 16; ++j) v[j] = v[j] * s2;
         return sc != 0xFFu;
@@ -359,7 +384,7 @@ __device__ __forceinline__ bool dequant8(uint32_t c, uint32_t sc, float ts, floa
         for (int j = 0; j < 8; ++j) v[j] = (v[j] * d) * ts;
         return (sc & 0x7Fu) != 0x7Fu;
     } else {
-        const float s2 = __uint_as_float(sc ? sc << 23 : 0x00400000u);  // 2^(sc-127)
+        const float s2 = mx_scale(sc);
         #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = v[j] * s2;
         return sc != 0xFFu;

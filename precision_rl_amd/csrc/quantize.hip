@@ -14,7 +14,7 @@
 // [2,3,0,1]).  Stores: codes are 8 bytes per lane and the guide bits 2 bytes,
 // both covering contiguous runs per wave; the bf16 output of fake quantization
 // is transposed back and stored per half-group like the loads.  Every lane
-// runs every DPP step (only loads and stores are predicated).
+// runs every DPP step (only stores are predicated).
 //
 // Per block (scale) [FQT-FP4 §3; TETRAJET §3; TRACE-JA "TRACEの仕組み"]:
 //   NVFP4 scale code = E4M3 RNE of amax / RN(Gmax*s_t) (clamped to 448),
@@ -80,23 +80,22 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     const uint32_t nhg = 2u * p.ngroups;
     auto gk = [&](int k) { return (hg0 + 128u * k + 64u * q) >> 1; };
 
+    // Lanes past the end load the last half-group instead (in bounds, no
+    // branch); their results are never stored.
     uint32_t w[kH][4];
     #pragma unroll
     for (int s = 0; s < kH; ++s) {
-        const uint32_t hg = hg0 + 64u * s;
-        w[s][0] = w[s][1] = w[s][2] = w[s][3] = 0u;
-        if (hg < nhg) load16_nt(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld), w[s]);
+        const uint32_t hg = min(hg0 + 64u * s, nhg - 1u);
+        load16_nt(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld), w[s]);
     }
     uint32_t gb[kG], gs[kG];
     #pragma unroll
     for (int k = 0; k < kG; ++k) {
         gb[k] = gs[k] = 0u;
         if constexpr (MODE == MODE_GUIDED) {
-            const uint32_t g = gk(k);
-            if (g < p.ngroups) {
-                gb[k] = reinterpret_cast<const uint16_t*>(p.gbits)[g];
-                gs[k] = p.gscales[FMT == 0 ? g : (g >> 1)];
-            }
+            const uint32_t g = min(gk(k), p.ngroups - 1u);
+            gb[k] = reinterpret_cast<const uint16_t*>(p.gbits)[g];
+            gs[k] = p.gscales[FMT == 0 ? g : (g >> 1)];
         }
     }
 
@@ -160,13 +159,28 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             r0 = r.w[0]; r1 = r.w[1]; r2 = r.w[2]; r3 = r.w[3];
         }
 
-        // MXFP4 without the RHT: v = bf16 * 2^-e exactly, at most 8 significant bits
+        // MXFP4 without the RHT: v = bf16 * 2^-e exactly, at most 8 significant
+        // bits.  Its E2M1 RTN and SR converts take y and divide by 2^e themselves.
         constexpr bool kShort = FMT == 1 && !RHT;
+        constexpr bool kInCvt = kShort && GRID == 0 && MODE != MODE_GUIDED;
         float v[16];
-        #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = y[j] * inv;
-        uint32_t c0 = encode8<GRID, MODE, kShort>(v, r0, r1, gb[k] & 0xFFu);
-        uint32_t c1 = encode8<GRID, MODE, kShort>(v + 8, r2, r3, gb[k] >> 8);
+        float cscale = 1.0f;
+        if constexpr (kInCvt) {
+            cscale = mx_scale(sc);
+            #pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = y[j];
+        } else {
+            #pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = y[j] * inv;
+        }
+        uint32_t c0, c1;
+        if constexpr (kInCvt && MODE == MODE_RTN) {   // straight from the bf16 bits
+            c0 = pack_rne8_bf16(gw, cscale);
+            c1 = pack_rne8_bf16(gw + 4, cscale);
+        } else {
+            c0 = encode8<GRID, MODE, kShort>(v, r0, r1, gb[k] & 0xFFu, cscale);
+            c1 = encode8<GRID, MODE, kShort>(v + 8, r2, r3, gb[k] >> 8, cscale);
+        }
         if (!finite) { c0 = 0; c1 = 0; }
 
         if constexpr (OUT == 1) {
