@@ -23,6 +23,7 @@ namespace fp4q {
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Streaming memory access.  Inputs are read once: non-temporal loads keep them
 // from displacing reusable lines.  Outputs use non-temporal stores when
@@ -163,13 +164,6 @@ __device__ __forceinline__ uint32_t cvt_rne2(uint32_t old, float a, float b, flo
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
 }
 
-// Truncating convert of two values; only byte 0 of the result is defined (the
-// builtin does not merge into an old destination value, unlike the RNE form).
-__device__ __forceinline__ uint32_t cvt_trunc2_b0(float a, float b) {
-    v2f x = {a, b};
-    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, 0u, 1.0f, 0) & 0xFFu;
-}
-
 __device__ __forceinline__ uint32_t pack_rne8(const float v[8], float scale = 1.0f) {
     uint32_t w = 0;
     w = cvt_rne2<0>(w, v[0], v[1], scale);
@@ -193,9 +187,31 @@ __device__ __forceinline__ uint32_t pack_rne8_bf16(const uint32_t w[4], float sc
     return r;
 }
 
+// Byte 0 of four convert results -> one dword (two byte permutes and an or).
+__device__ __forceinline__ uint32_t gather_b0(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3) {
+    return __builtin_amdgcn_perm(r1, r0, 0x0C0C0400u) | __builtin_amdgcn_perm(r3, r2, 0x04000C0Cu);
+}
+
 __device__ __forceinline__ uint32_t pack_trunc8(const float v[8]) {
-    return cvt_trunc2_b0(v[0], v[1]) | (cvt_trunc2_b0(v[2], v[3]) << 8) |
-           (cvt_trunc2_b0(v[4], v[5]) << 16) | (cvt_trunc2_b0(v[6], v[7]) << 24);
+    uint32_t r[4];
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v2f x = {v[2 * j], v[2 * j + 1]};
+        r[j] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, 0u, 1.0f, 0);
+    }
+    return gather_b0(r[0], r[1], r[2], r[3]);
+}
+
+// Truncation of 8 bf16 values (4 dwords) divided by a power-of-two scale,
+// straight from the bf16 bits: equal to the fp32-input truncation on every
+// bf16 bit pattern (checked on the GPU, both slots, scales 2^-127..2^127).
+__device__ __forceinline__ uint32_t pack_trunc8_bf16(const uint32_t w[4], float scale) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    uint32_t r[4];
+    #pragma unroll
+    for (int j = 0; j < 4; ++j)
+        r[j] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2_t, w[j]), 0u, scale, 0);
+    return gather_b0(r[0], r[1], r[2], r[3]);
 }
 
 __device__ __forceinline__ uint32_t sign_nibble(float v) { return (__float_as_uint(v) >> 28) & 8u; }
@@ -205,27 +221,43 @@ __device__ __forceinline__ uint32_t sign_nibble(float v) { return (__float_as_ui
 
 enum { MODE_RTN = 0, MODE_SR = 1, MODE_GUIDED = 2 };
 
-// Guided E2M1: L = truncation codes (lower bracket member, with sign).  A
-// value lies on a codeword exactly when truncating the next smaller magnitude
-// gives a different code (for +-0 that value is a NaN pattern, which the
-// convert maps to a saturated code, also different).  Off the grid, the upper
-// member is L+1 (never carries into the sign: k_lo <= 6 there); it is taken
+// Guided E2M1 from L = truncation codes (lower bracket member, with sign) and
+// Ld = truncation codes of the next smaller magnitude of each value.  A value
+// lies on a codeword exactly when L and Ld differ (for +-0 the next smaller
+// magnitude is a NaN pattern, which converts to a saturated code, also
+// different), or when L has magnitude 7: every value at or above 6 saturates
+// there and clamps to the codeword 6.  Off the grid the upper member is L+1
+// (never carries into the sign: the magnitude is at most 6 there); it is taken
 // when the LSB of L differs from the guide bit.
-__device__ __forceinline__ uint32_t encode8_guided_e2m1(const float v[8], uint32_t gbits) {
-    float vd[8];
-    #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float c = __builtin_amdgcn_fmed3f(v[j], -6.0f, 6.0f);
-        vd[j] = __uint_as_float(__float_as_uint(c) - 1u);
-    }
-    const uint32_t L = pack_trunc8(v);
-    const uint32_t Ld = pack_trunc8(vd);
+__device__ __forceinline__ uint32_t guided_from_trunc(uint32_t L, uint32_t Ld, uint32_t gbits) {
     uint32_t d = L ^ Ld;
     d |= d >> 1;
     d |= d >> 2;
-    const uint32_t on_grid = d & 0x11111111u;
+    const uint32_t seven = (((L & 0x77777777u) + 0x11111111u) & 0x88888888u) >> 3;
+    const uint32_t on_grid = (d | seven) & 0x11111111u;
     const uint32_t mism = (L ^ spread8_to_nibbles(gbits)) & 0x11111111u;
     return L + (mism & ~on_grid);
+}
+
+// v: already scaled values; the next smaller magnitude is the fp32 bit
+// pattern minus one.
+__device__ __forceinline__ uint32_t encode8_guided_e2m1(const float v[8], uint32_t gbits) {
+    float vd[8];
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) vd[j] = __uint_as_float(__float_as_uint(v[j]) - 1u);
+    return guided_from_trunc(pack_trunc8(v), pack_trunc8(vd), gbits);
+}
+
+// MXFP4 without the RHT: w are the bf16 inputs, the convert divides by
+// scale = 2^e.  The next smaller bf16 magnitude (pattern minus one per half)
+// serves as well as the next smaller fp32 one: every codeword times 2^e is a
+// bf16 value, so no codeword lies strictly between the two.
+__device__ __forceinline__ uint32_t encode8_guided_e2m1_bf16(const uint32_t w[4], uint32_t gbits, float scale) {
+    uint32_t wd[4];
+    #pragma unroll
+    for (int j = 0; j < 4; ++j)
+        wd[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w[j]) - (u16x2){1, 1});
+    return guided_from_trunc(pack_trunc8_bf16(w, scale), pack_trunc8_bf16(wd, scale), gbits);
 }
 
 // SR E2M1: the grid is uniform with step 0.5, 1, 2 on [0,2), [2,4), [4,6].
@@ -458,8 +490,6 @@ __device__ __forceinline__ uint32_t dpp_swap1(uint32_t v) {
 __device__ __forceinline__ uint32_t dpp_swap2(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
 }
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Largest |bf16| bit pattern of 16 values (8 dwords) with sign bits cleared;
 // >= 0x7F80 means the group holds a non-finite value.  Packed 16-bit max.

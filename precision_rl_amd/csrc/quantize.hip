@@ -160,9 +160,9 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         }
 
         // MXFP4 without the RHT: v = bf16 * 2^-e exactly, at most 8 significant
-        // bits.  Its E2M1 RTN and SR converts take y and divide by 2^e themselves.
+        // bits.  Its E2M1 converts take the inputs and divide by 2^e themselves.
         constexpr bool kShort = FMT == 1 && !RHT;
-        constexpr bool kInCvt = kShort && GRID == 0 && MODE != MODE_GUIDED;
+        constexpr bool kInCvt = kShort && GRID == 0;
         float v[16];
         float cscale = 1.0f;
         if constexpr (kInCvt) {
@@ -177,6 +177,9 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         if constexpr (kInCvt && MODE == MODE_RTN) {   // straight from the bf16 bits
             c0 = pack_rne8_bf16(gw, cscale);
             c1 = pack_rne8_bf16(gw + 4, cscale);
+        } else if constexpr (kInCvt && MODE == MODE_GUIDED) {
+            c0 = encode8_guided_e2m1_bf16(gw, gb[k] & 0xFFu, cscale);
+            c1 = encode8_guided_e2m1_bf16(gw + 4, gb[k] >> 8, cscale);
         } else {
             c0 = encode8<GRID, MODE, kShort>(v, r0, r1, gb[k] & 0xFFu, cscale);
             c1 = encode8<GRID, MODE, kShort>(v + 8, r2, r3, gb[k] >> 8, cscale);
