@@ -457,13 +457,32 @@ __device__ __forceinline__ void butterfly16(float a[16]) {
     }
 }
 
-// Sign mask of the RHT diagonal: bit j of word 0 of Philox(key = seed, counter (0,0,1,0)).
+// Sign mask of the RHT diagonal: bit j of word 0 of Philox(key = seed, counter
+// (0,0,1,0)).  The seed is the same for every lane; written with 32-bit
+// products so the compiler keeps the whole generator on the scalar unit.
 __device__ __forceinline__ uint32_t rht_sign_mask(uint64_t seed) {
-    return philox4x32_10(0u, 0u, 1u, 0u, (uint32_t)seed, (uint32_t)(seed >> 32)).w[0] & 0xFFFFu;
+    uint32_t x0 = 0u, x1 = 0u, x2 = 1u, x3 = 0u;
+    uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    #pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint32_t hi0 = __umulhi(x0, 0xD2511F53u), lo0 = x0 * 0xD2511F53u;
+        const uint32_t hi2 = __umulhi(x2, 0xCD9E8D57u), lo2 = x2 * 0xCD9E8D57u;
+        const uint32_t y0 = hi2 ^ x1 ^ k0, y2 = hi0 ^ x3 ^ k1;
+        x1 = lo2;
+        x3 = lo0;
+        x0 = y0;
+        x2 = y2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return x0 & 0xFFFFu;
 }
 
 // 16 bf16 (8 dwords) -> fp32, with optional forward RHT (signs first).
-template <bool RHT>
+// QUARTER = false leaves out the final exact multiply by 1/4: callers fold it
+// into their block scale.  (The butterfly sums of bf16 inputs are multiples of
+// 2^-133, so a * 1/4 is always exact; it never needs to be rounded.)
+template <bool RHT, bool QUARTER = true>
 __device__ __forceinline__ void widen16(const uint32_t w[8], uint32_t signs, float y[16]) {
     #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -475,8 +494,10 @@ __device__ __forceinline__ void widen16(const uint32_t w[8], uint32_t signs, flo
         for (int j = 0; j < 16; ++j)
             y[j] = __uint_as_float(__float_as_uint(y[j]) ^ (((signs >> j) & 1u) << 31));
         butterfly16(y);
-        #pragma unroll
-        for (int j = 0; j < 16; ++j) y[j] = y[j] * 0.25f;
+        if constexpr (QUARTER) {
+            #pragma unroll
+            for (int j = 0; j < 16; ++j) y[j] = y[j] * 0.25f;
+        }
     }
 }
 

@@ -50,11 +50,11 @@ __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
         #pragma unroll
         for (int u = 0; u < kAmaxU; ++u) {
             if constexpr (RHT) {
-                float y[16];
-                widen16<true>(w[u], signs, y);
+                float a[16];   // the transform before its exact factor 1/4
+                widen16<true, false>(w[u], signs, a);
                 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const uint32_t k = __float_as_uint(y[j]) & 0x7FFFFFFFu;
+                    const uint32_t k = __float_as_uint(a[j]) & 0x7FFFFFFFu;
                     m = k < 0x7F800000u ? max(m, k) : m;
                 }
             } else {
@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
             }
         }
     }
+    if constexpr (RHT) m = __float_as_uint(__uint_as_float(m) * 0.25f);   // exact: max |y| = max |a| / 4
     #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;

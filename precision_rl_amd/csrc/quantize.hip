@@ -14,7 +14,8 @@
 // [2,3,0,1]).  Stores: codes are 8 bytes per lane and the guide bits 2 bytes,
 // both covering contiguous runs per wave; the bf16 output of fake quantization
 // is transposed back and stored per half-group like the loads.  Every lane
-// runs every DPP step (only stores are predicated).
+// runs every DPP step (only stores are predicated).  Kernels with the RHT are
+// bound by arithmetic; they load each group directly and skip the exchange.
 //
 // Per block (scale) [FQT-FP4 §3; TETRAJET §3; TRACE-JA "TRACEの仕組み"]:
 //   NVFP4 scale code = E4M3 RNE of amax / RN(Gmax*s_t) (clamped to 448),
@@ -81,12 +82,23 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     auto gk = [&](int k) { return (hg0 + 128u * k + 64u * q) >> 1; };
 
     // Lanes past the end load the last half-group instead (in bounds, no
-    // branch); their results are never stored.
+    // branch); their results are never stored.  With the RHT the kernel is
+    // bound by arithmetic, not by memory, so each lane loads its own groups
+    // directly (two 16-byte loads each) and skips the pair exchange.
     uint32_t w[kH][4];
-    #pragma unroll
-    for (int s = 0; s < kH; ++s) {
-        const uint32_t hg = min(hg0 + 64u * s, nhg - 1u);
-        load16_nt(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld), w[s]);
+    if constexpr (RHT) {
+        #pragma unroll
+        for (int k = 0; k < kG; ++k) {
+            const uint32_t g = min(gk(k), p.ngroups - 1u);
+            load16_nt(p.x + half_offset<CONTIG>(2u * g, p.gpr, p.ld), w[2 * k]);
+            load16_nt(p.x + half_offset<CONTIG>(2u * g + 1u, p.gpr, p.ld), w[2 * k + 1]);
+        }
+    } else {
+        #pragma unroll
+        for (int s = 0; s < kH; ++s) {
+            const uint32_t hg = min(hg0 + 64u * s, nhg - 1u);
+            load16_nt(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld), w[s]);
+        }
     }
     uint32_t gb[kG], gs[kG];
     #pragma unroll
@@ -110,10 +122,17 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     for (int k = 0; k < kG; ++k) {
         const uint32_t g = gk(k);
         uint32_t gw[8];
-        pair_exchange(w[2 * k], w[2 * k + 1], q, gw, gw + 4);   // -> this lane's whole group
+        if constexpr (RHT) {
+            #pragma unroll
+            for (int j = 0; j < 4; ++j) { gw[j] = w[2 * k][j]; gw[4 + j] = w[2 * k + 1][j]; }
+        } else {
+            pair_exchange(w[2 * k], w[2 * k + 1], q, gw, gw + 4);   // -> this lane's whole group
+        }
 
+        // With the RHT, y holds the transform before its exact factor 1/4
+        // (a = 4 y); the 1/4 is applied to the block amax and folded into inv.
         float y[16];
-        widen16<RHT>(gw, signs, y);
+        widen16<RHT, false>(gw, signs, y);
 
         // block amax key: monotone in the amax (bf16 bits, or fp32 bits with the
         // RHT); NaN and Inf give keys >= 0x7F800000
@@ -122,7 +141,7 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             float m = 0.0f;
             #pragma unroll
             for (int j = 0; j < 16; ++j) m = __builtin_elementwise_maximum(m, fabsf(y[j]));
-            amax_key = __float_as_uint(m);
+            amax_key = __float_as_uint(m * 0.25f);
         } else {
             amax_key = amax_bits16(gw) << 16;
         }
@@ -169,6 +188,17 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             cscale = mx_scale(sc);
             #pragma unroll
             for (int j = 0; j < 16; ++j) v[j] = y[j];
+        } else if constexpr (RHT) {
+            // v = RN((a/4) * inv) = RN(a * (inv/4)) when inv/4 is exact: always
+            // for MXFP4 (a power of two >= 2^-129), and for NVFP4 unless inv < 2^-124
+            const float inv4 = inv * 0.25f;
+            if (FMT == 1 || inv >= 0x1p-124f) {
+                #pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = y[j] * inv4;
+            } else {
+                #pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = (y[j] * 0.25f) * inv;
+            }
         } else {
             #pragma unroll
             for (int j = 0; j < 16; ++j) v[j] = y[j] * inv;
@@ -191,14 +221,21 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             const bool ok = dequant16<FMT, GRID>(c0, c1, sc, ts, dv);
             uint32_t o[8];
             to_bf16x16(dv, ok, o);
-            // back to half-groups (the same exchange, inverted): slot 2k takes this
-            // lane's first half (q = 0) or the partner's second half (q = 1), slot
-            // 2k+1 the partner's first half (q = 0) or this lane's second half
-            uint32_t oa[4], ob[4];
-            pair_exchange(o, o + 4, q, oa, ob);
-            const uint32_t ha = hg0 + 128u * k, hb = ha + 64u;
-            if (ha < nhg) st_out4(p.fq_out + half_offset<false>(ha, p.gpr, p.ld_out), 0, oa[0], oa[1], oa[2], oa[3]);
-            if (hb < nhg) st_out4(p.fq_out + half_offset<false>(hb, p.gpr, p.ld_out), 0, ob[0], ob[1], ob[2], ob[3]);
+            if constexpr (RHT) {   // this lane's own group, as loaded
+                if (g < p.ngroups) {
+                    st_out4(p.fq_out + half_offset<false>(2u * g, p.gpr, p.ld_out), 0, o[0], o[1], o[2], o[3]);
+                    st_out4(p.fq_out + half_offset<false>(2u * g + 1u, p.gpr, p.ld_out), 0, o[4], o[5], o[6], o[7]);
+                }
+            } else {
+                // back to half-groups (the same exchange, inverted): slot 2k takes this
+                // lane's first half (q = 0) or the partner's second half (q = 1), slot
+                // 2k+1 the partner's first half (q = 0) or this lane's second half
+                uint32_t oa[4], ob[4];
+                pair_exchange(o, o + 4, q, oa, ob);
+                const uint32_t ha = hg0 + 128u * k, hb = ha + 64u;
+                if (ha < nhg) st_out4(p.fq_out + half_offset<false>(ha, p.gpr, p.ld_out), 0, oa[0], oa[1], oa[2], oa[3]);
+                if (hb < nhg) st_out4(p.fq_out + half_offset<false>(hb, p.gpr, p.ld_out), 0, ob[0], ob[1], ob[2], ob[3]);
+            }
         } else if (g < p.ngroups) {
             st_out2(p.codes, g, c0, c1);
             if constexpr (FMT == 0) {
