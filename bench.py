@@ -248,8 +248,16 @@ def headline(args, fq, torch, W, ceiling):
     ms = back_to_back(torch, lambda i: fq.fp4_fake_quantize(xs[i % P], cfg_rtn, None, outs[i % P]["gb"],
                                                             outs[i % P]["gs"], out=fqo[i % P]), args.steps)
     fake = report(ms, (2 + 1 / 8 + 1 / 32 + 2) * n, n, ceiling)
+    # full-code guided diagnostic: x against the rollout's RTN codes of x_r
+    for k in range(P):
+        step_fns(k)["quantize_rtn"]()
+    cnt = torch.empty(3, dtype=torch.int64, device="cuda")
+    ms = back_to_back(torch, lambda i: fq.fp4_guide_mismatch(xs[i % P], cfg_rtn, outs[i % P]["rc"], outs[i % P]["rs"],
+                                                             None, out=cnt), args.steps)
+    diag = dict(report(ms, (2 + 0.5 + 1 / 32) * n, n, ceiling),
+                **mismatch_counts(fq, xs[0], cfg_rtn, outs[0]["rc"], outs[0]["rs"], None))
     return dict(rows=rows, cols=cols, n=n, ms_step=ms_step, ms_serial=ms_serial, ms_two=ms_two, step_bytes=step_bytes,
-                kernels=kernels, bytes_per=bytes_per, x_h=x_h, xr_h=xr_h, outs=outs[0], fake=fake)
+                kernels=kernels, bytes_per=bytes_per, x_h=x_h, xr_h=xr_h, outs=outs[0], fake=fake, diag=diag)
 
 
 def parity_sample(torch, h, oracle_mod, rows_s=64):
@@ -291,6 +299,14 @@ def cpu_baseline(args, W, oracle_mod, h):
 
 
 # ---------------------------------------------------------------- other workloads
+def mismatch_counts(fq, x, cfg, rcodes, rscales, ts):
+    """Full-code guided diagnostic of x against a rollout's codes: how often the 1-bit guide
+    cannot reproduce the rollout's codeword (non-adjacent) or its code (mismatched)."""
+    n, nonadj, mism = (int(v) for v in fq.fp4_guide_mismatch(x, cfg, rcodes, rscales, ts).cpu())
+    return {"elements": n, "non_adjacent": nonadj, "mismatched": mism,
+            "non_adjacent_frac": nonadj / max(n, 1), "mismatched_frac": mism / max(n, 1)}
+
+
 def other_workloads(args, fq, torch, W, ceiling):
     res = {}
     it = args.config_iters
@@ -314,6 +330,9 @@ def other_workloads(args, fq, torch, W, ceiling):
     r["quantize_rtn"] = report(back_to_back(torch, lambda i: fq.fp4_quantize(xs[i % P], cfg, tss[i % P], codes=oc, scales=os_), it), 2.5625 * n, n, ceiling)
     r["quantize_rtn_emit"] = report(back_to_back(torch, lambda i: fq.fp4_quantize(xs[i % P], cfg, tss[i % P], emit=True, codes=oc, scales=os_, bits=ob), it), 2.6875 * n, n, ceiling)
     r["quantize_guided"] = report(back_to_back(torch, lambda i: fq.fp4_quantize_guided(xs[i % P], cfg, guides[i % P][2], guides[i % P][1], tss[i % P], codes=oc, scales=os_), it), 2.75 * n, n, ceiling)
+    cnt = torch.empty(3, dtype=torch.int64, device="cuda")
+    r["guide_mismatch"] = report(back_to_back(torch, lambda i: fq.fp4_guide_mismatch(xs[i % P], cfg, guides[i % P][0], guides[i % P][1], tss[i % P], out=cnt), it), 2.5625 * n, n, ceiling)
+    r["guide_mismatch_counts"] = mismatch_counts(fq, xs[0], cfg, guides[0][0], guides[0][1], tss[0])
     res["nvfp4_act_4096x2048"] = r
     del xs, xrs, guides
 
@@ -452,6 +471,7 @@ def main():
         "copy_ceiling": ceiling,
         "kernels": h["kernels"],
         "fake_quantize_guided_bf16": h["fake"],
+        "guide_mismatch_c2": h["diag"],
         "workloads": workloads,
         "source_sha": sha,
     }

@@ -187,6 +187,23 @@ fp4_status guide_unpack(const fp4_cfg* cfg, const void* guide_bits, const void* 
                         int64_t rows, int64_t cols, void* mant_u8, void* scales_out,
                         hipStream_t stream);
 
+/* Full-code guided diagnostic [TRACE-JA "量子化情報キャッシュ": one mantissa
+ * bit names the rollout's codeword only when that codeword brackets the
+ * training value; other cases are the rare non-adjacent mismatches].  Guided
+ * rounding of x with the guide bits taken from the rollout's full codes
+ * (their LSBs) and the rollout's block scales (and tensor scale, NVFP4), the
+ * result g compared with the rollout codes r.  Nothing else is written.
+ *   counts        device uint64[3], 8-byte aligned, overwritten:
+ *                 [0] elements of the blocks guided rounding encodes (finite
+ *                     input, finite rollout scale),
+ *                 [1] of those, |g| != |r| (non-adjacent: the bit cannot name r),
+ *                 [2] of those, g != r (sign included).
+ *   rollout_codes, rollout_scales  the rollout's quantization of a tensor of
+ *                 the same shape, in the layouts fp4_quantize writes. */
+fp4_status fp4_guide_mismatch(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                              const float* tensor_scale, const void* rollout_codes, const void* rollout_scales,
+                              unsigned long long* counts, hipStream_t stream);
+
 /* Standalone 16-point random Hadamard transform [UFP4 RHT section] of each
  * 16-group of a bf16 matrix: forward y = 1/4 H16 D x, inverse x = D 1/4 H16 y,
  * Sylvester order, butterfly stages h = 1,2,4,8 in fp32.  D_j = -1 iff bit j

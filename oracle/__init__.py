@@ -92,6 +92,8 @@ def lib():
         L.orc_guide_pack.argtypes = [C.POINTER(OrcCfg), P, P, I64, I64, P, P]
         L.orc_guide_unpack.restype = None
         L.orc_guide_unpack.argtypes = [C.POINTER(OrcCfg), P, P, I64, I64, P, P]
+        L.orc_guide_mismatch.restype = C.c_int
+        L.orc_guide_mismatch.argtypes = [C.POINTER(OrcCfg), P, I64, I64, I64, F, P, P, P]
         L.orc_encode_many.restype = None
         L.orc_encode_many.argtypes = [C.c_int, C.c_int, P, P, P, I64]
         L.orc_encode_breakpoints.restype = I64
@@ -242,3 +244,19 @@ def encode_breakpoints(grid: int, mode: int, aux: int, lo: int, hi: int, cap: in
     out = np.empty(cap, dtype=np.uint32)
     n = lib().orc_encode_breakpoints(grid, mode, aux, lo, hi, _p(out), cap)
     return out[:min(n, cap)].copy(), n
+
+
+def guide_mismatch(cfg: Cfg, x: np.ndarray, ts: float, rollout_codes: np.ndarray, rollout_scales: np.ndarray,
+                   cols: int | None = None) -> tuple:
+    """(elements, non-adjacent, mismatched) of 1-bit guided rounding against the rollout's full codes."""
+    x, rows, ld = _bf16_2d(x, cols)
+    cols = ld if cols is None else cols
+    xc = np.ascontiguousarray(x)
+    out = np.zeros(3, dtype=np.uint64)
+    cc = cfg.c()
+    rc = lib().orc_guide_mismatch(C.byref(cc), _p(xc), rows, cols, ld, ts,
+                                  _p(np.ascontiguousarray(rollout_codes, np.uint8)),
+                                  _p(np.ascontiguousarray(rollout_scales, np.uint8)), _p(out))
+    if rc:
+        raise ValueError(f"orc_guide_mismatch failed ({rc})")
+    return tuple(int(v) for v in out)

@@ -38,6 +38,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <float.h>
 
@@ -511,6 +512,62 @@ void orc_guide_unpack(const orc_cfg* cfg, const uint8_t* bits, const uint8_t* gs
     const int64_t n = rows * cols;
     for (int64_t i = 0; i < n; ++i) mant[i] = (bits[i / 8] >> (i % 8)) & 1u;
     memcpy(scales_out, gscales, (size_t)(n / block_size(cfg)));
+}
+
+/* ------------------------------------------------------------------ */
+/* full-code guided diagnostic [TRACE-JA "量子化情報キャッシュ": one     */
+/* mantissa bit names the rollout's codeword only when that codeword is */
+/* one of the two that bracket the training value; other cases are the */
+/* rare non-adjacent mismatches]                                        */
+/* ------------------------------------------------------------------ */
+
+/* The 1-bit guide is the LSB of each rollout code r and the guide scales are
+ * the rollout's block scales; g is the guided result for x.  Blocks that
+ * guided rounding does not encode (non-finite input after the RHT, NaN guide
+ * scale) are left out.
+ *   counts[0] = elements of the blocks taken into account,
+ *   counts[1] = of those, |g| != |r| (non-adjacent: the bit cannot name r),
+ *   counts[2] = of those, g != r (sign included).
+ * Returns 0, or 1 for an invalid shape, 2 when out of memory. */
+int orc_guide_mismatch(const orc_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                       float ts, const uint8_t* rcodes, const uint8_t* rscales, uint64_t counts[3]) {
+    const int B = block_size(cfg);
+    if (cols % B != 0) return 1;
+    const int64_t n = rows * cols, nblk = cols / B;
+    counts[0] = counts[1] = counts[2] = 0;
+    uint8_t* gbits = (uint8_t*)calloc((size_t)(n / 8 + 1), 1);
+    uint8_t* gcodes = (uint8_t*)malloc((size_t)(n / 2 + 1));
+    uint8_t* gscales = (uint8_t*)malloc((size_t)(n / B + 1));
+    if (!gbits || !gcodes || !gscales) {
+        free(gbits); free(gcodes); free(gscales);
+        return 2;
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        unsigned r = (rcodes[i / 2] >> (4 * (i % 2))) & 0xFu;
+        gbits[i / 8] |= (uint8_t)((r & 1u) << (i % 8));
+    }
+    orc_quantize(cfg, ORC_GUIDED, x, 0, rows, cols, ld, ts, gbits, rscales, gcodes, gscales, NULL);
+    const uint32_t signs = orc_rht_signs(cfg->rht_seed);
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nblk; ++b) {
+            float y[32], inv;
+            int finite = 1;
+            for (int g = 0; g < B; g += 16) load_group(cfg, x + r * ld, b * B + g, signs, y + g);
+            for (int j = 0; j < B; ++j)
+                if (!isfinite(y[j])) finite = 0;
+            if (!finite || !orc_guided_params(cfg, rscales[r * nblk + b], ts, &inv)) continue;
+            for (int j = 0; j < B; ++j) {
+                const int64_t i = r * cols + b * B + j;
+                const unsigned rc = (rcodes[i / 2] >> (4 * (i % 2))) & 0xFu;
+                const unsigned gc = (gcodes[i / 2] >> (4 * (i % 2))) & 0xFu;
+                counts[0] += 1;
+                counts[1] += (rc & 7u) != (gc & 7u);
+                counts[2] += rc != gc;
+            }
+        }
+    }
+    free(gbits); free(gcodes); free(gscales);
+    return 0;
 }
 
 /* ------------------------------------------------------------------ */

@@ -266,6 +266,35 @@ fp4_status fp4_fake_quantize(const fp4_cfg* cfg, int guided, const void* x_bf16,
                       "fake quantize launch");
 }
 
+fp4_status fp4_guide_mismatch(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                              const float* tensor_scale, const void* rollout_codes, const void* rollout_scales,
+                              unsigned long long* counts, hipStream_t stream) {
+    FP4Q_TRY(check_cfg(cfg));
+    FP4Q_TRY(need(counts, 8, "counts"));
+    uint64_t ng = 0;
+    FP4Q_TRY(check_matrix(rows, cols, ld, block_of(cfg->format), x_bf16, &ng));
+    fp4q::QuantParams p{};
+    p.counts = counts;
+    if (ng == 0) {   // nothing to count: clear the counters and return
+        p.ngroups = 0;
+        return hip_status(fp4q::launch_guide_mismatch(cfg->format, cfg->grid, cfg->rht16 != 0, true, p, stream),
+                          "guide mismatch launch");
+    }
+    FP4Q_TRY(need(rollout_codes, 16, "rollout_codes"));
+    FP4Q_TRY(need(rollout_scales, 1, "rollout_scales"));
+    if (cfg->format == FP4_NVFP4) FP4Q_TRY(need(tensor_scale, 4, "tensor_scale"));
+    p.x = static_cast<const uint16_t*>(x_bf16);
+    p.ld = ld;
+    p.ngroups = (uint32_t)ng;
+    p.gpr = fp4q::make_fastdiv((uint32_t)(cols / 16));
+    p.ts = tensor_scale;
+    p.rcodes = static_cast<const uint8_t*>(rollout_codes);
+    p.gscales = static_cast<const uint8_t*>(rollout_scales);
+    p.rht_seed = cfg->rht_seed;
+    return hip_status(fp4q::launch_guide_mismatch(cfg->format, cfg->grid, cfg->rht16 != 0, ld == cols, p, stream),
+                      "guide mismatch launch");
+}
+
 fp4_status fp4_dequantize(const fp4_cfg* cfg, const void* codes, const void* scales,
                           const float* tensor_scale, int64_t rows, int64_t cols, void* out,
                           int64_t ld_out, fp4_dtype dtype, hipStream_t stream) {

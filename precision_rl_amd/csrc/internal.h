@@ -45,6 +45,8 @@ struct QuantParams {
     uint64_t rht_seed;          // RHT: Philox key of the sign diagonal
     uint16_t* fq_out;           // fake quantization: bf16 output (dequantized codes)
     int64_t ld_out;             // its row stride in elements
+    const uint8_t* rcodes;      // guide diagnostic: the rollout's full codes (guide bits are their LSBs)
+    unsigned long long* counts; // guide diagnostic: elements, non-adjacent, mismatched (zeroed first)
 };
 
 // Up to kMaxGroup tensors sharing one configuration, quantized by one launch.
@@ -103,6 +105,10 @@ struct EncodeParams {
 // Launchers (return hipGetLastError() of the launch).
 hipError_t launch_quantize(int format, int grid, int mode, bool rht, bool emit, bool contig,
                            const QuantParams& p, hipStream_t s);
+// Guided rounding against the rollout's full codes (p.rcodes, p.gscales, p.ts):
+// adds the counts of elements, non-adjacent and mismatched codes to p.counts.
+hipError_t launch_guide_mismatch(int format, int grid, bool rht, bool contig, const QuantParams& p, hipStream_t s);
+
 // Quantize then dequantize to bf16 in one pass (p.fq_out, p.ld_out); no codes written.
 hipError_t launch_fake_quantize(int format, int grid, int mode, bool rht, bool contig,
                                 const QuantParams& p, hipStream_t s);

@@ -68,11 +68,18 @@ __device__ __forceinline__ void pair_exchange(const uint32_t a[4], const uint32_
     }
 }
 
+// Number of nonzero nibbles of w.
+__device__ __forceinline__ uint32_t nonzero_nibbles(uint32_t w) {
+    return __builtin_popcount((w | (w >> 1) | (w >> 2) | (w >> 3)) & 0x11111111u);
+}
+
 // One workgroup's share (kChunkGroups groups starting at chunk `wg`) of one tensor.
 // OUT = 0 stores codes, scales (and emitted guide bits); OUT = 1 stores the
-// dequantized bf16 values instead (fake quantization).
+// dequantized bf16 values instead (fake quantization); OUT = 2 (guided only)
+// takes the guide bits from the rollout's full codes and counts, instead of
+// storing anything, how often the guided result differs from those codes.
 template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG, int OUT = 0>
-__device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg) {
+__device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg, uint32_t* acc = nullptr) {
     constexpr float kGmax = GRID == 0 ? 6.0f : 7.0f;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t q = lane & 1u;
@@ -101,15 +108,23 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         }
     }
     uint32_t gb[kG], gs[kG];
+    v2u32 rc[kG];
     #pragma unroll
     for (int k = 0; k < kG; ++k) {
         gb[k] = gs[k] = 0u;
+        rc[k] = (v2u32){0u, 0u};
         if constexpr (MODE == MODE_GUIDED) {
             const uint32_t g = min(gk(k), p.ngroups - 1u);
-            gb[k] = reinterpret_cast<const uint16_t*>(p.gbits)[g];
+            if constexpr (OUT == 2) {
+                rc[k] = reinterpret_cast<const v2u32*>(p.rcodes)[g];
+                gb[k] = gather_nibble_lsbs(rc[k].x) | (gather_nibble_lsbs(rc[k].y) << 8);
+            } else {
+                gb[k] = reinterpret_cast<const uint16_t*>(p.gbits)[g];
+            }
             gs[k] = p.gscales[FMT == 0 ? g : (g >> 1)];
         }
     }
+    uint32_t n_elem = 0, n_nonadj = 0, n_mism = 0;   // OUT == 2
 
     const uint32_t signs = RHT ? rht_sign_mask(p.rht_seed) : 0u;   // uniform: scalar unit
     float ts = 1.0f, denom = 1.0f;
@@ -216,7 +231,14 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         }
         if (!finite) { c0 = 0; c1 = 0; }
 
-        if constexpr (OUT == 1) {
+        if constexpr (OUT == 2) {
+            if (finite && g < p.ngroups) {   // blocks guided rounding encodes
+                const uint32_t d0 = c0 ^ rc[k].x, d1 = c1 ^ rc[k].y;
+                n_elem += 16u;
+                n_nonadj += nonzero_nibbles(d0 & 0x77777777u) + nonzero_nibbles(d1 & 0x77777777u);
+                n_mism += nonzero_nibbles(d0) + nonzero_nibbles(d1);
+            }
+        } else if constexpr (OUT == 1) {
             float dv[16];
             const bool ok = dequant16<FMT, GRID>(c0, c1, sc, ts, dv);
             uint32_t o[8];
@@ -249,6 +271,12 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             }
         }
     }
+
+    if constexpr (OUT == 2) {
+        acc[0] += n_elem;
+        acc[1] += n_nonadj;
+        acc[2] += n_mism;
+    }
 }
 
 template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG>
@@ -276,6 +304,54 @@ hipError_t launch_grouped_t(const GroupedQuantParams& gp, hipStream_t s) {
     const uint32_t blocks = gp.wg_start[gp.n];
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_quantize_grouped<FMT, GRID, MODE, RHT, EMIT>), dim3(blocks), dim3(kThreads), 0, s, gp);
+    return hipGetLastError();
+}
+
+// At most kMismatchBlocks workgroups, each looping over chunks with its counts
+// in registers, then one atomic per counter and workgroup: thousands of
+// same-address atomics (one per chunk) would serialize and dominate.
+constexpr uint32_t kMismatchBlocks = 1024;
+
+template <int FMT, int GRID, bool RHT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void k_guide_mismatch(const QuantParams p, uint32_t nchunks) {
+    uint32_t acc[3] = {0u, 0u, 0u};
+    for (uint32_t wg = blockIdx.x; wg < nchunks; wg += gridDim.x)   // the same trip count in a workgroup
+        quantize_chunk<FMT, GRID, MODE_GUIDED, RHT, false, CONTIG, 2>(p, wg, acc);
+    __shared__ uint32_t red[3][kThreads / 64];
+    #pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        #pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) acc[c] += (uint32_t)__shfl_xor((int)acc[c], o);
+    }
+    if ((threadIdx.x & 63u) == 0) {
+        #pragma unroll
+        for (int c = 0; c < 3; ++c) red[c][threadIdx.x >> 6] = acc[c];
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) {
+        unsigned long long t = 0;
+        #pragma unroll
+        for (int wv = 0; wv < kThreads / 64; ++wv) t += red[threadIdx.x][wv];
+        if (t) atomicAdd(p.counts + threadIdx.x, t);
+    }
+}
+
+// Clears the three diagnostic counters (vector stores, one lane each).
+__global__ void k_zero_counts(unsigned long long* c) {
+    if (threadIdx.x < 3) c[threadIdx.x] = 0ull;
+}
+
+template <int FMT, int GRID>
+hipError_t launch_mismatch_g(bool rht, bool contig, const QuantParams& p, hipStream_t s) {
+    const uint32_t chunks = (p.ngroups + kChunkGroups - 1) / kChunkGroups;
+    const dim3 b(chunks < kMismatchBlocks ? chunks : kMismatchBlocks), t(kThreads);
+    if (rht) {
+        if (contig) hipLaunchKernelGGL((k_guide_mismatch<FMT, GRID, true, true>), b, t, 0, s, p, chunks);
+        else hipLaunchKernelGGL((k_guide_mismatch<FMT, GRID, true, false>), b, t, 0, s, p, chunks);
+    } else {
+        if (contig) hipLaunchKernelGGL((k_guide_mismatch<FMT, GRID, false, true>), b, t, 0, s, p, chunks);
+        else hipLaunchKernelGGL((k_guide_mismatch<FMT, GRID, false, false>), b, t, 0, s, p, chunks);
+    }
     return hipGetLastError();
 }
 
@@ -384,6 +460,15 @@ hipError_t launch_quantize_grouped(int format, int grid, int mode, bool rht, boo
     }
     return grid == 0 ? launch_grouped_m<1, 0>(mode, rht, emit, gp, s)
                      : launch_grouped_m<1, 1>(mode, rht, emit, gp, s);
+}
+
+hipError_t launch_guide_mismatch(int format, int grid, bool rht, bool contig, const QuantParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(64), 0, s, p.counts);
+    if (p.ngroups == 0) return hipGetLastError();
+    if (format == 0) {
+        return grid == 0 ? launch_mismatch_g<0, 0>(rht, contig, p, s) : launch_mismatch_g<0, 1>(rht, contig, p, s);
+    }
+    return grid == 0 ? launch_mismatch_g<1, 0>(rht, contig, p, s) : launch_mismatch_g<1, 1>(rht, contig, p, s);
 }
 
 hipError_t launch_fake_quantize(int format, int grid, int mode, bool rht, bool contig,

@@ -70,7 +70,7 @@ MAX_GROUP = 16
 
 _lib = None
 EXPORTS = ("fp4_tensor_scale", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
-           "fp4_fake_quantize", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_rht16",
+           "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_rht16",
            "fp4_encode_values", "fp4_stream_copy", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
            "fp4_status_str", "fp4_last_error")
 
@@ -92,6 +92,7 @@ def lib():
         "fp4_quantize_guided": [CP, P, I64, I64, I64, P, P, P, P, P, P],
         "fp4_quantize_grouped": [CP, I, I, C.POINTER(_CTensor), P],
         "fp4_fake_quantize": [CP, I, P, I64, I64, I64, P, P, P, P, I64, P],
+        "fp4_guide_mismatch": [CP, P, I64, I64, I64, P, P, P, P, P],
         "fp4_dequantize": [CP, P, P, P, I64, I64, P, I64, I, P],
         "guide_pack": [CP, P, P, I64, I64, P, P, P],
         "guide_unpack": [CP, P, P, I64, I64, P, P, P],
@@ -250,6 +251,20 @@ def fp4_fake_quantize(x: torch.Tensor, cfg: Fp4Config, tensor_scale: torch.Tenso
     _check(lib().fp4_fake_quantize(C.byref(c), int(guided), _ptr(x), rows, cols, ld, _ptr(tensor_scale),
                                    _ptr(guide_bits), _ptr(guide_scales), _ptr(out), ld_out, _stream(x)),
            "fp4_fake_quantize")
+    return out
+
+
+def fp4_guide_mismatch(x: torch.Tensor, cfg: Fp4Config, rollout_codes: torch.Tensor, rollout_scales: torch.Tensor,
+                       tensor_scale: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Guided rounding of x with the rollout's full codes as the guide, compared with those codes.
+    Returns a device int64[3]: elements counted, non-adjacent (|g| != |r|), mismatched (g != r)."""
+    _on_gpu(x, rollout_codes, rollout_scales, tensor_scale, out)
+    rows, cols, ld = _matrix(x)
+    if out is None:
+        out = torch.empty(3, dtype=torch.int64, device=x.device)
+    c = cfg.c()
+    _check(lib().fp4_guide_mismatch(C.byref(c), _ptr(x), rows, cols, ld, _ptr(tensor_scale), _ptr(rollout_codes),
+                                    _ptr(rollout_scales), _ptr(out), _stream(x)), "fp4_guide_mismatch")
     return out
 
 

@@ -29,7 +29,7 @@ def fq():
 
 def test_header_declares_the_expected_calls():
     names = _declared()
-    for n in ["fp4_quantize", "fp4_quantize_guided", "fp4_dequantize", "guide_pack", "guide_unpack",
+    for n in ["fp4_quantize", "fp4_quantize_guided", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_guide_mismatch",
               "fp4_rht16", "fp4_tensor_scale", "fp4_encode_values", "fp4_codes_bytes",
               "fp4_scales_bytes", "fp4_guide_bytes", "fp4_status_str", "fp4_last_error"]:
         assert n in names, n
@@ -87,6 +87,15 @@ def test_host_side_argument_errors(fq):
     assert L.fp4_dequantize(C.byref(c), C.c_void_p(A), C.c_void_p(A), C.c_void_p(A), 4, 32,
                             C.c_void_p(A), 16, 0, None) == 2
     assert L.fp4_rht16(C.c_void_p(A), 4, 40, 40, 7, 0, C.c_void_p(A), 0, None) == 2
+    # guide mismatch: counts pointer required and 8-byte aligned; shapes as for quantize
+    gm = L.fp4_guide_mismatch
+    assert gm(C.byref(c), C.c_void_p(A), 4, 32, 32, C.c_void_p(A), C.c_void_p(A), C.c_void_p(A), None, None) == 1
+    assert gm(C.byref(c), C.c_void_p(A), 4, 32, 32, C.c_void_p(A), C.c_void_p(A), C.c_void_p(A),
+              C.c_void_p(A + 4), None) == 3
+    assert gm(C.byref(c), C.c_void_p(A), 4, 24, 24, C.c_void_p(A), C.c_void_p(A), C.c_void_p(A),
+              C.c_void_p(A), None) == 2
+    assert gm(C.byref(c), C.c_void_p(A), 4, 32, 32, None, C.c_void_p(A), C.c_void_p(A),
+              C.c_void_p(A), None) == 1                   # NVFP4 needs the tensor scale
 
 
 def test_binding_refuses_cpu_tensors(fq):

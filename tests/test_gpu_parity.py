@@ -198,6 +198,31 @@ def test_special_blocks(fq):
                 assert (host(c) == oc_c).all(), (fmt, rht, rnd)
 
 
+@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("ts", [1e35, 3e34, 1.0])
+def test_guided_rht_with_tiny_reciprocals(fq, grid, ts):
+    # The RHT kernels fold the transform's factor 1/4 into inv unless inv < 2^-124.
+    # Guided mode takes block and tensor scales from the caller, so large guide
+    # scales with a large tensor scale reach the other branch: S = dec * ts > 2^124.
+    rows, cols = 32, 256
+    rng = np.random.default_rng(int(ts) % 97 + grid)
+    x = (rng.standard_normal((rows, cols)) * 1.5e37).astype(np.float32)
+    xh = W.f32_to_bf16_rne(x)
+    cfg = fq.Fp4Config(grid=grid, rht16=True, rht_seed=7)
+    oc = ocfg(cfg)
+    gb = rng.integers(0, 256, rows * cols // 8, dtype=np.uint8)
+    gs = rng.choice(np.array([0x7E, 0x7D, 0x76, 0x70, 0x58, 0x38], dtype=np.uint8), rows * cols // 16)
+    t32 = np.float32(ts)
+    c, s_ = fq.fp4_quantize_guided(dev(xh), cfg, torch.from_numpy(gb).cuda(), torch.from_numpy(gs).cuda(),
+                                   torch.tensor([t32], device="cuda"))
+    oc_c, oc_s = O.quantize(oc, O.GUIDED, xh, float(t32), guide_bits=gb, guide_scales=gs)
+    assert (host(s_) == oc_s).all() and (host(c) == oc_c).all()
+    if ts == 1e35:   # the branch is taken for some blocks and the codes are not all zero
+        S = np.array([O.e4m3_decode(int(v)) for v in gs]) * float(t32)
+        assert (S > 2.0 ** 124).any()
+        assert (host(c) != 0).any()
+
+
 def test_guided_with_nan_guide_scales(fq):
     rows, cols = 8, 64
     xh = W.c1_x(rows, cols, seed=2)
@@ -317,6 +342,48 @@ def test_dequant_bf16_ties(fq):
         got = fq.fp4_dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(sc).cuda(), cfg, 1, 512,
                                 torch.tensor([ts], device="cuda"), dtype=torch.bfloat16)
         assert (host(got.view(torch.int16)).reshape(-1) == want.view(np.int16)).all()
+
+
+@pytest.mark.parametrize("fmt,grid,rht", [(0, 0, False), (1, 0, False), (0, 1, True), (1, 1, True), (1, 0, True)])
+@pytest.mark.parametrize("shape,pad", [((256, 512), 0), ((37, 544), 24), ((3, 32), 0), ((129, 96), 8)])
+def test_guide_mismatch_vs_oracle(fq, fmt, grid, rht, shape, pad):
+    rows, cols = shape
+    if cols % (32 if fmt else 16):
+        pytest.skip("shape not valid for this block size")
+    x_h = W.c1_x(rows, cols, seed=rows + 1)
+    xr_h = W.c1_rollout(rows, cols, seed=rows + 1)
+    xr_h[::3] = W.f32_to_bf16_rne(W.bf16_to_f32(x_h[::3]) * np.float32(1.7))   # far rollout rows
+    cfg = fq.Fp4Config(format=fmt, grid=grid, rht16=rht, rht_seed=7)
+    oc = ocfg(cfg)
+    xr = dev(xr_h)
+    ts_t = fq.fp4_tensor_scale(xr, cfg) if fmt == 0 else None
+    ts = O.tensor_scale(oc, xr_h) if fmt == 0 else 1.0
+    rc, rs = fq.fp4_quantize(xr, cfg, ts_t)
+    o_rc, o_rs = O.quantize(oc, O.RTN, xr_h, ts)
+    assert (host(rc) == o_rc).all() and (host(rs) == o_rs).all()
+    counts = fq.fp4_guide_mismatch(dev(x_h, pad), cfg, rc, rs, ts_t)
+    want = O.guide_mismatch(oc, x_h, ts, o_rc, o_rs)
+    assert tuple(int(v) for v in host(counts)) == want
+    assert want[1] > 0
+
+
+def test_guide_mismatch_bracket_cases_and_empty(fq):
+    cases = [(2.4, 5), (2.4, 6), (2.4, 0xD), (2.0, 5), (2.0, 4), (-0.3, 9), (0.3, 8), (7.0, 6)] + [(1.0, 2)] * 8
+    x = np.array([[v for v, _ in cases] * 3], dtype=np.float32)
+    r = np.array([c for _, c in cases] * 3, dtype=np.uint8)
+    xh = W.f32_to_bf16_rne(x)
+    xh[0, 16 + 3] = 0x7FC0                                   # second block: non-finite input
+    rc = (r[0::2] | (r[1::2] << 4)).astype(np.uint8)
+    rs = np.array([0x38, 0x38, 0x7F], dtype=np.uint8)        # third block: NaN rollout scale
+    cfg = fq.Fp4Config()
+    ts = torch.ones(1, device="cuda")
+    counts = fq.fp4_guide_mismatch(dev(xh), cfg, torch.from_numpy(rc).cuda(), torch.from_numpy(rs).cuda(), ts)
+    assert tuple(int(v) for v in host(counts)) == O.guide_mismatch(O.Cfg(), xh, 1.0, rc, rs) == (16, 3, 5)
+    empty = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((3,), 7, dtype=torch.int64, device="cuda")
+    fq.fp4_guide_mismatch(empty, cfg, torch.empty(0, dtype=torch.uint8, device="cuda"),
+                          torch.empty(0, dtype=torch.uint8, device="cuda"), ts, out=out)
+    assert host(out).tolist() == [0, 0, 0]
 
 
 # ---------------------------------------------------------------- dequantize, guide, rht

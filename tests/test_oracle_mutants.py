@@ -111,6 +111,12 @@ MUTANTS = {
     "dequant_block_of_16_always": ("quantize", [("unsigned s = scales[i / B];", "unsigned s = scales[i / 16];")]),
     "dequant_drops_ts": ("quantize", [("val = orc_mul32(gd, ts);", "val = gd;")]),
     "dequant_nan_payload": ("quantize", [("uint32_t qnan = 0x7FC00000u;", "uint32_t qnan = 0x7FC00001u;")]),
+    "mismatch_nonadjacent_counts_sign": ("quantize", [("counts[1] += (rc & 7u) != (gc & 7u);",
+                                                         "counts[1] += rc != gc;")]),
+    "mismatch_counts_nonfinite_blocks": ("quantize", [("if (!finite || !orc_guided_params(cfg, rscales[r * nblk + b], ts, &inv)) continue;",
+                                                       "if (!orc_guided_params(cfg, rscales[r * nblk + b], ts, &inv)) continue;")]),
+    "mismatch_guide_from_wrong_bit": ("quantize", [("gbits[i / 8] |= (uint8_t)((r & 1u) << (i % 8));",
+                                                    "gbits[i / 8] |= (uint8_t)(((r >> 1) & 1u) << (i % 8));")]),
     "guide_pack_wrong_bit": ("quantize", [("bits[i / 8] |= (uint8_t)((code & 1u) << (i % 8));",
                               "bits[i / 8] |= (uint8_t)(((code >> 1) & 1u) << (i % 8));")]),
 }

@@ -427,3 +427,47 @@ def test_cache_is_one_sixth_of_full_codes_for_deep_half():
     full = W.C4_LAYERS * per_layer * Fraction(1, 2) + W.C4_LAYERS * per_layer * Fraction(1, 16)
     assert guide == 314_572_800 and full == 1_887_436_800
     assert guide / full == Fraction(1, 6)
+
+
+def _block_with(vals_codes):
+    """16 (x value, rollout code) pairs -> bf16 row, packed rollout codes."""
+    x = np.array([v for v, _ in vals_codes], dtype=np.float32)[None, :]
+    r = np.array([c for _, c in vals_codes], dtype=np.uint8)
+    return _bf16(x), _pack(r)
+
+
+def test_guide_mismatch_counts_the_bracket_cases(orc):
+    # unit scale (rollout block scale 0x38 = 1.0, tensor scale 1): v = |x|
+    cases = [(2.4, 5), (2.4, 6), (2.4, 0xD), (2.0, 5), (2.0, 4), (-0.3, 9), (0.3, 8), (7.0, 6)]
+    # 2.4 brackets {2, 3}: code 5 (3.0) is named by its LSB; code 6 (4.0, LSB 0) is not, the bit
+    # picks 2.0 instead; -3.0 has the right magnitude but the other sign.  2.0 is a codeword:
+    # it keeps code 4 whatever the bit.  7.0 clamps to the codeword 6 (code 7).
+    cases += [(1.0, 2)] * 8
+    xh, rc = _block_with(cases)
+    nan_block, nan_rc = _block_with([(1.0, 2)] * 16)
+    nan_block[0, 3] = 0x7FC0                       # non-finite input: block left out
+    sb, sb_rc = _block_with([(1.0, 2)] * 16)       # its scale will be the NaN code: left out
+    x = np.concatenate([xh, nan_block, sb], axis=1)
+    r = np.concatenate([rc, nan_rc, sb_rc])
+    scales = np.array([0x38, 0x38, 0x7F], dtype=np.uint8)
+    n, nonadj, mism = orc.guide_mismatch(orc.Cfg(), x, 1.0, r, scales)
+    assert (n, nonadj, mism) == (16, 3, 5)
+
+
+@pytest.mark.parametrize("fmt,grid,rht", [(0, 0, False), (1, 0, False), (0, 1, True), (1, 1, False)])
+def test_guide_mismatch_is_zero_for_the_own_rtn_and_recounts(orc, fmt, grid, rht):
+    R, C = 48, 256
+    x = W.c5_x(R, C, seed=8)
+    cfg = orc.Cfg(format=fmt, grid=grid, rht16=rht, rht_seed=7)
+    ts = orc.tensor_scale(cfg, x) if fmt == 0 else 1.0
+    rc, rs = orc.quantize(cfg, orc.RTN, x, ts)
+    assert orc.guide_mismatch(cfg, x, ts, rc, rs) == (R * C, 0, 0)
+    # a rollout of 1.7 x: recount from the oracle's guided codes
+    xr = _bf16(_f32(x) * np.float32(1.7))
+    rc2, rs2 = orc.quantize(cfg, orc.RTN, xr, ts)
+    gb = np.packbits((_unpack(rc2) & 1).astype(np.uint8), bitorder="little")
+    gc, _ = orc.quantize(cfg, orc.GUIDED, x, ts, guide_bits=gb, guide_scales=rs2)
+    g, r = _unpack(gc), _unpack(rc2)
+    want = (R * C, int(((g & 7) != (r & 7)).sum()), int((g != r).sum()))
+    assert orc.guide_mismatch(cfg, x, ts, rc2, rs2) == want
+    assert want[1] > R * C // 4
