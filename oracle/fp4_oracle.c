@@ -553,8 +553,7 @@ int orc_guide_mismatch(const orc_cfg* cfg, const uint16_t* x, int64_t rows, int6
             float y[32], inv;
             int finite = 1;
             for (int g = 0; g < B; g += 16) load_group(cfg, x + r * ld, b * B + g, signs, y + g);
-            for (int j = 0; j < B; ++j)
-                if (!isfinite(y[j])) finite = 0;
+            for (int j = 0; j < B; ++j) finite = finite && isfinite(y[j]);
             if (!finite || !orc_guided_params(cfg, rscales[r * nblk + b], ts, &inv)) continue;
             for (int j = 0; j < B; ++j) {
                 const int64_t i = r * cols + b * B + j;
