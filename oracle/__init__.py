@@ -94,6 +94,8 @@ def lib():
         L.orc_guide_unpack.argtypes = [C.POINTER(OrcCfg), P, P, I64, I64, P, P]
         L.orc_guide_mismatch.restype = C.c_int
         L.orc_guide_mismatch.argtypes = [C.POINTER(OrcCfg), P, I64, I64, I64, F, P, P, P]
+        L.orc_gemm_mx.restype = C.c_int
+        L.orc_gemm_mx.argtypes = [P, P, P, P, I64, I64, I64, P, P]
         L.orc_encode_many.restype = None
         L.orc_encode_many.argtypes = [C.c_int, C.c_int, P, P, P, I64]
         L.orc_encode_breakpoints.restype = I64
@@ -260,3 +262,22 @@ def guide_mismatch(cfg: Cfg, x: np.ndarray, ts: float, rollout_codes: np.ndarray
     if rc:
         raise ValueError(f"orc_guide_mismatch failed ({rc})")
     return tuple(int(v) for v in out)
+
+
+def gemm_mx(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray, b_scales: np.ndarray,
+            M: int, N: int, K: int) -> tuple:
+    """MXFP4 product A * B^T in float64: returns (C[M, N], sum_k |a b| [M, N]).
+
+    A is [M, K] and B is [N, K], each given as the codes and scales the MXFP4
+    quantizer writes for a row-major tensor (blocks of 32 along K)."""
+    ac = np.ascontiguousarray(a_codes, np.uint8).ravel()
+    asc = np.ascontiguousarray(a_scales, np.uint8).ravel()
+    bc = np.ascontiguousarray(b_codes, np.uint8).ravel()
+    bsc = np.ascontiguousarray(b_scales, np.uint8).ravel()
+    assert ac.size >= M * K // 2 and asc.size >= M * K // 32
+    assert bc.size >= N * K // 2 and bsc.size >= N * K // 32
+    c = np.empty((M, N), dtype=np.float64)
+    mag = np.empty((M, N), dtype=np.float64)
+    if lib().orc_gemm_mx(_p(ac), _p(asc), _p(bc), _p(bsc), M, N, K, _p(c), _p(mag)):
+        raise ValueError("oracle gemm: K must be a multiple of 32")
+    return c, mag

@@ -31,8 +31,8 @@
  * the correctly rounded fp32 result (double has more than 2*24+2 bits).
  *
  * Parity pins (see tests/test_oracle_*.py): grids, scale codecs, RTN, SR and
- * guided encodes, dequantization and the RHT are pinned against closed forms,
- * brute force and library routines.  Philox4x32-10 is pinned against rocRAND.
+ * guided encodes, dequantization, the RHT and the MXFP4 matrix product are
+ * pinned against closed forms, brute force and library routines.  Philox4x32-10 is pinned against rocRAND.
  * The RHT butterfly's rounding order is pinned only where every partial sum
  * is exact ("parity unpinned" beyond that: the order is a reading).
  */
@@ -566,6 +566,45 @@ int orc_guide_mismatch(const orc_cfg* cfg, const uint16_t* x, int64_t rows, int6
         }
     }
     free(gbits); free(gcodes); free(gscales);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 matrix product [TETRAJET §3-4: matrix products whose operands  */
+/* are both FP4 values with per-group scales]                          */
+/* ------------------------------------------------------------------ */
+
+/* Value of element i of an MXFP4 tensor with blocks of 32 along its rows:
+ * (-1)^sign * G[k] * 2^(e - 127), exact in double; NaN for a 0xFF scale. */
+static double mx_value(const uint8_t* codes, const uint8_t* scales, int64_t i) {
+    unsigned code = (codes[i / 2] >> (4 * (i % 2))) & 0xFu;
+    double v = orc_grid(ORC_E2M1, (int)(code & 7)) * orc_e8m0_decode(scales[i / 32]);
+    return (code & 8) ? -v : v;
+}
+
+/* C[m][n] = sum over k of a(m,k) * b(n,k), where a is the [M, K] tensor whose
+ * MXFP4 codes and scales are a_codes / a_scales (the layouts the quantizer
+ * writes for a row-major [M, K] input) and b likewise the [N, K] tensor of
+ * b_codes / b_scales: the product A * B^T with the reduction along the
+ * blocked dimension.  Every product is exact in double and the sum runs in k
+ * order in double.  absdot (may be NULL) receives sum over k of |a(m,k) b(n,k)|,
+ * the scale of the rounding error any fp32 summation may make.
+ * Returns 0, or 1 when K is not a multiple of 32. */
+int orc_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, double* c, double* absdot) {
+    if (K % 32 != 0) return 1;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double prod = mx_value(a_codes, a_scales, m * K + k) * mx_value(b_codes, b_scales, n * K + k);
+                acc += prod;
+                mag += fabs(prod);
+            }
+            c[m * N + n] = acc;
+            if (absdot) absdot[m * N + n] = mag;
+        }
+    }
     return 0;
 }
 

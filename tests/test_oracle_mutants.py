@@ -11,7 +11,10 @@ oracle that silently disarms a mutant fails here too.
 
 Not planted: rewrites that are equal in exact arithmetic and differ only in
 rounding order (for example the order of the RHT butterfly stages); that
-order is a reading of the pages and is not pinned by them.
+order is a reading of the pages and is not pinned by them.  Likewise not
+planted in the matrix product: one permutation of the K elements applied to
+both operands alike (say, reading the two nibbles of a byte the other way
+round), which leaves every result unchanged.
 """
 import os
 import subprocess
@@ -23,7 +26,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "fp4_oracle.c")
-PINS = ["codecs", "encode", "quantize", "philox_rht"]
+PINS = ["codecs", "encode", "quantize", "philox_rht", "gemm"]
 
 # name -> (pin file expected to catch it, run first; [(exact text, replacement), ...])
 MUTANTS = {
@@ -117,6 +120,16 @@ MUTANTS = {
                                                        "if (!orc_guided_params(cfg, rscales[r * nblk + b], ts, &inv)) continue;")]),
     "mismatch_guide_from_wrong_bit": ("quantize", [("gbits[i / 8] |= (uint8_t)((r & 1u) << (i % 8));",
                                                     "gbits[i / 8] |= (uint8_t)(((r >> 1) & 1u) << (i % 8));")]),
+    # MXFP4 matrix product
+    "gemm_sign_from_wrong_bit": ("gemm", [("return (code & 8) ? -v : v;", "return (code & 4) ? -v : v;")]),
+    "gemm_scale_per_16": ("gemm", [("orc_e8m0_decode(scales[i / 32])", "orc_e8m0_decode(scales[i / 16])")]),
+    "gemm_nan_scale_ignored": ("gemm", [("orc_e8m0_decode(scales[i / 32])", "ldexp(1.0, (int)scales[i / 32] - 127)")]),
+    "gemm_uniform_grid": ("gemm", [("orc_grid(ORC_E2M1, (int)(code & 7))", "orc_grid(ORC_UNIFORM, (int)(code & 7))")]),
+    "gemm_a_transposed": ("gemm", [("mx_value(a_codes, a_scales, m * K + k)", "mx_value(a_codes, a_scales, k * M + m)")]),
+    "gemm_b_reversed": ("gemm", [("mx_value(b_codes, b_scales, n * K + k)", "mx_value(b_codes, b_scales, n * K + (K - 1 - k))")]),
+    "gemm_drops_last_block": ("gemm", [("for (int64_t k = 0; k < K; ++k) {\n                const double prod",
+                                        "for (int64_t k = 0; k < K - 32; ++k) {\n                const double prod")]),
+    "gemm_absdot_signed": ("gemm", [("mag += fabs(prod);", "mag += prod;")]),
     "guide_pack_wrong_bit": ("quantize", [("bits[i / 8] |= (uint8_t)((code & 1u) << (i % 8));",
                               "bits[i / 8] |= (uint8_t)(((code >> 1) & 1u) << (i % 8));")]),
 }
