@@ -204,6 +204,29 @@ fp4_status fp4_guide_mismatch(const fp4_cfg* cfg, const void* x_bf16, int64_t ro
                               const float* tensor_scale, const void* rollout_codes, const void* rollout_scales,
                               unsigned long long* counts, hipStream_t stream);
 
+/* MXFP4 matrix product on the matrix cores [TETRAJET section 3: FP4 values
+ * with one scale per group; section 4: the matrix products of every linear
+ * layer take MXFP4 operands]:
+ *   C[m][n] = sum over k of a(m,k) * b(n,k),   m < M, n < N, k < K,
+ * where a is the [M, K] tensor given by a_codes / a_scales and b the [N, K]
+ * tensor given by b_codes / b_scales, each in exactly the layouts fp4_quantize
+ * writes for a row-major input with format FP4_MXFP4 and the E2M1 grid:
+ * codes K/2 bytes per row, E8M0 scales K/32 bytes per row (blocks of 32
+ * along K).  So C = A * B^T; for a linear layer y = x W^T, A holds the
+ * activations [tokens, in] and B the weight [out, in].
+ *   The products are summed in fp32 by the matrix cores, in an order of
+ * their own: |C - C_exact| <= (K + 1) 2^-24 sum_k |a b| + K 2^-149 holds for
+ * finite results.  A 0xFF (NaN) scale makes the results of its row of A or
+ * B NaN.  Output dense enough for row stride ldc >= N elements: fp32, or
+ * bf16 by round-to-nearest-even of the fp32 result.
+ *   K % 32 == 0 (K == 0 writes zeros); M == 0 or N == 0 is a no-op.
+ *   Alignment: codes 16 bytes, scales 1 byte, c 4 (fp32) or 2 (bf16) bytes.
+ *   The grid of the codes is E2M1 only: the uniform grid and NVFP4 blocks
+ *   are not accepted by this product (the caller keeps them apart). */
+fp4_status fp4_gemm_mxfp4(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
+                          int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, fp4_dtype dtype,
+                          hipStream_t stream);
+
 /* Standalone 16-point random Hadamard transform [UFP4 RHT section] of each
  * 16-group of a bf16 matrix: forward y = 1/4 H16 D x, inverse x = D 1/4 H16 y,
  * Sylvester order, butterfly stages h = 1,2,4,8 in fp32.  D_j = -1 iff bit j

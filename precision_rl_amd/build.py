@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp4q.so")
-SOURCES = ["abi.hip", "quantize.hip", "misc.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "misc.hip", "gemm.hip"]
 HEADERS = ["device.h", "internal.h"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -356,6 +356,40 @@ fp4_status guide_unpack(const fp4_cfg* cfg, const void* guide_bits, const void* 
     return hip_status(fp4q::launch_guide_unpack(cfg->format, p, stream), "guide_unpack launch");
 }
 
+fp4_status fp4_gemm_mxfp4(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
+                          int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, fp4_dtype dtype,
+                          hipStream_t stream) {
+    if (dtype != FP4_OUT_F32 && dtype != FP4_OUT_BF16) return fail(FP4_ERR_ARG, "unknown dtype %d", (int)dtype);
+    if (M < 0 || N < 0 || K < 0)
+        return fail(FP4_ERR_ARG, "negative shape M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
+    if (K % 32 != 0) return fail(FP4_ERR_SHAPE, "K=%lld is not a multiple of 32", (long long)K);
+    if (M == 0 || N == 0) return ok();
+    if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 40))
+        return fail(FP4_ERR_SHAPE, "shape too large M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
+    if ((uint64_t)((M + 127) / 128) * (uint64_t)((N + 127) / 128) >= (1ull << 31))
+        return fail(FP4_ERR_SHAPE, "too many 128 x 128 tiles of C");
+    if (ldc < N) return fail(FP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    FP4Q_TRY(need(c, dtype == FP4_OUT_BF16 ? 2 : 4, "c"));
+    if (K > 0) {
+        FP4Q_TRY(need(a_codes, 16, "a_codes"));
+        FP4Q_TRY(need(a_scales, 1, "a_scales"));
+        FP4Q_TRY(need(b_codes, 16, "b_codes"));
+        FP4Q_TRY(need(b_scales, 1, "b_scales"));
+    }
+    fp4q::GemmParams p{};
+    p.a = static_cast<const uint8_t*>(a_codes);
+    p.as = static_cast<const uint8_t*>(a_scales);
+    p.b = static_cast<const uint8_t*>(b_codes);
+    p.bs = static_cast<const uint8_t*>(b_scales);
+    p.c = c;
+    p.ldc = ldc;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.tiles_n = (uint32_t)((N + 127) / 128);
+    return hip_status(fp4q::launch_gemm_mx(dtype == FP4_OUT_BF16, p, stream), "gemm launch");
+}
+
 fp4_status fp4_rht16(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
                      int inverse, void* out, fp4_dtype dtype, hipStream_t stream) {
     if (dtype != FP4_OUT_F32 && dtype != FP4_OUT_BF16) return fail(FP4_ERR_ARG, "unknown dtype %d", (int)dtype);

@@ -102,6 +102,19 @@ struct EncodeParams {
     uint32_t n8;                // number of 8-element units
 };
 
+// MXFP4 matrix product C[M, N] = A[M, K] * B[N, K]^T (codes and E8M0 scales
+// along K, as the quantizer writes them); K % 32 == 0, M, N >= 1.
+struct GemmParams {
+    const uint8_t* a;           // A codes, K/2 bytes per row
+    const uint8_t* as;          // A scales, K/32 bytes per row
+    const uint8_t* b;
+    const uint8_t* bs;
+    void* c;                    // fp32 or bf16, row stride ldc elements
+    int64_t ldc;
+    int64_t M, N, K;
+    uint32_t tiles_n;           // 128-column tiles of C
+};
+
 // Launchers (return hipGetLastError() of the launch).
 hipError_t launch_quantize(int format, int grid, int mode, bool rht, bool emit, bool contig,
                            const QuantParams& p, hipStream_t s);
@@ -124,5 +137,8 @@ hipError_t launch_guide_unpack(int format, const GuideParams& p, hipStream_t s);
 hipError_t launch_rht16(bool inverse, bool bf16_out, bool contig, const RhtParams& p, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n16, hipStream_t s);
 hipError_t launch_encode_values(int grid, int mode, const EncodeParams& p, hipStream_t s);
+// Workgroups (128 x 128 tiles of C) of the MXFP4 product.
+uint32_t gemm_tiles(int64_t M, int64_t N);
+hipError_t launch_gemm_mx(bool bf16_out, const GemmParams& p, hipStream_t s);
 
 }  // namespace fp4q

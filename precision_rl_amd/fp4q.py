@@ -70,7 +70,8 @@ MAX_GROUP = 16
 
 _lib = None
 EXPORTS = ("fp4_tensor_scale", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
-           "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_rht16",
+           "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_unpack",
+           "fp4_gemm_mxfp4", "fp4_rht16",
            "fp4_encode_values", "fp4_stream_copy", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
            "fp4_status_str", "fp4_last_error")
 
@@ -96,6 +97,7 @@ def lib():
         "fp4_dequantize": [CP, P, P, P, I64, I64, P, I64, I, P],
         "guide_pack": [CP, P, P, I64, I64, P, P, P],
         "guide_unpack": [CP, P, P, I64, I64, P, P, P],
+        "fp4_gemm_mxfp4": [P, P, P, P, I64, I64, I64, P, I64, I, P],
         "fp4_rht16": [P, I64, I64, I64, C.c_uint64, I, P, I, P],
         "fp4_encode_values": [I, I, P, P, I64, P, P],
         "fp4_stream_copy": [P, P, C.c_size_t, P],
@@ -281,6 +283,21 @@ def fp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, cfg: Fp4Config, ro
     c = cfg.c()
     _check(lib().fp4_dequantize(C.byref(c), _ptr(codes), _ptr(scales), _ptr(tensor_scale), rows, cols,
                                 _ptr(out), ld_out, kind, _stream(codes)), "fp4_dequantize")
+    return out
+
+
+def fp4_gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
+                   M: int, N: int, K: int, dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[M, N] = A * B^T from the MXFP4 codes and scales of A [M, K] and B [N, K] (blocks along K)."""
+    _on_gpu(a_codes, a_scales, b_codes, b_scales, out)
+    if out is None:
+        out = torch.empty((M, N), dtype=dtype, device=a_codes.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("gemm output must be bfloat16 or float32")
+    ldc = out.stride(0) if M > 1 else N
+    kind = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    _check(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
+                                _ptr(out), ldc, kind, _stream(a_codes)), "fp4_gemm_mxfp4")
     return out
 
 

@@ -24,6 +24,9 @@ pages name no dataset for this path, so all values are synthetic):
   and activations 8192 x 4096 N(0,1); rollout copies add relative 1e-3 noise.
 * ``c5``  GEMM operand 65536 x 8192, N(0,1) with 0.5 % outliers x30 (uniform
   grid, RHT16, SR).
+* ``mx_operand``  raw MXFP4 operands for the matrix product: uniformly random
+  code bytes and E8M0 scale bytes drawn from a stated range (the product's
+  parity inputs; the benchmark quantizes the c4 tensors instead).
 """
 from __future__ import annotations
 
@@ -204,6 +207,23 @@ def c5_shape(small: bool = False):
 
 def c5_x(rows=65536, cols=8192, seed=7, r0=0, r1=None) -> np.ndarray:
     return f32_to_bf16_rne(normal_outliers_f32(rows, cols, seed, 0, 5e-3, 30.0, r0, r1))
+
+
+# Raw MXFP4 operand [rows, K]: codes uint8[rows*K/2], scales uint8[rows*K/32]
+def mx_operand(rows: int, K: int, seed: int, stream: int, scale_lo: int = 118, scale_hi: int = 133,
+               r0: int = 0, r1=None):
+    r1 = rows if r1 is None else r1
+
+    def codes(c, n):
+        return _rng(seed, stream, c).integers(0, 256, (n, K // 2), dtype=np.uint8)
+
+    def scales(c, n):
+        return _rng(seed, stream + 1, c).integers(scale_lo, scale_hi + 1, (n, K // 32), dtype=np.uint8)
+    return _gen(rows, K // 2, r0, r1, codes), _gen(rows, K // 32, r0, r1, scales)
+
+
+# Matrix product workload: activations [8192, 4096] times one expert weight [1536 out, 4096 in]
+GEMM_SHAPE = (8192, 1536, 4096)
 
 
 C5_RHT_SEED = 7

@@ -30,7 +30,7 @@ def fq():
 def test_header_declares_the_expected_calls():
     names = _declared()
     for n in ["fp4_quantize", "fp4_quantize_guided", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_guide_mismatch",
-              "fp4_rht16", "fp4_tensor_scale", "fp4_encode_values", "fp4_codes_bytes",
+              "fp4_gemm_mxfp4", "fp4_rht16", "fp4_tensor_scale", "fp4_encode_values", "fp4_codes_bytes",
               "fp4_scales_bytes", "fp4_guide_bytes", "fp4_status_str", "fp4_last_error"]:
         assert n in names, n
 
@@ -96,6 +96,24 @@ def test_host_side_argument_errors(fq):
               C.c_void_p(A), None) == 2
     assert gm(C.byref(c), C.c_void_p(A), 4, 32, 32, None, C.c_void_p(A), C.c_void_p(A),
               C.c_void_p(A), None) == 1                   # NVFP4 needs the tensor scale
+
+
+def test_gemm_host_side_errors(fq):
+    g = fq.lib().fp4_gemm_mxfp4
+    A = 1 << 20
+    p = C.c_void_p(A)
+    assert g(p, p, p, p, -1, 4, 64, p, 4, 0, None) == 1          # negative shape
+    assert g(p, p, p, p, 4, 4, 48, p, 4, 0, None) == 2           # K % 32
+    assert g(p, p, p, p, 4, 8, 64, p, 4, 0, None) == 2           # ldc < N
+    assert g(p, p, p, p, 4, 4, 64, p, 4, 9, None) == 1           # unknown dtype
+    assert g(None, p, p, p, 4, 4, 64, p, 4, 0, None) == 1        # null A codes
+    assert g(p, p, p, None, 4, 4, 64, p, 4, 0, None) == 1        # null B scales
+    assert g(C.c_void_p(A + 8), p, p, p, 4, 4, 64, p, 4, 0, None) == 3   # codes not 16-byte aligned
+    assert g(p, p, p, p, 4, 4, 64, C.c_void_p(A + 2), 4, 0, None) == 3   # fp32 output not 4-byte aligned
+    assert g(p, p, p, p, 1 << 31, 4, 64, p, 4, 0, None) == 2     # M too large
+    # M == 0 or N == 0 is a no-op that touches nothing
+    assert g(None, None, None, None, 0, 4, 64, None, 4, 0, None) == 0
+    assert g(None, None, None, None, 4, 0, 64, None, 0, 1, None) == 0
 
 
 def test_binding_refuses_cpu_tensors(fq):
