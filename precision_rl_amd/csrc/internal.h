@@ -112,7 +112,8 @@ struct GemmParams {
     void* c;                    // fp32 or bf16, row stride ldc elements
     int64_t ldc;
     int64_t M, N, K;
-    uint32_t tiles_n;           // 128-column tiles of C
+    uint32_t tiles_n;           // column tiles of C
+    uint32_t xcd_remap;         // 1: hand out tiles XCD by XCD (grid size a multiple of 8)
 };
 
 // Launchers (return hipGetLastError() of the launch).
@@ -137,8 +138,6 @@ hipError_t launch_guide_unpack(int format, const GuideParams& p, hipStream_t s);
 hipError_t launch_rht16(bool inverse, bool bf16_out, bool contig, const RhtParams& p, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n16, hipStream_t s);
 hipError_t launch_encode_values(int grid, int mode, const EncodeParams& p, hipStream_t s);
-// Workgroups (128 x 128 tiles of C) of the MXFP4 product.
-uint32_t gemm_tiles(int64_t M, int64_t N);
 hipError_t launch_gemm_mx(bool bf16_out, const GemmParams& p, hipStream_t s);
 
 }  // namespace fp4q

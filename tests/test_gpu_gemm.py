@@ -157,6 +157,24 @@ def test_empty_is_noop(fq):
     torch.cuda.synchronize()
 
 
+def test_large_tiles_ragged_sampled(fq):
+    # enough 256 x 192 tiles to fill the chip, with ragged last tiles in both M and N
+    M, N, K = 4100, 3000, 256
+    say(f"gemm large tiles ragged M={M} N={N} K={K}")
+    a, asc = W.mx_operand(M, K, seed=51, stream=0)
+    b, bsc = W.mx_operand(N, K, seed=52, stream=0)
+    rng = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([rng.choice(M, 32, replace=False), np.arange(M - 8, M), np.arange(0, 4)]))
+    cols = np.unique(np.concatenate([rng.choice(N, 32, replace=False), np.arange(N - 8, N), np.arange(0, 4)]))
+    e_rows, m_rows = O.gemm_mx(a[rows], asc[rows], b, bsc, len(rows), N, K)
+    e_cols, m_cols = O.gemm_mx(a, asc, b[cols], bsc[cols], M, len(cols), K)
+    for dtype in (torch.float32, torch.bfloat16):
+        got = run(fq, a, asc, b, bsc, M, N, K, dtype)
+        bf = dtype == torch.bfloat16
+        check(got[rows], e_rows, m_rows, K, bf, f"large tiles rows {dtype}")
+        check(got[:, cols], e_cols, m_cols, K, bf, f"large tiles cols {dtype}")
+
+
 def test_full_size_expert_gemm_sampled(fq):
     # the benchmark's product: activations [8192, 4096] x expert weight [1536, 4096]^T, bf16 and fp32 out;
     # 64 sampled rows x all columns and all rows x 48 sampled columns checked against the oracle
