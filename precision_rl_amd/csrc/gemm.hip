@@ -175,33 +175,49 @@ __global__ __launch_bounds__(256) void k_gemm_mx_any(const GemmParams p) {
 }  // namespace
 
 // ---------------------------------------------------------------- main path
-// K % 128 == 0: operands stream into LDS by direct buffer-to-LDS loads, three
-// stages deep, so no registers hold data in flight and two stages of loads
-// overlap each stage's MFMAs.  A wave instruction writes 64 lanes x 16 bytes
-// contiguously, so the tile cannot be padded; instead a row's four 16-byte
-// pieces (one per scale block) sit in the order blk ^ swz(row), which puts
-// the 16 rows that 16 consecutive lanes read at one block on 16 distinct
-// 16-byte bank groups (and any 8 consecutive rows on 8).  Loads of rows past
-// M or N fall outside the buffer range and return zeros.
+// K % 512 == 0.  A workgroup of 4 waves (2 x 2) computes a (64 WM) x (64 WN)
+// tile of C.  K advances 256 values per stage: 128 bytes of codes per row,
+// one whole cache line -- the memory system's cost is per line touched, and
+// 64-byte half lines would halve the load rate.  Both operands stream into LDS
+// by direct buffer-to-LDS loads (no registers hold data in flight), double
+// buffered.  A wave instruction writes 64 lanes x 16 bytes contiguously, so
+// the tile cannot be padded; instead the eight 16-byte pieces of a staged row
+// (one per scale block) sit in the order blk ^ swz(row), which puts the 16
+// rows that 16 consecutive lanes read at one block on 16 distinct 16-byte
+// bank groups (and any 8 consecutive rows on 8).  The scales of four stages
+// (32 bytes of a row) come in with one load per row.  Loads of rows past M or
+// N fall outside the buffer range and return zeros.
 
-// Piece order of a staged row: bits 1-2 of the row xor bits 3-4.
-static __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// Piece order of a staged row of 8 pieces: low 3 bits of row ^ (row >> 3).
+static __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kScaleChunk = 4;   // stages whose scales one load per row brings
 
 template <int WM, int WN>
 struct LdsTile {
     static constexpr int RA = 64 * WM, RB = 64 * WN;      // rows of A and B per tile
-    static constexpr int CODE_BYTES = (RA + RB) * 64;     // one stage of codes
-    static constexpr int STAGE_BYTES = CODE_BYTES + (RA + RB) * 4;
-    static constexpr int NCODE = (RA + RB) / 16;          // wave loads of codes per stage
-    static constexpr int NSCALE = (RA + RB) / 64;         // wave loads of scales per stage
+    static constexpr int ROWS = RA + RB;                  // stacked: A rows, then B rows
+    static constexpr int CODE_BYTES = ROWS * 128;         // one stage of codes
+    static constexpr int SCALE_BYTES = ROWS * 32;         // one chunk of scales (4 stages x 8 blocks)
+    static constexpr int NCODE = ROWS / 8;                // wave loads of codes per stage (8 rows each)
+    static constexpr int NCW = NCODE / 4;                 // ... per wave: 2 (WM + WN)
+    static constexpr int NSCALE = ROWS / 32;              // wave loads of scales per chunk (32 rows each)
+    static constexpr int NSQ = (NSCALE + 3) / 4;          // scale loads every wave issues per stage
+    static constexpr int BATCH = NCW + NSQ;               // loads every wave issues per stage
+    // scale loads with nothing to load (not the first stage of a chunk, or
+    // past the last row block) still issue, with an empty range, into a sink
+    static constexpr int SINK_BYTES = 4 * NSQ * 1024;
+    static constexpr int LDS_BYTES = 2 * CODE_BYTES + 2 * SCALE_BYTES + SINK_BYTES;
+    static_assert(NCODE % 4 == 0, "code loads split evenly over the 4 waves");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
 };
-
-constexpr int kStages = 3;
 
 // s_waitcnt immediate: at most n vector-memory operations of this wave outstanding.
 #define FP4Q_VMCNT(n) (0x0F70 | ((n) & 0xF) | (((n) >> 4) << 14))
+// s_waitcnt immediate: no LDS operation of this wave outstanding.
+#define FP4Q_LGKMCNT0 0xC07F
 
 // Workgroup barrier without a memory fence: the waits before it are explicit,
 // and the empty asm statements keep the compiler from moving LDS accesses
@@ -218,39 +234,115 @@ static int gemm_config(int64_t M, int64_t N) {
     return ((M + 255) / 256) * ((N + 191) / 192) >= 256 ? 1 : 0;
 }
 
-// This wave's share of the direct-to-LDS loads of one stage (wave loads
-// i = wave, wave + 4, ...; see the kernel) into LDS stage buffer buf.
 __device__ __forceinline__ int clamp31(int64_t v) { return (int)(v > 0x7FFFFFFF ? 0x7FFFFFFF : v); }
 
 struct Bases {
     const uint8_t *a, *b, *as, *bs;   // first row of this tile in each operand
     int na, nb, nas, nbs;             // bytes from there to the end of each operand (clamped)
+    int rowb;                         // bytes per row of codes
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 
-template <int WM, int WN, int PER>
-__device__ __forceinline__ void issue_stage(uint8_t* smem, const Bases& bs, const int* voff, int wave,
-                                            int64_t step, int buf) {
+// This wave's loads of stage t, all issued whatever t, so that the K loop has
+// no branches: code load q (stacked rows 8 i .. 8 i + 7, i = wave + 4 q) into
+// code buffer t % 2, and scale load q (stacked rows 32 j .. 32 j + 31,
+// j = wave + 4 q) into scale buffer (t / 4) % 2 when t starts a chunk.  Loads
+// with nothing to load (t past the last stage, a scale load off a chunk start,
+// j past the last row block) get an empty range: they move no data and write
+// zeros into LDS the kernel no longer reads (scale loads into the sink).
+// PART selects which of the loads to issue: 0 all, 1 the scale loads and the
+// first half of the code loads, 2 the second half of the code loads.
+template <int WM, int WN, int PART = 0>
+__device__ __forceinline__ void issue_stage(uint8_t* smem, const Bases& bs, const int* voff, const int* soff,
+                                            int wave, int t, int steps) {
     using T = LdsTile<WM, WN>;
-    constexpr int NL = T::NCODE + T::NSCALE;
-    uint8_t* st = smem + buf * T::STAGE_BYTES;
+    const bool live = t < steps;
+    uint8_t* cb = smem + (t & 1) * T::CODE_BYTES;
+    const __amdgpu_buffer_rsrc_t ra = rsrc(bs.a, live ? bs.na : 0);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(bs.b, live ? bs.nb : 0);
+    constexpr int Q0 = PART == 2 ? T::NCW / 2 : 0, Q1 = PART == 1 ? T::NCW / 2 : T::NCW;
     #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int i = wave + 4 * q;
-        if (i < T::NCODE) {
-            const bool isa = i < T::RA / 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isa ? rsrc(bs.a, bs.na) : rsrc(bs.b, bs.nb),
-                                                     (lds_ptr_t)(st + i * 1024), 16, voff[q], (int)(step * 64), 0, 0);
-        } else if (i < NL) {
-            const int j = i - T::NCODE;
-            const bool isa = j < T::RA / 64;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isa ? rsrc(bs.as, bs.nas) : rsrc(bs.bs, bs.nbs),
-                                                     (lds_ptr_t)(st + T::CODE_BYTES + j * 256), 4, voff[q],
-                                                     (int)(step * 4), 0, 0);
+    for (int q = Q0; q < Q1; ++q) {
+        // stacked row 32 q + (8 wave + lane / 8): its piece order depends on q only through q & 1
+        const int vo = voff[q & 1] + (int)((32 * q - (q < 2 * WM ? 0 : T::RA)) * bs.rowb);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 2 * WM ? ra : rb, (lds_ptr_t)(cb + (wave + 4 * q) * 1024), 16,
+                                                 vo, t * 128, 0, 0);
+    }
+    if constexpr (PART == 2) return;
+    const bool chunk = live && (t & (kScaleChunk - 1)) == 0;
+    uint8_t* sb = smem + 2 * T::CODE_BYTES + ((t / kScaleChunk) & 1) * T::SCALE_BYTES;
+    uint8_t* sink = smem + 2 * T::CODE_BYTES + 2 * T::SCALE_BYTES;
+    #pragma unroll
+    for (int q = 0; q < T::NSQ; ++q) {
+        const int j = wave + 4 * q;
+        const bool real = chunk && j < T::NSCALE;
+        const __amdgpu_buffer_rsrc_t r = j < 2 * WM ? rsrc(bs.as, real ? bs.nas : 0) : rsrc(bs.bs, real ? bs.nbs : 0);
+        const int so = soff[q];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)((real ? sb : sink) + j * 1024), 16, so, t * 8, 0, 0);
+    }
+}
+
+// Operands of K slice KS of stage st for this wave: A rows of 32-row blocks
+// rowA0 .. rowA0 + WM - 1 and B rows of blocks rowB0 .. rowB0 + WN - 1 of the
+// stacked tile, 16 bytes per lane (block 2 KS + kc of the lane's row).
+template <int WM, int WN, int KS>
+__device__ __forceinline__ void read_ops(const uint8_t* smem, int st, const int (&roff)[4][2], int rowA0, int rowB0,
+                                         v4u32 (&a)[WM], v4u32 (&b)[WN]) {
+    const uint8_t* ca = smem + (st & 1) * LdsTile<WM, WN>::CODE_BYTES;
+    #pragma unroll
+    for (int i = 0; i < WM; ++i) {
+        const int m = rowA0 + i;
+        a[i] = *reinterpret_cast<const v4u32*>(ca + roff[KS][m & 1] + m * 32 * 128);
+    }
+    #pragma unroll
+    for (int j = 0; j < WN; ++j) {
+        const int m = rowB0 + j;
+        b[j] = *reinterpret_cast<const v4u32*>(ca + roff[KS][m & 1] + m * 32 * 128);
+    }
+}
+
+// Scale word W (blocks 4 W .. 4 W + 3) of stage st for this wave's rows,
+// moved down by 8 kc bits so that byte 2 (ks & 1) is the lane's block 2 ks + kc
+// for the K slices ks = 2 W, 2 W + 1.
+template <int WM, int WN, int W>
+__device__ __forceinline__ void read_scales(const uint8_t* sbase, int st, int scA, int scB, int kc,
+                                            uint32_t (&sa)[WM], uint32_t (&sb)[WN]) {
+    const uint8_t* sc = sbase + ((st / kScaleChunk) & 1) * LdsTile<WM, WN>::SCALE_BYTES +
+                        8 * (st & (kScaleChunk - 1)) + 4 * W;
+    #pragma unroll
+    for (int i = 0; i < WM; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(sc + scA + i * 32 * 32) >> (8 * kc);
+    #pragma unroll
+    for (int j = 0; j < WN; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(sc + scB + j * 32 * 32) >> (8 * kc);
+}
+
+// The WM x WN MFMAs of K slice KS; ua, ub hold the scale word of this slice.
+template <int WM, int WN, int KS>
+__device__ __forceinline__ void mfmas(v16f (&acc)[WM][WN], const v4u32 (&a)[WM], const v4u32 (&b)[WN],
+                                      const uint32_t (&ua)[WM], const uint32_t (&ub)[WN]) {
+    #pragma unroll
+    for (int i = 0; i < WM; ++i) {
+        const v8i av = (v8i){(int)a[i].x, (int)a[i].y, (int)a[i].z, (int)a[i].w, 0, 0, 0, 0};
+        #pragma unroll
+        for (int j = 0; j < WN; ++j) {
+            const v8i bv = (v8i){(int)b[j].x, (int)b[j].y, (int)b[j].z, (int)b[j].w, 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 4, 4, 2 * (KS & 1),
+                                                                      (int)ua[i], 2 * (KS & 1), (int)ub[j]);
         }
+    }
+}
+
+// One element of C: fp32, or bf16 by round-to-nearest-even.
+template <bool BF16>
+__device__ __forceinline__ void store_c(__amdgpu_buffer_rsrc_t rc, int voff, float v) {
+    if constexpr (BF16) {
+        const bf16x2 h = __builtin_convertvector((v2f){v, 0.0f}, bf16x2);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(__builtin_bit_cast(uint32_t, h) & 0xFFFFu), rc, voff, 0,
+                                              0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, voff, 0, 0);
     }
 }
 
@@ -281,25 +373,19 @@ __global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
     bs.nas = clamp31((p.M - m0) * srow);
     bs.nbs = clamp31((p.N - n0) * srow);
 
-    // wave load i of a stage: codes i < NCODE (rows 16 i' .. 16 i' + 15 of A, then of B),
-    // then scales (rows 64 j .. 64 j + 63 of A, then of B); this wave takes i = wave, wave + 4, ...
-    constexpr int NL = T::NCODE + T::NSCALE;
-    constexpr int PER = (NL + 3) / 4;
-    static_assert(PER <= 63, "vmcnt range");
-    const int cnt = (NL - wave + 3) / 4;   // loads this wave issues per stage: PER or PER - 1
-    int voff[PER];
+    // per-lane offsets of this wave's loads (the stage enters as a scalar offset)
+    bs.rowb = (int)rowb;
+    int voff[2], soff[T::NSQ];
     #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int i = wave + 4 * q;
-        if (i < T::NCODE) {
-            const int ia = i < T::RA / 16 ? i : i - T::RA / 16;
-            const int row = 16 * ia + (lane >> 2);
-            voff[q] = (int)(row * rowb) + 16 * ((lane & 3) ^ swz(row));
-        } else {
-            const int j = i - T::NCODE;
-            const int ja = j < T::RA / 64 ? j : j - T::RA / 64;
-            voff[q] = (int)((64 * ja + lane) * srow);
-        }
+    for (int q = 0; q < 2; ++q) {
+        const int row = 8 * (wave + 4 * q) + (lane >> 3);              // stacked row of code load q
+        voff[q] = (int)((8 * wave + (lane >> 3)) * rowb) + 16 * ((lane & 7) ^ swz(row));
+    }
+    #pragma unroll
+    for (int q = 0; q < T::NSQ; ++q) {
+        const int j = wave + 4 * q;
+        const int row = 32 * j + (lane >> 1);
+        soff[q] = (int)((j < 2 * WM ? row : row - T::RA) * srow) + 16 * (lane & 1);
     }
 
     v16f acc[WM][WN];
@@ -308,77 +394,104 @@ __global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
         #pragma unroll
         for (int j = 0; j < WN; ++j) acc[i][j] = (v16f){};
 
-    const int64_t steps = p.K / 128;
+    // Each stage is four MFMA K slices (ks = 0..3; lane block 2 ks + kc).  The
+    // operands of slice ks + 2 are read from LDS while the MFMAs of slice ks
+    // run, so that every wave keeps many LDS reads in flight; between the
+    // second and third slices' MFMAs the workgroup meets at the barrier that
+    // certifies the next stage's loads, starts the loads of the stage after it
+    // into the buffers just read, and reads the next stage's scales and first
+    // two slices.
+    const int steps = (int)(p.K / 256);   // >= 2, even
+    // A stacked row 32 m + r32 holds block blk at piece blk ^ swz(row) =
+    // blk ^ lsw ^ 4 (m & 1), lsw = (r32 ^ r32 / 8) & 7: one lane offset per K
+    // slice and parity of m, the rest an immediate
+    int roff[4][2];
     #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-        if (s < steps) issue_stage<WM, WN, PER>(smem, bs, voff, wave, s, s);
-    for (int64_t s = 0; s < steps; ++s) {
-        const int buf = (int)(s % kStages);
-        // this wave's loads of stage s are done once at most those of stage s + 1 remain
-        // (loads complete in order); the barrier then covers every wave's loads
-        if (s + 1 < steps) {
-            if (cnt == PER) __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(PER));
-            else __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(PER - 1));
-        } else {
-            __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
-        }
-        barrier_only();
-        if (s + kStages - 1 < steps)
-            issue_stage<WM, WN, PER>(smem, bs, voff, wave, s + kStages - 1,
-                                     (int)((s + kStages - 1) % kStages));
-        const uint8_t* sa_codes = smem + buf * T::STAGE_BYTES;
-        const uint8_t* sb_codes = sa_codes + T::RA * 64;
-        const uint32_t* sa_sc = reinterpret_cast<const uint32_t*>(sa_codes + T::CODE_BYTES);
-        const uint32_t* sb_sc = sa_sc + T::RA;
-        uint32_t sca[WM], scb[WN];
+    for (int ks = 0; ks < 4; ++ks)
         #pragma unroll
-        for (int i = 0; i < WM; ++i) sca[i] = sa_sc[wm * 32 * WM + i * 32 + r32];
-        #pragma unroll
-        for (int j = 0; j < WN; ++j) scb[j] = sb_sc[wn * 32 * WN + j * 32 + r32];
-        #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int blk = 2 * ks + kc;
-            v8i a[WM], b[WN];
-            #pragma unroll
-            for (int i = 0; i < WM; ++i) {
-                const int row = wm * 32 * WM + i * 32 + r32;
-                const v4u32 v = *reinterpret_cast<const v4u32*>(sa_codes + row * 64 + 16 * (blk ^ swz(row)));
-                a[i] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            }
-            #pragma unroll
-            for (int j = 0; j < WN; ++j) {
-                const int row = wn * 32 * WN + j * 32 + r32;
-                const v4u32 v = *reinterpret_cast<const v4u32*>(sb_codes + row * 64 + 16 * (blk ^ swz(row)));
-                b[j] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            }
-            #pragma unroll
-            for (int i = 0; i < WM; ++i)
-                #pragma unroll
-                for (int j = 0; j < WN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        a[i], b[j], acc[i][j], 4, 4, 0, (int)(sca[i] >> (8 * blk)), 0, (int)(scb[j] >> (8 * blk)));
-        }
-    }
+        for (int par = 0; par < 2; ++par)
+            roff[ks][par] = r32 * 128 + 16 * ((2 * ks + kc) ^ ((r32 ^ (r32 >> 3)) & 7) ^ (4 * par));
+    const int rowA0 = wm * WM, rowB0 = T::RA / 32 + wn * WN;   // first 32-row blocks of this wave
+    const int scA = (wm * 32 * WM + r32) * 32, scB = (T::RA + wn * 32 * WN + r32) * 32;
 
+    // operand sets for K slices 0..3 of a stage (read two slices ahead of their MFMAs)
+    v4u32 a0[WM], b0[WN], a1[WM], b1[WN], a2[WM], b2[WN], a3[WM], b3[WN];
+    uint32_t sa0[WM], sb0[WN], sa1[WM], sb1[WN];   // scale words 0 and 1 of the stage
+    const uint8_t* sbase = smem + 2 * T::CODE_BYTES;
+
+    issue_stage<WM, WN>(smem, bs, voff, soff, wave, 0, steps);
+    issue_stage<WM, WN>(smem, bs, voff, soff, wave, 1, steps);
+    // stage 0 is in once only stage 1's loads remain (loads complete in order)
+    __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(T::BATCH));
+    barrier_only();
+    read_scales<WM, WN, 0>(sbase, 0, scA, scB, kc, sa0, sb0);
+    read_ops<WM, WN, 0>(smem, 0, roff, rowA0, rowB0, a0, b0);
+    read_ops<WM, WN, 1>(smem, 0, roff, rowA0, rowB0, a1, b1);
+    for (int s = 0; s + 1 < steps; ++s) {
+        read_ops<WM, WN, 2>(smem, s, roff, rowA0, rowB0, a2, b2);
+        read_scales<WM, WN, 1>(sbase, s, scA, scB, kc, sa1, sb1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas<WM, WN, 0>(acc, a0, b0, sa0, sb0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_ops<WM, WN, 3>(smem, s, roff, rowA0, rowB0, a3, b3);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas<WM, WN, 1>(acc, a1, b1, sa0, sb0);
+        __builtin_amdgcn_sched_barrier(0);
+        // this wave's reads of stage s and its loads of stage s + 1 are done; after
+        // the barrier every wave's are, so stage s + 2 may load into stage s's buffers
+        __builtin_amdgcn_s_waitcnt(FP4Q_LGKMCNT0);
+        __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
+        barrier_only();
+        read_scales<WM, WN, 0>(sbase, s + 1, scA, scB, kc, sa0, sb0);
+        read_ops<WM, WN, 0>(smem, s + 1, roff, rowA0, rowB0, a0, b0);
+        issue_stage<WM, WN, 1>(smem, bs, voff, soff, wave, s + 2, steps);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas<WM, WN, 2>(acc, a2, b2, sa1, sb1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_ops<WM, WN, 1>(smem, s + 1, roff, rowA0, rowB0, a1, b1);
+        issue_stage<WM, WN, 2>(smem, bs, voff, soff, wave, s + 2, steps);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas<WM, WN, 3>(acc, a3, b3, sa1, sb1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+        const int s = steps - 1;
+        read_ops<WM, WN, 2>(smem, s, roff, rowA0, rowB0, a2, b2);
+        read_ops<WM, WN, 3>(smem, s, roff, rowA0, rowB0, a3, b3);
+        read_scales<WM, WN, 1>(sbase, s, scA, scB, kc, sa1, sb1);
+        mfmas<WM, WN, 0>(acc, a0, b0, sa0, sb0);
+        mfmas<WM, WN, 1>(acc, a1, b1, sa0, sb0);
+        mfmas<WM, WN, 2>(acc, a2, b2, sa1, sb1);
+        mfmas<WM, WN, 3>(acc, a3, b3, sa1, sb1);
+    }
+    // the loads issued past the last stage must land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
+
+    // C: result r of MFMA tile (i, j) in this lane is row 32 i + 8 (r / 4) + 4 kc + r % 4, column
+    // 32 j + r32 of the wave's quarter.  Stores go through a buffer resource whose range ends at
+    // row M, and where a lane's column in tile j is at or past N, all of that tile's stores from
+    // the lane are offset past the range, so the hardware drops every element outside C without
+    // a test per element.
+    constexpr int ESZ = BF16 ? 2 : 4;
+    // the row stride passes through an opaque copy here, so that none of the
+    // offsets below is computed ahead of the K loop and held in registers through it
+    int ldcb = (int)(p.ldc * ESZ);
+    asm volatile("" : "+s"(ldcb));
+    const int64_t row0 = m0 + wm * 32 * WM, col0 = n0 + wn * 32 * WN;
+    uint8_t* cw = reinterpret_cast<uint8_t*>(p.c) + (row0 * p.ldc + col0) * ESZ;
+    const int64_t crange = p.M > row0 ? (p.M - row0) * p.ldc * ESZ : 0;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(cw, (short)0, clamp31(crange), 0x00020000);
+    int vlane[WN];
+    #pragma unroll
+    for (int j = 0; j < WN; ++j)
+        vlane[j] = col0 + 32 * j + r32 < p.N ? 4 * kc * ldcb + (32 * j + r32) * ESZ : (int)0x80000000u;
     #pragma unroll
     for (int i = 0; i < WM; ++i)
         #pragma unroll
-        for (int j = 0; j < WN; ++j) {
-            const int64_t col = n0 + wn * 32 * WN + j * 32 + r32;
+        for (int j = 0; j < WN; ++j)
             #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 32 * WM + i * 32 + 8 * (r >> 2) + 4 * kc + (r & 3);
-                if (row < p.M && col < p.N) {
-                    if constexpr (BF16) {
-                        const bf16x2 h = __builtin_convertvector((v2f){acc[i][j][r], 0.0f}, bf16x2);
-                        reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + col] =
-                            (uint16_t)(__builtin_bit_cast(uint32_t, h) & 0xFFFFu);
-                    } else {
-                        reinterpret_cast<float*>(p.c)[row * p.ldc + col] = acc[i][j][r];
-                    }
-                }
-            }
-        }
+            for (int r = 0; r < 16; ++r)
+                store_c<BF16>(rc, vlane[j] + (32 * i + 8 * (r >> 2) + (r & 3)) * ldcb, acc[i][j][r]);
 }
 
 template <int WM, int WN>
@@ -388,19 +501,20 @@ static hipError_t launch_lds(bool bf16_out, GemmParams p, hipStream_t s) {
     p.tiles_n = (uint32_t)((p.N + T::RB - 1) / T::RB);
     const uint32_t g = tiles_m * p.tiles_n;
     p.xcd_remap = g % 8 == 0 ? 1u : 0u;
-    const size_t lds = (size_t)kStages * T::STAGE_BYTES;
-    if (bf16_out) hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, true>), dim3(g), dim3(256), lds, s, p);
-    else hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, false>), dim3(g), dim3(256), lds, s, p);
+    if (bf16_out) hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, true>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
+    else hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, false>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_mx(bool bf16_out, const GemmParams& p, hipStream_t s) {
-    const bool scale4 = p.K % 128 == 0 && ((uintptr_t)p.as & 3) == 0 && ((uintptr_t)p.bs & 3) == 0;
-    if (scale4 && p.K > 0 && p.K < (1ll << 24)) {
-        const int cfg = gemm_config(p.M, p.N);
-        if (cfg == 1) return launch_lds<4, 3>(bf16_out, p, s);
+    // main path: K a multiple of 512 (whole stages and 16-byte aligned scale loads)
+    const bool main_path = p.K % 512 == 0 && p.K > 0 && p.K < (1ll << 24) && ((uintptr_t)p.as & 15) == 0 &&
+                           ((uintptr_t)p.bs & 15) == 0;
+    if (main_path) {
+        if (gemm_config(p.M, p.N) == 1) return launch_lds<4, 3>(bf16_out, p, s);
         return launch_lds<2, 2>(bf16_out, p, s);
     }
+    const bool scale4 = p.K % 128 == 0 && ((uintptr_t)p.as & 3) == 0 && ((uintptr_t)p.bs & 3) == 0;
     GemmParams q = p;
     q.tiles_n = (uint32_t)((p.N + kTile - 1) / kTile);
     const dim3 grid((uint32_t)(((p.M + kTile - 1) / kTile) * q.tiles_n)), block(256);

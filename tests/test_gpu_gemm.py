@@ -60,6 +60,9 @@ def check(got, exact, mag, K, bf16, tag):
     bad = ~(err <= tol)
     rel = float((err / np.maximum(mag, 1e-300)).max()) if err.size else 0.0
     say(f"{tag}: max |err|/sum|ab| = {rel:.3e} (fp32 bound {(K + 1) * 2.0 ** -24:.3e})")
+    if bad.any():
+        where = np.argwhere(bad)
+        say(f"{tag}: bad rows {np.unique(where[:, 0])[:20]} cols {np.unique(where[:, 1])[:40]}")
     assert not bad.any(), f"{tag}: {int(bad.sum())} results outside the bound, first at {np.argwhere(bad)[0]}"
 
 
@@ -78,14 +81,15 @@ def test_random_operands(fq, M, N, K, dtype):
     check(got, exact, mag, K, dtype == torch.bfloat16, f"random {M}x{N}x{K}")
 
 
-def test_padded_output_rows(fq):
-    M, N, K = 150, 70, 256
-    say(f"gemm padded ldc M={M} N={N} K={K}")
+@pytest.mark.parametrize("M,N,K,ldc", [(150, 70, 256, 96), (130, 300, 1024, 320), (300, 200, 512, 232)])
+def test_padded_output_rows(fq, M, N, K, ldc):
+    # columns N .. ldc - 1 of every row must keep their sentinel: a store past N would land there
+    say(f"gemm padded ldc M={M} N={N} K={K} ldc={ldc}")
     a, asc = W.mx_operand(M, K, seed=5, stream=0)
     b, bsc = W.mx_operand(N, K, seed=6, stream=0)
     exact, mag = O.gemm_mx(a, asc, b, bsc, M, N, K)
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).ravel()).cuda()
-    buf = torch.full((M, 96), -7.0, dtype=torch.float32, device="cuda")
+    buf = torch.full((M, ldc), -7.0, dtype=torch.float32, device="cuda")
     fq.fp4_gemm_mxfp4(dev(a), dev(asc), dev(b), dev(bsc), M, N, K, out=buf[:, :N])
     torch.cuda.synchronize()
     h = buf.cpu().numpy()
@@ -158,8 +162,9 @@ def test_empty_is_noop(fq):
 
 
 def test_large_tiles_ragged_sampled(fq):
-    # enough 256 x 192 tiles to fill the chip, with ragged last tiles in both M and N
-    M, N, K = 4100, 3000, 256
+    # enough 256 x 192 tiles to fill the chip, with ragged last tiles in both M and N; the output
+    # rows are padded with a sentinel that no store may touch
+    M, N, K = 4100, 3000, 512
     say(f"gemm large tiles ragged M={M} N={N} K={K}")
     a, asc = W.mx_operand(M, K, seed=51, stream=0)
     b, bsc = W.mx_operand(N, K, seed=52, stream=0)
@@ -168,8 +173,14 @@ def test_large_tiles_ragged_sampled(fq):
     cols = np.unique(np.concatenate([rng.choice(N, 32, replace=False), np.arange(N - 8, N), np.arange(0, 4)]))
     e_rows, m_rows = O.gemm_mx(a[rows], asc[rows], b, bsc, len(rows), N, K)
     e_cols, m_cols = O.gemm_mx(a, asc, b[cols], bsc[cols], M, len(cols), K)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).ravel()).cuda()
     for dtype in (torch.float32, torch.bfloat16):
-        got = run(fq, a, asc, b, bsc, M, N, K, dtype)
+        buf = torch.full((M, N + 40), -7.0, dtype=dtype, device="cuda")
+        fq.fp4_gemm_mxfp4(dev(a), dev(asc), dev(b), dev(bsc), M, N, K, out=buf[:, :N])
+        torch.cuda.synchronize()
+        h = buf.float().cpu().numpy()
+        assert (h[:, N:] == -7.0).all(), "the product wrote past N in a padded row"
+        got = h[:, :N].astype(np.float64)
         bf = dtype == torch.bfloat16
         check(got[rows], e_rows, m_rows, K, bf, f"large tiles rows {dtype}")
         check(got[:, cols], e_cols, m_cols, K, bf, f"large tiles cols {dtype}")
