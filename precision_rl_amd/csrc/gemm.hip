@@ -304,32 +304,34 @@ __device__ __forceinline__ void read_ops(const uint8_t* smem, int st, const int 
     }
 }
 
-// Scale word W (blocks 4 W .. 4 W + 3) of stage st for this wave's rows,
-// moved down by 8 kc bits so that byte 2 (ks & 1) is the lane's block 2 ks + kc
-// for the K slices ks = 2 W, 2 W + 1.
-template <int WM, int WN, int W>
+// Both scale words of stage st for this wave's rows (word w: blocks 4 w ..
+// 4 w + 3), moved down by 8 kc bits so that byte 2 (ks & 1) of word ks / 2 is
+// the lane's block 2 ks + kc.  One 8-byte read per row: rows lie 32 bytes
+// apart, so narrower reads would cost the same bank conflicts twice.
+template <int WM, int WN>
 __device__ __forceinline__ void read_scales(const uint8_t* sbase, int st, int scA, int scB, int kc,
-                                            uint32_t (&sa)[WM], uint32_t (&sb)[WN]) {
-    const uint8_t* sc = sbase + ((st / kScaleChunk) & 1) * LdsTile<WM, WN>::SCALE_BYTES +
-                        8 * (st & (kScaleChunk - 1)) + 4 * W;
+                                            v2u32 (&sa)[WM], v2u32 (&sb)[WN]) {
+    const uint8_t* sc = sbase + ((st / kScaleChunk) & 1) * LdsTile<WM, WN>::SCALE_BYTES + 8 * (st & (kScaleChunk - 1));
     #pragma unroll
-    for (int i = 0; i < WM; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(sc + scA + i * 32 * 32) >> (8 * kc);
+    for (int i = 0; i < WM; ++i) sa[i] = *reinterpret_cast<const v2u32*>(sc + scA + i * 32 * 32) >> (8 * kc);
     #pragma unroll
-    for (int j = 0; j < WN; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(sc + scB + j * 32 * 32) >> (8 * kc);
+    for (int j = 0; j < WN; ++j) sb[j] = *reinterpret_cast<const v2u32*>(sc + scB + j * 32 * 32) >> (8 * kc);
 }
 
-// The WM x WN MFMAs of K slice KS; ua, ub hold the scale word of this slice.
+// The WM x WN MFMAs of K slice KS with the stage's scale words ua, ub.
 template <int WM, int WN, int KS>
 __device__ __forceinline__ void mfmas(v16f (&acc)[WM][WN], const v4u32 (&a)[WM], const v4u32 (&b)[WN],
-                                      const uint32_t (&ua)[WM], const uint32_t (&ub)[WN]) {
+                                      const v2u32 (&ua)[WM], const v2u32 (&ub)[WN]) {
     #pragma unroll
     for (int i = 0; i < WM; ++i) {
         const v8i av = (v8i){(int)a[i].x, (int)a[i].y, (int)a[i].z, (int)a[i].w, 0, 0, 0, 0};
+        const int sa = (int)(KS < 2 ? ua[i].x : ua[i].y);
         #pragma unroll
         for (int j = 0; j < WN; ++j) {
             const v8i bv = (v8i){(int)b[j].x, (int)b[j].y, (int)b[j].z, (int)b[j].w, 0, 0, 0, 0};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 4, 4, 2 * (KS & 1),
-                                                                      (int)ua[i], 2 * (KS & 1), (int)ub[j]);
+            const int sb = (int)(KS < 2 ? ub[j].x : ub[j].y);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 4, 4, 2 * (KS & 1), sa,
+                                                                      2 * (KS & 1), sb);
         }
     }
 }
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
 
     // operand sets for K slices 0..3 of a stage (read two slices ahead of their MFMAs)
     v4u32 a0[WM], b0[WN], a1[WM], b1[WN], a2[WM], b2[WN], a3[WM], b3[WN];
-    uint32_t sa0[WM], sb0[WN], sa1[WM], sb1[WN];   // scale words 0 and 1 of the stage
+    v2u32 sa[WM], sb[WN], na[WM], nb[WN];   // scale words of this stage and the next
     const uint8_t* sbase = smem + 2 * T::CODE_BYTES;
 
     issue_stage<WM, WN>(smem, bs, voff, soff, wave, 0, steps);
@@ -424,45 +426,47 @@ __global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
     // stage 0 is in once only stage 1's loads remain (loads complete in order)
     __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(T::BATCH));
     barrier_only();
-    read_scales<WM, WN, 0>(sbase, 0, scA, scB, kc, sa0, sb0);
+    read_scales<WM, WN>(sbase, 0, scA, scB, kc, sa, sb);
     read_ops<WM, WN, 0>(smem, 0, roff, rowA0, rowB0, a0, b0);
     read_ops<WM, WN, 1>(smem, 0, roff, rowA0, rowB0, a1, b1);
     for (int s = 0; s + 1 < steps; ++s) {
         read_ops<WM, WN, 2>(smem, s, roff, rowA0, rowB0, a2, b2);
-        read_scales<WM, WN, 1>(sbase, s, scA, scB, kc, sa1, sb1);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas<WM, WN, 0>(acc, a0, b0, sa0, sb0);
+        mfmas<WM, WN, 0>(acc, a0, b0, sa, sb);
         __builtin_amdgcn_sched_barrier(0);
         read_ops<WM, WN, 3>(smem, s, roff, rowA0, rowB0, a3, b3);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas<WM, WN, 1>(acc, a1, b1, sa0, sb0);
+        mfmas<WM, WN, 1>(acc, a1, b1, sa, sb);
         __builtin_amdgcn_sched_barrier(0);
         // this wave's reads of stage s and its loads of stage s + 1 are done; after
         // the barrier every wave's are, so stage s + 2 may load into stage s's buffers
         __builtin_amdgcn_s_waitcnt(FP4Q_LGKMCNT0);
         __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
         barrier_only();
-        read_scales<WM, WN, 0>(sbase, s + 1, scA, scB, kc, sa0, sb0);
+        read_scales<WM, WN>(sbase, s + 1, scA, scB, kc, na, nb);
         read_ops<WM, WN, 0>(smem, s + 1, roff, rowA0, rowB0, a0, b0);
         issue_stage<WM, WN, 1>(smem, bs, voff, soff, wave, s + 2, steps);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas<WM, WN, 2>(acc, a2, b2, sa1, sb1);
+        mfmas<WM, WN, 2>(acc, a2, b2, sa, sb);
         __builtin_amdgcn_sched_barrier(0);
         read_ops<WM, WN, 1>(smem, s + 1, roff, rowA0, rowB0, a1, b1);
         issue_stage<WM, WN, 2>(smem, bs, voff, soff, wave, s + 2, steps);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas<WM, WN, 3>(acc, a3, b3, sa1, sb1);
+        mfmas<WM, WN, 3>(acc, a3, b3, sa, sb);
         __builtin_amdgcn_sched_barrier(0);
+        #pragma unroll
+        for (int i = 0; i < WM; ++i) sa[i] = na[i];
+        #pragma unroll
+        for (int j = 0; j < WN; ++j) sb[j] = nb[j];
     }
     {
         const int s = steps - 1;
         read_ops<WM, WN, 2>(smem, s, roff, rowA0, rowB0, a2, b2);
         read_ops<WM, WN, 3>(smem, s, roff, rowA0, rowB0, a3, b3);
-        read_scales<WM, WN, 1>(sbase, s, scA, scB, kc, sa1, sb1);
-        mfmas<WM, WN, 0>(acc, a0, b0, sa0, sb0);
-        mfmas<WM, WN, 1>(acc, a1, b1, sa0, sb0);
-        mfmas<WM, WN, 2>(acc, a2, b2, sa1, sb1);
-        mfmas<WM, WN, 3>(acc, a3, b3, sa1, sb1);
+        mfmas<WM, WN, 0>(acc, a0, b0, sa, sb);
+        mfmas<WM, WN, 1>(acc, a1, b1, sa, sb);
+        mfmas<WM, WN, 2>(acc, a2, b2, sa, sb);
+        mfmas<WM, WN, 3>(acc, a3, b3, sa, sb);
     }
     // the loads issued past the last stage must land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
