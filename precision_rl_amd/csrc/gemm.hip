@@ -485,6 +485,42 @@ __global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
     uint8_t* cw = reinterpret_cast<uint8_t*>(p.c) + (row0 * p.ldc + col0) * ESZ;
     const int64_t crange = p.M > row0 ? (p.M - row0) * p.ldc * ESZ : 0;
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(cw, (short)0, clamp31(crange), 0x00020000);
+    if (p.staged && m0 + T::RA <= p.M && n0 + T::RB <= p.N) {
+        // whole tile inside C, rows 16-byte aligned: each wave turns its quarter around in LDS,
+        // half its rows at a time, and writes whole 16-byte pieces of rows
+        constexpr int HR = 16 * WM;              // rows per half
+        constexpr int PITCH = 32 * WN * ESZ;     // bytes per staged row
+        constexpr int PIECES = HR * PITCH / 16;  // 16-byte pieces per half
+        static_assert(PIECES % 64 == 0, "whole wave instructions per half");
+        uint8_t* st = smem + wave * HR * PITCH;
+        barrier_only();   // every wave is done with the K loop's LDS
+        #pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            #pragma unroll
+            for (int i = 0; i < WM / 2; ++i)
+                #pragma unroll
+                for (int j = 0; j < WN; ++j)
+                    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        uint8_t* d = st + (32 * i + 8 * (r >> 2) + 4 * kc + (r & 3)) * PITCH + (32 * j + r32) * ESZ;
+                        const float v = acc[h * (WM / 2) + i][j][r];
+                        if constexpr (BF16) {
+                            const bf16x2 b = __builtin_convertvector((v2f){v, 0.0f}, bf16x2);
+                            *reinterpret_cast<uint16_t*>(d) = (uint16_t)(__builtin_bit_cast(uint32_t, b) & 0xFFFFu);
+                        } else {
+                            *reinterpret_cast<float*>(d) = v;
+                        }
+                    }
+            #pragma unroll
+            for (int q = 0; q < PIECES / 64; ++q) {
+                const int c = q * 64 + lane, row = c / (PITCH / 16), piece = c % (PITCH / 16);
+                const v4u32 v = *reinterpret_cast<const v4u32*>(st + c * 16);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v), rc,
+                                                       (h * HR + row) * ldcb + piece * 16, 0, 0);
+            }
+        }
+        return;
+    }
     int vlane[WN];
     #pragma unroll
     for (int j = 0; j < WN; ++j)
@@ -505,6 +541,8 @@ static hipError_t launch_lds(bool bf16_out, GemmParams p, hipStream_t s) {
     p.tiles_n = (uint32_t)((p.N + T::RB - 1) / T::RB);
     const uint32_t g = tiles_m * p.tiles_n;
     p.xcd_remap = g % 8 == 0 ? 1u : 0u;
+    const int esz = bf16_out ? 2 : 4;
+    p.staged = ((uintptr_t)p.c & 15) == 0 && (p.ldc * esz) % 16 == 0 ? 1u : 0u;
     if (bf16_out) hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, true>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
     else hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, false>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
     return hipGetLastError();

@@ -114,6 +114,7 @@ struct GemmParams {
     int64_t M, N, K;
     uint32_t tiles_n;           // column tiles of C
     uint32_t xcd_remap;         // 1: hand out tiles XCD by XCD (grid size a multiple of 8)
+    uint32_t staged;            // 1: C and its rows 16-byte aligned (whole tiles stored through LDS)
 };
 
 // Launchers (return hipGetLastError() of the launch).
