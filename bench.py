@@ -27,8 +27,11 @@ step (per-launch events); its achieved rate uses the back-to-back duration,
 which compares directly with rocprofv3's kernel durations.  The other workloads (NVFP4 activation 4096x2048,
 KV cache at 131072 tokens, one deep guidance-cache layer, uniform grid + RHT16
 + SR on a 65536x8192 GEMM operand) are timed back to back and reported under
-"workloads".  The CPU baseline is the oracle timed on a bounded row sample of
-the headline step.
+"workloads", and so is the MXFP4 matrix product of one deep layer's
+activations [8192, 4096] with one expert weight [1536 out, 4096 in], both
+quantized by the library, reported as TFLOP/s against the dense FP4 matrix
+peak.  The CPU baseline is the oracle timed on a bounded row sample of the
+headline step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--streams 1|2]
 """
@@ -47,6 +50,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak (no sparsity), TFLOP/s
 
 
 def log(*a):
@@ -60,6 +64,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2))
     ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="only the MXFP4 matrix product workload (one JSON line of its figures)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the CPU-baseline sample")
     ap.add_argument("--config-iters", type=int, default=20)
@@ -404,6 +410,33 @@ def other_workloads(args, fq, torch, W, ceiling):
     return res
 
 
+def gemm_workload(args, fq, torch, W):
+    """MXFP4 product C = A * B^T: A the activations [8192, 4096] N(0, 1), B one expert weight
+    [1536 out, 4096 in] N(0, 0.02^2) (the guidance-cache layer's tensors, weight stored out x in so
+    that both operands are blocked along K), both quantized by fp4_quantize (MXFP4, RTN)."""
+    M, N, K = W.GEMM_SHAPE
+    log(f"MXFP4 GEMM {M}x{N}x{K} ...")
+    xa = to_dev(W.f32_to_bf16_rne(W.normal_outliers_f32(M, K, 1020, 16, 0.0, 1.0)))
+    xb = to_dev(W.f32_to_bf16_rne(W.normal_outliers_f32(N, K, 1020, 0, 0.0, 1.0, sigma=0.02)))
+    cfg = fq.Fp4Config(format=fq.MXFP4)
+    a, asc = fq.fp4_quantize(xa, cfg)
+    b, bsc = fq.fp4_quantize(xb, cfg)
+    del xa, xb
+    flops = 2.0 * M * N * K
+    reps = max(20, args.config_iters)
+    res = {"M": M, "N": N, "K": K, "flops": flops}
+    for name, dt in (("bf16_out", torch.bfloat16), ("f32_out", torch.float32)):
+        out = torch.empty((M, N), dtype=dt, device="cuda")
+        ms = back_to_back(torch, lambda i: fq.fp4_gemm_mxfp4(a, asc, b, bsc, M, N, K, out=out), reps, warm=5)
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4)}
+    r = res["bf16_out"]
+    res["roofline"] = {"bound": "mfma", "kernel": "k_gemm_mx_lds", "achieved": r["TFLOPs"], "peak": PEAK_FP4_TFLOPS,
+                       "unit": "TFLOP/s", "frac": r["frac_fp4_peak"], "traffic": None,
+                       "algorithmic_flops_per_launch": flops, "avg_launch_us": r["us"]}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -417,6 +450,14 @@ def main():
     from precision_rl_amd import fp4q as fq, workloads as W
     fq.lib()
     torch.cuda.set_device(0)
+    if args.gemm_only:
+        g = gemm_workload(args, fq, torch, W)
+        print(json.dumps({"metric": "MXFP4 GEMM TFLOP/s", "value": g["bf16_out"]["TFLOPs"], "unit": "TFLOP/s",
+                          "n_gpus": 1, "higher_is_better": True, "dtype": "fp4 x fp4 -> f32 (bf16 out)",
+                          "data": "synthetic", "config": {"workload": "MXFP4 GEMM activations [8192, 4096] x "
+                                                                     "expert weight [1536, 4096]^T"},
+                          "roofline": g["roofline"], "gemm": g}), flush=True)
+        return
 
     ceiling = copy_ceiling(torch, fq)
     h = headline(args, fq, torch, W, ceiling["GBps"])
@@ -429,6 +470,8 @@ def main():
         log("CPU baseline (oracle) ...")
         cpu = cpu_baseline(args, W, oracle_mod, h)
     workloads = {} if args.quick else other_workloads(args, fq, torch, W, ceiling["GBps"])
+    if not args.quick:
+        workloads["mxfp4_gemm_8192x1536x4096"] = gemm_workload(args, fq, torch, W)
 
     n = h["n"]
     value = h["step_bytes"] / (h["ms_step"] * 1e-3) / 1e9
