@@ -219,13 +219,34 @@ fp4_status fp4_guide_mismatch(const fp4_cfg* cfg, const void* x_bf16, int64_t ro
  * finite results.  A 0xFF (NaN) scale makes the results of its row of A or
  * B NaN.  Output dense enough for row stride ldc >= N elements: fp32, or
  * bf16 by round-to-nearest-even of the fp32 result.
- *   K % 32 == 0 (K == 0 writes zeros); M == 0 or N == 0 is a no-op.
+ *   K % 32 == 0 (K == 0 writes zeros); M == 0 or N == 0 is a no-op;
+ *   ldc <= 2^21.
  *   Alignment: codes 16 bytes, scales 1 byte, c 4 (fp32) or 2 (bf16) bytes.
  *   The grid of the codes is E2M1 only: the uniform grid and NVFP4 blocks
  *   are not accepted by this product (the caller keeps them apart). */
 fp4_status fp4_gemm_mxfp4(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
                           int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, fp4_dtype dtype,
                           hipStream_t stream);
+
+/* One product of a grouped call (fields as in fp4_gemm_mxfp4). */
+typedef struct {
+    const void* a_codes;
+    const void* a_scales;
+    const void* b_codes;
+    const void* b_scales;
+    int64_t M, N, K;
+    void* c;
+    int64_t ldc;
+} fp4_gemm_desc;
+
+/* Up to 16 MXFP4 products in one launch, e.g. the routed experts of an MoE
+ * layer, each with its own token rows and weight [TETRAJET section 4: every
+ * linear layer's products take MXFP4 operands; TRACE-JA: MoE models].  Same
+ * result as fp4_gemm_mxfp4 on each product in turn; products with M or N of 0
+ * are skipped.  Every product is checked before anything is launched (the
+ * message names the product).  All products run in one launch when every K is
+ * a multiple of 512 with 16-byte aligned scales; otherwise one launch each. */
+fp4_status fp4_gemm_mxfp4_grouped(int n, const fp4_gemm_desc* products, fp4_dtype dtype, hipStream_t stream);
 
 /* Standalone 16-point random Hadamard transform [UFP4 RHT section] of each
  * 16-group of a bf16 matrix: forward y = 1/4 H16 D x, inverse x = D 1/4 H16 y,

@@ -356,19 +356,28 @@ fp4_status guide_unpack(const fp4_cfg* cfg, const void* guide_bits, const void* 
     return hip_status(fp4q::launch_guide_unpack(cfg->format, p, stream), "guide_unpack launch");
 }
 
-fp4_status fp4_gemm_mxfp4(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
-                          int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, fp4_dtype dtype,
-                          hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks one product's arguments and fills its parameter block; *empty is set
+// when M or N is 0 (nothing to do).
+fp4_status gemm_params(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
+                       int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, fp4_dtype dtype, fp4q::GemmParams* p,
+                       bool* empty) {
     if (dtype != FP4_OUT_F32 && dtype != FP4_OUT_BF16) return fail(FP4_ERR_ARG, "unknown dtype %d", (int)dtype);
     if (M < 0 || N < 0 || K < 0)
         return fail(FP4_ERR_ARG, "negative shape M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
     if (K % 32 != 0) return fail(FP4_ERR_SHAPE, "K=%lld is not a multiple of 32", (long long)K);
-    if (M == 0 || N == 0) return ok();
+    *empty = M == 0 || N == 0;
+    if (*empty) return FP4_OK;
     if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 40))
         return fail(FP4_ERR_SHAPE, "shape too large M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
     if ((uint64_t)((M + 127) / 128) * (uint64_t)((N + 127) / 128) >= (1ull << 31))
         return fail(FP4_ERR_SHAPE, "too many 128 x 128 tiles of C");
     if (ldc < N) return fail(FP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    // the stores address a 256-row band of C with 32-bit offsets
+    if (ldc > (1ll << 21)) return fail(FP4_ERR_SHAPE, "ldc=%lld too large", (long long)ldc);
     FP4Q_TRY(need(c, dtype == FP4_OUT_BF16 ? 2 : 4, "c"));
     if (K > 0) {
         FP4Q_TRY(need(a_codes, 16, "a_codes"));
@@ -376,18 +385,53 @@ fp4_status fp4_gemm_mxfp4(const void* a_codes, const void* a_scales, const void*
         FP4Q_TRY(need(b_codes, 16, "b_codes"));
         FP4Q_TRY(need(b_scales, 1, "b_scales"));
     }
+    *p = fp4q::GemmParams{};
+    p->a = static_cast<const uint8_t*>(a_codes);
+    p->as = static_cast<const uint8_t*>(a_scales);
+    p->b = static_cast<const uint8_t*>(b_codes);
+    p->bs = static_cast<const uint8_t*>(b_scales);
+    p->c = c;
+    p->ldc = ldc;
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->tiles_n = (uint32_t)((N + 127) / 128);
+    return FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4_status fp4_gemm_mxfp4(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
+                          int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, fp4_dtype dtype,
+                          hipStream_t stream) {
     fp4q::GemmParams p{};
-    p.a = static_cast<const uint8_t*>(a_codes);
-    p.as = static_cast<const uint8_t*>(a_scales);
-    p.b = static_cast<const uint8_t*>(b_codes);
-    p.bs = static_cast<const uint8_t*>(b_scales);
-    p.c = c;
-    p.ldc = ldc;
-    p.M = M;
-    p.N = N;
-    p.K = K;
-    p.tiles_n = (uint32_t)((N + 127) / 128);
+    bool empty = false;
+    FP4Q_TRY(gemm_params(a_codes, a_scales, b_codes, b_scales, M, N, K, c, ldc, dtype, &p, &empty));
+    if (empty) return ok();
     return hip_status(fp4q::launch_gemm_mx(dtype == FP4_OUT_BF16, p, stream), "gemm launch");
+}
+
+fp4_status fp4_gemm_mxfp4_grouped(int n, const fp4_gemm_desc* products, fp4_dtype dtype, hipStream_t stream) {
+    if (n < 1 || n > fp4q::kMaxGemmGroup) return fail(FP4_ERR_ARG, "n=%d outside 1..%d", n, fp4q::kMaxGemmGroup);
+    if (!products) return fail(FP4_ERR_ARG, "products is NULL");
+    fp4q::GroupedGemmParams gp{};
+    for (int i = 0; i < n; ++i) {
+        const fp4_gemm_desc& d = products[i];
+        fp4q::GemmParams p{};
+        bool empty = false;
+        const fp4_status st = gemm_params(d.a_codes, d.a_scales, d.b_codes, d.b_scales, d.M, d.N, d.K, d.c, d.ldc,
+                                          dtype, &p, &empty);
+        if (st != FP4_OK) {
+            char msg[512];
+            snprintf(msg, sizeof msg, "%s", g_err);
+            return fail(st, "product %d: %s", i, msg);
+        }
+        if (!empty) gp.g[gp.n++] = p;
+    }
+    if (gp.n == 0) return ok();
+    return hip_status(fp4q::launch_gemm_mx_grouped(dtype == FP4_OUT_BF16, gp, stream), "grouped gemm launch");
 }
 
 fp4_status fp4_rht16(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,

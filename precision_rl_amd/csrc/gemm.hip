@@ -348,20 +348,14 @@ __device__ __forceinline__ void store_c(__amdgpu_buffer_rsrc_t rc, int voff, flo
     }
 }
 
+// Tile (tm, tn) of the product p, computed by the calling workgroup.
 template <int WM, int WN, bool BF16>
-__global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint32_t tn, uint8_t* smem) {
     using T = LdsTile<WM, WN>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, kc = lane >> 5;
-
-    // tile of this workgroup; consecutive workgroups go to different XCDs, so
-    // tiles are handed out XCD by XCD when the grid divides evenly
-    uint32_t bid = blockIdx.x;
-    if (p.xcd_remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
-    const uint32_t tm = bid / p.tiles_n, tn = bid - tm * p.tiles_n;
     const int64_t m0 = (int64_t)tm * T::RA, n0 = (int64_t)tn * T::RB;
     const int64_t rowb = p.K / 2, srow = p.K / 32;
 
@@ -534,6 +528,37 @@ __global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
                 store_c<BF16>(rc, vlane[j] + (32 * i + 8 * (r >> 2) + (r & 3)) * ldcb, acc[i][j][r]);
 }
 
+// Consecutive workgroups go to different XCDs, so when the grid divides
+// evenly, tiles are handed out XCD by XCD: the workgroups of one XCD then
+// share operand rows in its L2.
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t remap) {
+    uint32_t bid = blockIdx.x;
+    if (remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+    return bid;
+}
+
+template <int WM, int WN, bool BF16>
+__global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const uint32_t bid = xcd_tile(p.xcd_remap);
+    const uint32_t tm = bid / p.tiles_n, tn = bid - tm * p.tiles_n;
+    gemm_tile<WM, WN, BF16>(p, tm, tn, smem);
+}
+
+// Several products in one launch: the tiles of product i are workgroups
+// tile_start[i] .. tile_start[i + 1] - 1.
+template <int WM, int WN, bool BF16>
+__global__ __launch_bounds__(256) void k_gemm_mx_lds_grouped(const GroupedGemmParams gp) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const uint32_t bid = xcd_tile(gp.xcd_remap);
+    uint32_t i = 0;
+    while (i + 1 < gp.n && bid >= gp.tile_start[i + 1]) ++i;
+    const GemmParams& p = gp.g[i];
+    const uint32_t local = bid - gp.tile_start[i];
+    const uint32_t tm = local / p.tiles_n, tn = local - tm * p.tiles_n;
+    gemm_tile<WM, WN, BF16>(p, tm, tn, smem);
+}
+
 template <int WM, int WN>
 static hipError_t launch_lds(bool bf16_out, GemmParams p, hipStream_t s) {
     using T = LdsTile<WM, WN>;
@@ -548,11 +573,55 @@ static hipError_t launch_lds(bool bf16_out, GemmParams p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int WM, int WN>
+static hipError_t launch_lds_grouped(bool bf16_out, GroupedGemmParams gp, hipStream_t s) {
+    using T = LdsTile<WM, WN>;
+    const int esz = bf16_out ? 2 : 4;
+    gp.tile_start[0] = 0;
+    for (uint32_t i = 0; i < gp.n; ++i) {
+        GemmParams& p = gp.g[i];
+        const uint32_t tiles_m = (uint32_t)((p.M + T::RA - 1) / T::RA);
+        p.tiles_n = (uint32_t)((p.N + T::RB - 1) / T::RB);
+        p.xcd_remap = 0;
+        p.staged = ((uintptr_t)p.c & 15) == 0 && (p.ldc * esz) % 16 == 0 ? 1u : 0u;
+        gp.tile_start[i + 1] = gp.tile_start[i] + tiles_m * p.tiles_n;
+    }
+    const uint32_t g = gp.tile_start[gp.n];
+    if (g == 0) return hipSuccess;
+    gp.xcd_remap = g % 8 == 0 ? 1u : 0u;
+    if (bf16_out)
+        hipLaunchKernelGGL((k_gemm_mx_lds_grouped<WM, WN, true>), dim3(g), dim3(256), T::LDS_BYTES, s, gp);
+    else
+        hipLaunchKernelGGL((k_gemm_mx_lds_grouped<WM, WN, false>), dim3(g), dim3(256), T::LDS_BYTES, s, gp);
+    return hipGetLastError();
+}
+
+static bool main_path_ok(const GemmParams& p) {
+    return p.K % 512 == 0 && p.K > 0 && p.K < (1ll << 24) && ((uintptr_t)p.as & 15) == 0 &&
+           ((uintptr_t)p.bs & 15) == 0;
+}
+
+hipError_t launch_gemm_mx_grouped(bool bf16_out, const GroupedGemmParams& gp, hipStream_t s) {
+    bool all_main = true;
+    int64_t big = 0;
+    for (uint32_t i = 0; i < gp.n; ++i) {
+        all_main = all_main && main_path_ok(gp.g[i]);
+        big += ((gp.g[i].M + 255) / 256) * ((gp.g[i].N + 191) / 192);
+    }
+    if (!all_main) {   // one launch per product
+        for (uint32_t i = 0; i < gp.n; ++i) {
+            const hipError_t e = launch_gemm_mx(bf16_out, gp.g[i], s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    if (big >= 256) return launch_lds_grouped<4, 3>(bf16_out, gp, s);
+    return launch_lds_grouped<2, 2>(bf16_out, gp, s);
+}
+
 hipError_t launch_gemm_mx(bool bf16_out, const GemmParams& p, hipStream_t s) {
     // main path: K a multiple of 512 (whole stages and 16-byte aligned scale loads)
-    const bool main_path = p.K % 512 == 0 && p.K > 0 && p.K < (1ll << 24) && ((uintptr_t)p.as & 15) == 0 &&
-                           ((uintptr_t)p.bs & 15) == 0;
-    if (main_path) {
+    if (main_path_ok(p)) {
         if (gemm_config(p.M, p.N) == 1) return launch_lds<4, 3>(bf16_out, p, s);
         return launch_lds<2, 2>(bf16_out, p, s);
     }

@@ -141,4 +141,15 @@ hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n16, hipStrea
 hipError_t launch_encode_values(int grid, int mode, const EncodeParams& p, hipStream_t s);
 hipError_t launch_gemm_mx(bool bf16_out, const GemmParams& p, hipStream_t s);
 
+// Up to kMaxGemmGroup products in one launch (one launch per product when
+// some product's K is not a multiple of 512).
+constexpr int kMaxGemmGroup = 16;
+struct GroupedGemmParams {
+    GemmParams g[kMaxGemmGroup];
+    uint32_t tile_start[kMaxGemmGroup + 1];   // prefix sums of per-product tile counts
+    uint32_t n;
+    uint32_t xcd_remap;
+};
+hipError_t launch_gemm_mx_grouped(bool bf16_out, const GroupedGemmParams& gp, hipStream_t s);
+
 }  // namespace fp4q

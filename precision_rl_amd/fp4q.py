@@ -71,9 +71,15 @@ MAX_GROUP = 16
 _lib = None
 EXPORTS = ("fp4_tensor_scale", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
            "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_unpack",
-           "fp4_gemm_mxfp4", "fp4_rht16",
+           "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_rht16",
            "fp4_encode_values", "fp4_stream_copy", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
            "fp4_status_str", "fp4_last_error")
+
+
+class _CGemm(C.Structure):
+    _fields_ = [("a_codes", C.c_void_p), ("a_scales", C.c_void_p), ("b_codes", C.c_void_p),
+                ("b_scales", C.c_void_p), ("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64),
+                ("c", C.c_void_p), ("ldc", C.c_int64)]
 
 
 def lib():
@@ -98,6 +104,7 @@ def lib():
         "guide_pack": [CP, P, P, I64, I64, P, P, P],
         "guide_unpack": [CP, P, P, I64, I64, P, P, P],
         "fp4_gemm_mxfp4": [P, P, P, P, I64, I64, I64, P, I64, I, P],
+        "fp4_gemm_mxfp4_grouped": [I, C.POINTER(_CGemm), I, P],
         "fp4_rht16": [P, I64, I64, I64, C.c_uint64, I, P, I, P],
         "fp4_encode_values": [I, I, P, P, I64, P, P],
         "fp4_stream_copy": [P, P, C.c_size_t, P],
@@ -299,6 +306,27 @@ def fp4_gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch
     _check(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
                                 _ptr(out), ldc, kind, _stream(a_codes)), "fp4_gemm_mxfp4")
     return out
+
+
+def fp4_gemm_mxfp4_grouped(products, dtype=torch.bfloat16, outs=None):
+    """Several MXFP4 products in one call: products is a list of (a_codes, a_scales, b_codes, b_scales, M, N, K).
+    Returns the list of C tensors (outs, or new [M, N] tensors of dtype)."""
+    if not products:
+        raise ValueError("no products")
+    arr = (_CGemm * len(products))()
+    res = []
+    for i, (ac, asc, bc, bsc, M, N, K) in enumerate(products):
+        _on_gpu(ac, asc, bc, bsc)
+        out = outs[i] if outs is not None else torch.empty((M, N), dtype=dtype, device=ac.device)
+        _on_gpu(out)
+        ldc = out.stride(0) if M > 1 else N
+        arr[i] = _CGemm(_ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), M, N, K, _ptr(out), ldc)
+        res.append(out)
+    if len({o.dtype for o in res}) != 1 or res[0].dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("grouped gemm outputs must all be bfloat16 or all float32")
+    kind = OUT_BF16 if res[0].dtype == torch.bfloat16 else OUT_F32
+    _check(lib().fp4_gemm_mxfp4_grouped(len(products), arr, kind, _stream(products[0][0])), "fp4_gemm_mxfp4_grouped")
+    return res
 
 
 def guide_pack(codes: torch.Tensor, scales: torch.Tensor, cfg: Fp4Config, rows: int, cols: int,

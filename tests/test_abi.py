@@ -30,7 +30,7 @@ def fq():
 def test_header_declares_the_expected_calls():
     names = _declared()
     for n in ["fp4_quantize", "fp4_quantize_guided", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_guide_mismatch",
-              "fp4_gemm_mxfp4", "fp4_rht16", "fp4_tensor_scale", "fp4_encode_values", "fp4_codes_bytes",
+              "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_rht16", "fp4_tensor_scale", "fp4_encode_values", "fp4_codes_bytes",
               "fp4_scales_bytes", "fp4_guide_bytes", "fp4_status_str", "fp4_last_error"]:
         assert n in names, n
 
@@ -114,6 +114,26 @@ def test_gemm_host_side_errors(fq):
     # M == 0 or N == 0 is a no-op that touches nothing
     assert g(None, None, None, None, 0, 4, 64, None, 4, 0, None) == 0
     assert g(None, None, None, None, 4, 0, 64, None, 0, 1, None) == 0
+
+
+def test_grouped_gemm_host_side_errors(fq):
+    L = fq.lib()
+    A = 1 << 20
+    arr = (fq._CGemm * 17)()
+    for i in range(17):
+        arr[i] = fq._CGemm(A, A, A, A, 4, 4, 64, A, 4)
+    g = L.fp4_gemm_mxfp4_grouped
+    assert g(0, arr, 0, None) == 1
+    assert g(17, arr, 0, None) == 1
+    assert g(2, None, 0, None) == 1
+    arr[1] = fq._CGemm(A, A, A, A, 4, 4, 48, A, 4)            # K % 32
+    assert g(2, arr, 0, None) == 2
+    assert "product 1" in L.fp4_last_error().decode()
+    arr[1] = fq._CGemm(A, A, A, A, 4, 8, 64, A, 4)            # ldc < N
+    assert g(2, arr, 0, None) == 2
+    arr[0] = fq._CGemm(None, None, None, None, 0, 4, 64, None, 4)
+    arr[1] = fq._CGemm(None, None, None, None, 4, 0, 64, None, 0)
+    assert g(2, arr, 0, None) == 0                            # every product empty: nothing launched
 
 
 def test_binding_refuses_cpu_tensors(fq):

@@ -203,3 +203,46 @@ def test_full_size_expert_gemm_sampled(fq):
         bf = dtype == torch.bfloat16
         check(got[rows], e_rows, m_rows, K, bf, f"full size rows {dtype}")
         check(got[:, cols], e_cols, m_cols, K, bf, f"full size cols {dtype}")
+
+
+@pytest.mark.parametrize("K", [512, 160])
+def test_grouped_experts_vs_oracle(fq, K):
+    # eight experts with their own token counts (one empty) and weights: K = 512 runs as one launch,
+    # K = 160 as one launch per product
+    Ms = [300, 0, 129, 700, 64, 1, 256, 413]
+    N = 192
+    say(f"gemm grouped K={K} Ms={Ms}")
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).ravel()).cuda()
+    prods, refs = [], []
+    for e, M in enumerate(Ms):
+        a, asc = W.mx_operand(M, K, seed=70 + e, stream=0)
+        b, bsc = W.mx_operand(N, K, seed=90 + e, stream=0)
+        prods.append((dev(a), dev(asc), dev(b), dev(bsc), M, N, K))
+        refs.append(O.gemm_mx(a, asc, b, bsc, M, N, K) if M else None)
+    for dtype in (torch.float32, torch.bfloat16):
+        outs = fq.fp4_gemm_mxfp4_grouped(prods, dtype=dtype)
+        torch.cuda.synchronize()
+        for e, (M, out, ref) in enumerate(zip(Ms, outs, refs)):
+            if M:
+                check(out.float().cpu().numpy().astype(np.float64), ref[0], ref[1], K, dtype == torch.bfloat16,
+                      f"grouped expert {e} {dtype}")
+
+
+def test_grouped_large_tiles_sampled(fq):
+    # 8 experts x 1024 tokens x [1536, 512] weights: 256 tiles of 256 x 192 in one launch
+    E, M, N, K = 8, 1024, 1536, 512
+    say(f"gemm grouped large E={E} M={M} N={N} K={K}")
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).ravel()).cuda()
+    rng = np.random.default_rng(12)
+    prods, host = [], []
+    for e in range(E):
+        a, asc = W.mx_operand(M, K, seed=110 + e, stream=0)
+        b, bsc = W.mx_operand(N, K, seed=130 + e, stream=0)
+        prods.append((dev(a), dev(asc), dev(b), dev(bsc), M, N, K))
+        host.append((a, asc, b, bsc))
+    outs = fq.fp4_gemm_mxfp4_grouped(prods, dtype=torch.float32)
+    torch.cuda.synchronize()
+    for e, (a, asc, b, bsc) in enumerate(host):
+        rows = np.sort(rng.choice(M, 16, replace=False))
+        ref, mag = O.gemm_mx(a[rows], asc[rows], b, bsc, len(rows), N, K)
+        check(outs[e].cpu().numpy()[rows].astype(np.float64), ref, mag, K, False, f"grouped large expert {e}")

@@ -125,8 +125,8 @@ MUTANTS = {
     "gemm_scale_per_16": ("gemm", [("orc_e8m0_decode(scales[i / 32])", "orc_e8m0_decode(scales[i / 16])")]),
     "gemm_nan_scale_ignored": ("gemm", [("orc_e8m0_decode(scales[i / 32])", "ldexp(1.0, (int)scales[i / 32] - 127)")]),
     "gemm_uniform_grid": ("gemm", [("orc_grid(ORC_E2M1, (int)(code & 7))", "orc_grid(ORC_UNIFORM, (int)(code & 7))")]),
-    "gemm_a_transposed": ("gemm", [("mx_value(a_codes, a_scales, m * K + k)", "mx_value(a_codes, a_scales, k * M + m)")]),
-    "gemm_b_reversed": ("gemm", [("mx_value(b_codes, b_scales, n * K + k)", "mx_value(b_codes, b_scales, n * K + (K - 1 - k))")]),
+    "gemm_a_transposed": ("gemm", [("av[m * K + k] * bv", "av[k * M + m] * bv")]),
+    "gemm_b_reversed": ("gemm", [("bv[n * K + k];", "bv[n * K + (K - 1 - k)];")]),
     "gemm_drops_last_block": ("gemm", [("for (int64_t k = 0; k < K; ++k) {\n                const double prod",
                                         "for (int64_t k = 0; k < K - 32; ++k) {\n                const double prod")]),
     "gemm_absdot_signed": ("gemm", [("mag += fabs(prod);", "mag += prod;")]),
