@@ -279,5 +279,5 @@ def gemm_mx(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray, b_sc
     c = np.empty((M, N), dtype=np.float64)
     mag = np.empty((M, N), dtype=np.float64)
     if lib().orc_gemm_mx(_p(ac), _p(asc), _p(bc), _p(bsc), M, N, K, _p(c), _p(mag)):
-        raise ValueError("oracle gemm: K must be a multiple of 32")
+        raise ValueError("oracle gemm: K must be a multiple of 32 (or out of memory)")
     return c, mag

@@ -586,18 +586,27 @@ static double mx_value(const uint8_t* codes, const uint8_t* scales, int64_t i) {
  * MXFP4 codes and scales are a_codes / a_scales (the layouts the quantizer
  * writes for a row-major [M, K] input) and b likewise the [N, K] tensor of
  * b_codes / b_scales: the product A * B^T with the reduction along the
- * blocked dimension.  Every product is exact in double and the sum runs in k
- * order in double.  absdot (may be NULL) receives sum over k of |a(m,k) b(n,k)|,
- * the scale of the rounding error any fp32 summation may make.
- * Returns 0, or 1 when K is not a multiple of 32. */
+ * blocked dimension.  Both operands are first decoded to double (exact), then
+ * every product is exact in double and the sum runs in k order in double.
+ * absdot (may be NULL) receives sum over k of |a(m,k) b(n,k)|, the scale of
+ * the rounding error any fp32 summation may make.
+ * Returns 0, 1 when K is not a multiple of 32, 2 when out of memory. */
 int orc_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                 const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, double* c, double* absdot) {
     if (K % 32 != 0) return 1;
+    double* av = (double*)malloc((size_t)(M * K + 1) * sizeof(double));
+    double* bv = (double*)malloc((size_t)(N * K + 1) * sizeof(double));
+    if (!av || !bv) {
+        free(av); free(bv);
+        return 2;
+    }
+    for (int64_t i = 0; i < M * K; ++i) av[i] = mx_value(a_codes, a_scales, i);
+    for (int64_t i = 0; i < N * K; ++i) bv[i] = mx_value(b_codes, b_scales, i);
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0, mag = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                const double prod = mx_value(a_codes, a_scales, m * K + k) * mx_value(b_codes, b_scales, n * K + k);
+                const double prod = av[m * K + k] * bv[n * K + k];
                 acc += prod;
                 mag += fabs(prod);
             }
@@ -605,6 +614,7 @@ int orc_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* 
             if (absdot) absdot[m * N + n] = mag;
         }
     }
+    free(av); free(bv);
     return 0;
 }
 
