@@ -181,6 +181,22 @@ fp4_status fp4_dequantize(const fp4_cfg* cfg, const void* codes, const void* sca
 fp4_status guide_pack(const fp4_cfg* cfg, const void* codes, const void* scales, int64_t rows,
                       int64_t cols, void* guide_bits, void* guide_scales, hipStream_t stream);
 
+/* One tensor of a grouped guide_pack (fields as in guide_pack). */
+typedef struct {
+    const void* codes;
+    const void* scales;
+    int64_t rows, cols;
+    void* guide_bits;
+    void* guide_scales;
+} fp4_guide_desc;
+
+/* guide_pack of up to 16 tensors sharing one configuration in one launch, e.g.
+ * the routed experts and activations of one deep layer [TRACE-JA
+ * "量子化情報キャッシュ": the guide is kept per deep layer].  Same result as
+ * guide_pack on each tensor; empty tensors are skipped; every tensor is
+ * checked before anything is launched (the message names the tensor). */
+fp4_status guide_pack_grouped(const fp4_cfg* cfg, int n, const fp4_guide_desc* tensors, hipStream_t stream);
+
 /* Inverse view of the guide: mant_u8[i] = guide bit i (0 or 1), scales_out =
  * guide_scales. */
 fp4_status guide_unpack(const fp4_cfg* cfg, const void* guide_bits, const void* guide_scales,

@@ -345,6 +345,29 @@ fp4_status guide_pack(const fp4_cfg* cfg, const void* codes, const void* scales,
     return hip_status(fp4q::launch_guide_pack(cfg->format, p, stream), "guide_pack launch");
 }
 
+fp4_status guide_pack_grouped(const fp4_cfg* cfg, int n, const fp4_guide_desc* tensors, hipStream_t stream) {
+    FP4Q_TRY(check_cfg(cfg));
+    if (n < 1 || n > fp4q::kMaxGroup) return fail(FP4_ERR_ARG, "n=%d outside 1..%d", n, fp4q::kMaxGroup);
+    if (!tensors) return fail(FP4_ERR_ARG, "tensors is NULL");
+    fp4q::GroupedGuideParams gp{};
+    for (int t = 0; t < n; ++t) {
+        const fp4_guide_desc& d = tensors[t];
+        uint64_t ng = 0;
+        const fp4_status st = guide_common(cfg, d.rows, d.cols, d.codes, d.scales, d.guide_bits, d.guide_scales, &ng);
+        if (st != FP4_OK) {
+            char msg[512];
+            snprintf(msg, sizeof msg, "%s", g_err);
+            return fail(st, "tensor %d: %s", t, msg);
+        }
+        if (ng == 0) continue;
+        gp.t[gp.n++] = fp4q::GuideParams{static_cast<const uint8_t*>(d.codes), static_cast<const uint8_t*>(d.scales),
+                                         static_cast<uint8_t*>(d.guide_bits), static_cast<uint8_t*>(d.guide_scales),
+                                         (uint32_t)ng};
+    }
+    if (gp.n == 0) return ok();
+    return hip_status(fp4q::launch_guide_pack_grouped(cfg->format, gp, stream), "grouped guide_pack launch");
+}
+
 fp4_status guide_unpack(const fp4_cfg* cfg, const void* guide_bits, const void* guide_scales,
                         int64_t rows, int64_t cols, void* mant_u8, void* scales_out,
                         hipStream_t stream) {

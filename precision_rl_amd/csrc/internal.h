@@ -136,6 +136,12 @@ hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantP
                              hipStream_t s);
 hipError_t launch_guide_pack(int format, const GuideParams& p, hipStream_t s);
 hipError_t launch_guide_unpack(int format, const GuideParams& p, hipStream_t s);
+struct GroupedGuideParams {
+    GuideParams t[kMaxGroup];
+    uint32_t wg_start[kMaxGroup + 1];   // prefix sums of per-tensor workgroup counts
+    uint32_t n;
+};
+hipError_t launch_guide_pack_grouped(int format, GroupedGuideParams gp, hipStream_t s);
 hipError_t launch_rht16(bool inverse, bool bf16_out, bool contig, const RhtParams& p, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n16, hipStream_t s);
 hipError_t launch_encode_values(int grid, int mode, const EncodeParams& p, hipStream_t s);

@@ -147,12 +147,13 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) 
 #endif
 constexpr int kGuideSlots = FP4Q_GUIDE_SLOTS;
 
+// Workgroup wg of guide_pack over one tensor.
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void k_guide_pack(const GuideParams p) {
+__device__ __forceinline__ void guide_pack_wg(const GuideParams& p, uint32_t wg) {
     // an odd NVFP4 group count leaves a last unit of one group (8 bytes of codes)
     const uint32_t nunits = (p.ngroups + 1u) >> 1;
     const uint32_t half_unit = (p.ngroups & 1u) ? nunits - 1u : 0xFFFFFFFFu;
-    const uint32_t u0 = blockIdx.x * (kThreads * kGuideSlots) + (threadIdx.x >> 6) * (64u * kGuideSlots) +
+    const uint32_t u0 = wg * (kThreads * kGuideSlots) + (threadIdx.x >> 6) * (64u * kGuideSlots) +
                         (threadIdx.x & 63u);
     v4u32 c[kGuideSlots];
     uint32_t sc[kGuideSlots];
@@ -193,6 +194,20 @@ __global__ __launch_bounds__(kThreads) void k_guide_pack(const GuideParams p) {
             st_out(p.scales_out + 2 * u, (uint8_t)sc[s]);
         }
     }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_guide_pack(const GuideParams p) {
+    guide_pack_wg<FMT>(p, blockIdx.x);
+}
+
+// Up to kMaxGroup tensors in one launch: tensor t takes workgroups
+// wg_start[t] .. wg_start[t + 1] - 1.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_guide_pack_grouped(const GroupedGuideParams gp) {
+    uint32_t t = 0;
+    while (t + 1 < gp.n && blockIdx.x >= gp.wg_start[t + 1]) ++t;
+    guide_pack_wg<FMT>(gp.t[t], blockIdx.x - gp.wg_start[t]);
 }
 
 __device__ __forceinline__ uint32_t bits4_to_bytes(uint32_t b) {
@@ -335,6 +350,21 @@ hipError_t launch_guide_pack(int format, const GuideParams& p, hipStream_t s) {
     const dim3 b((units + kThreads * kGuideSlots - 1) / (kThreads * kGuideSlots)), t(kThreads);
     if (format == 0) hipLaunchKernelGGL(k_guide_pack<0>, b, t, 0, s, p);
     else hipLaunchKernelGGL(k_guide_pack<1>, b, t, 0, s, p);
+    return hipGetLastError();
+}
+
+static uint32_t guide_pack_wgs(uint32_t ngroups) {
+    const uint32_t units = (ngroups + 1u) >> 1;
+    return (units + kThreads * kGuideSlots - 1) / (kThreads * kGuideSlots);
+}
+
+hipError_t launch_guide_pack_grouped(int format, GroupedGuideParams gp, hipStream_t s) {
+    gp.wg_start[0] = 0;
+    for (uint32_t t = 0; t < gp.n; ++t) gp.wg_start[t + 1] = gp.wg_start[t] + guide_pack_wgs(gp.t[t].ngroups);
+    const dim3 b(gp.wg_start[gp.n]), th(kThreads);
+    if (b.x == 0) return hipSuccess;
+    if (format == 0) hipLaunchKernelGGL(k_guide_pack_grouped<0>, b, th, 0, s, gp);
+    else hipLaunchKernelGGL(k_guide_pack_grouped<1>, b, th, 0, s, gp);
     return hipGetLastError();
 }
 

@@ -70,10 +70,16 @@ MAX_GROUP = 16
 
 _lib = None
 EXPORTS = ("fp4_tensor_scale", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
-           "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_unpack",
+           "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_pack_grouped",
+           "guide_unpack",
            "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_rht16",
            "fp4_encode_values", "fp4_stream_copy", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
            "fp4_status_str", "fp4_last_error")
+
+
+class _CGuide(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("rows", C.c_int64), ("cols", C.c_int64),
+                ("guide_bits", C.c_void_p), ("guide_scales", C.c_void_p)]
 
 
 class _CGemm(C.Structure):
@@ -102,6 +108,7 @@ def lib():
         "fp4_guide_mismatch": [CP, P, I64, I64, I64, P, P, P, P, P],
         "fp4_dequantize": [CP, P, P, P, I64, I64, P, I64, I, P],
         "guide_pack": [CP, P, P, I64, I64, P, P, P],
+        "guide_pack_grouped": [CP, I, C.POINTER(_CGuide), P],
         "guide_unpack": [CP, P, P, I64, I64, P, P, P],
         "fp4_gemm_mxfp4": [P, P, P, P, I64, I64, I64, P, I64, I, P],
         "fp4_gemm_mxfp4_grouped": [I, C.POINTER(_CGemm), I, P],
@@ -339,6 +346,28 @@ def guide_pack(codes: torch.Tensor, scales: torch.Tensor, cfg: Fp4Config, rows: 
     _check(lib().guide_pack(C.byref(c), _ptr(codes), _ptr(scales), rows, cols, _ptr(bits), _ptr(gscales),
                             _stream(codes)), "guide_pack")
     return bits, gscales
+
+
+def guide_pack_grouped(tensors, cfg: Fp4Config, outs=None):
+    """guide_pack of several tensors in one launch: tensors is a list of (codes, scales, rows, cols).
+    Returns the list of (guide_bits, guide_scales)."""
+    if not tensors:
+        raise ValueError("no tensors")
+    arr = (_CGuide * len(tensors))()
+    res = []
+    for i, (codes, scales, rows, cols) in enumerate(tensors):
+        _on_gpu(codes, scales)
+        n = rows * cols
+        if outs is not None:
+            bits, gs = outs[i]
+        else:
+            bits, gs = _u8(n // 8, codes), _u8(n // cfg.block, codes)
+        _on_gpu(bits, gs)
+        arr[i] = _CGuide(_ptr(codes), _ptr(scales), rows, cols, _ptr(bits), _ptr(gs))
+        res.append((bits, gs))
+    c = cfg.c()
+    _check(lib().guide_pack_grouped(C.byref(c), len(tensors), arr, _stream(tensors[0][0])), "guide_pack_grouped")
+    return res
 
 
 def guide_unpack(bits: torch.Tensor, gscales: torch.Tensor, cfg: Fp4Config, rows: int, cols: int,

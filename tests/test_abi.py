@@ -30,7 +30,7 @@ def fq():
 def test_header_declares_the_expected_calls():
     names = _declared()
     for n in ["fp4_quantize", "fp4_quantize_guided", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_guide_mismatch",
-              "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_rht16", "fp4_tensor_scale", "fp4_encode_values", "fp4_codes_bytes",
+              "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "guide_pack_grouped", "fp4_rht16", "fp4_tensor_scale", "fp4_encode_values", "fp4_codes_bytes",
               "fp4_scales_bytes", "fp4_guide_bytes", "fp4_status_str", "fp4_last_error"]:
         assert n in names, n
 
@@ -134,6 +134,27 @@ def test_grouped_gemm_host_side_errors(fq):
     arr[0] = fq._CGemm(None, None, None, None, 0, 4, 64, None, 4)
     arr[1] = fq._CGemm(None, None, None, None, 4, 0, 64, None, 0)
     assert g(2, arr, 0, None) == 0                            # every product empty: nothing launched
+
+
+def test_grouped_guide_pack_host_side_errors(fq):
+    L = fq.lib()
+    A = 1 << 20
+    cfg = fq.Fp4Config().c()
+    arr = (fq._CGuide * 17)()
+    for i in range(17):
+        arr[i] = fq._CGuide(A, A, 4, 32, A, A)
+    g = L.guide_pack_grouped
+    assert g(C.byref(cfg), 0, arr, None) == 1
+    assert g(C.byref(cfg), 17, arr, None) == 1
+    assert g(C.byref(cfg), 2, None, None) == 1
+    arr[1] = fq._CGuide(A, A, 4, 24, A, A)               # cols % 16
+    assert g(C.byref(cfg), 2, arr, None) == 2
+    assert "tensor 1" in L.fp4_last_error().decode()
+    arr[1] = fq._CGuide(A, None, 4, 32, A, A)            # null scales
+    assert g(C.byref(cfg), 2, arr, None) == 1
+    arr[0] = fq._CGuide(None, None, 0, 32, None, None)
+    arr[1] = fq._CGuide(None, None, 4, 0, None, None)
+    assert g(C.byref(cfg), 2, arr, None) == 0              # all empty: nothing launched
 
 
 def test_binding_refuses_cpu_tensors(fq):

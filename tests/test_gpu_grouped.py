@@ -82,3 +82,26 @@ def test_grouped_sixteen_tensors_equal_single_calls(fq):
     for x, g in zip(xs, grouped):
         c, s = fq.fp4_quantize(x, cfg)
         assert torch.equal(c, g[0]) and torch.equal(s, g[1])
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_grouped_guide_pack(fq, fmt):
+    # codes and scales from the oracle's quantization of mixed shapes (odd NVFP4 group counts included);
+    # one grouped launch equals the oracle's guide_pack on each tensor, bit for bit
+    B = 32 if fmt else 16
+    shapes = [(r, c) for r, c in SHAPES + [(3, 48), (5, 16)] if c % B == 0]
+    oc = O.Cfg(format=fmt)
+    cfg = fq.Fp4Config(format=fmt)
+    host, tensors = [], []
+    for i, (r, c) in enumerate(shapes):
+        h = W.c1_x(r, c, seed=40 + i)
+        ts = O.tensor_scale(oc, h) if fmt == 0 else 1.0
+        codes, scales = O.quantize(oc, O.RTN, h, ts)
+        host.append((codes, scales, r, c))
+        tensors.append((torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), r, c))
+    outs = fq.guide_pack_grouped(tensors, cfg)
+    torch.cuda.synchronize()
+    for i, (codes, scales, r, c) in enumerate(host):
+        bits, gs = O.guide_pack(oc, codes, scales, r, c)
+        assert (outs[i][0].cpu().numpy() == bits).all(), i
+        assert (outs[i][1].cpu().numpy() == gs).all(), i
