@@ -275,7 +275,8 @@ fp4_status fp4_rht16(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld,
 /* Element encode of n pre-scaled fp32 values (the per-element rounding step
  * on its own, for exhaustive verification): out[i] = sign<<3 | k of v[i]
  * clamped to Gmax; mode FP4_MODE_RTN, FP4_MODE_SR (aux[i] = random byte) or
- * FP4_MODE_GUIDED (aux[i] = guide bit).  aux may be NULL for RTN.
+ * FP4_MODE_GUIDED (aux[i] = guide bit).  aux may be NULL for RTN.  The code
+ * of a NaN value is unspecified (quantization zeroes every block holding one).
  * n % 8 == 0; v 16-byte aligned, aux and out 8-byte aligned. */
 fp4_status fp4_encode_values(int grid, int mode, const float* v, const uint8_t* aux, int64_t n,
                              uint8_t* out, hipStream_t stream);

@@ -260,31 +260,21 @@ __device__ __forceinline__ uint32_t encode8_guided_e2m1_bf16(const uint32_t w[4]
     return guided_from_trunc(pack_trunc8_bf16(w, scale), pack_trunc8_bf16(wd, scale), gbits);
 }
 
-// SR E2M1: the grid is uniform with step 0.5, 1, 2 on [0,2), [2,4), [4,6].
-// r = vc / step (exact) and the element rounds up iff frac(r) > c with
-// c = (2u+1)/512; equivalently k = base + ceil(r - c) (r - c is exact
-// wherever it matters).
-__device__ __forceinline__ uint32_t encode1_sr_e2m1(float v, uint32_t u) {
-    const float vc = fminf(fabsf(v), 6.0f);
-    const int e = (int)(__float_as_uint(vc) >> 23);
-    const int q = min(max(e - 127, 0), 2);            // 0, 1, 2 for the three step sizes
-    const float r = __builtin_ldexpf(vc, 1 - q);
-    const float c = __builtin_fmaf((float)u, 0.00390625f, 0.001953125f);
-    const int k = (int)__builtin_ceilf(r - c) + 2 * q;
-    return (uint32_t)k | sign_nibble(v);
-}
-
-// SR E2M1 through the hardware convert, one element per instruction (slot 0;
-// slot 1 converts +0).  The convert rounds up iff D + R >= 2^32, with D the
-// discarded fraction of the bracket as a 32-bit fixed-point number; the word
-// R = (~u << 24) | 0x7FFFFF makes that "D > (2u+1) * 2^23", i.e. 2u+1 < 512 f.
-// It is exact except below 1.0, where it keeps 23 fraction bits: a value with
-// at most 14 significant bits never lies strictly within 2^-23 above a
-// threshold (thresholds are multiples of 2^-10 and v >= 2^-10 there), so it is
-// exact for such values.  Checked on the GPU against encode1_sr_e2m1 over every
-// fp32 value in [-8, 8] and every u: the only differences are values with 15
-// or more significant bits.  MXFP4 without the RHT scales bf16 inputs by a
-// power of two, so its v has at most 8 significant bits.
+// SR E2M1: the grid is uniform with step 0.5, 1, 2 on [0,2), [2,4), [4,6], and
+// an element rounds up iff the fraction f of its bracket exceeds c = (2u+1)/512,
+// i.e. iff |v| > lo + c * step.  Every such threshold, and every bracket end, is a
+// multiple of 2^-10.
+//
+// The hardware convert, one element per instruction (slot 0; slot 1 converts
+// +0), rounds up iff D + R >= 2^32, with D the discarded fraction of the bracket
+// as a 32-bit fixed-point number; the word R = (~u << 24) | 0x7FFFFF makes that
+// "D > (2u+1) * 2^23", i.e. 2u+1 < 512 f.  It is exact except below 1.0, where it
+// keeps 23 fraction bits of v.  Checked on the GPU against the rule above over
+// every fp32 value in [-8, 8] and every u: the only differences are values lying
+// strictly within 2^-23 above a threshold, which have 15 or more significant
+// bits.  So it is exact for every multiple of 2^-23 (encode8_sr_e2m1_w below),
+// and for every value with at most 14 significant bits (MXFP4 without the RHT
+// scales bf16 inputs by a power of two, so its v has at most 8).
 // nw = ~(four random bytes); byte j of nw becomes the top byte of R.
 __device__ __forceinline__ uint32_t sr_word(uint32_t nw, int j) {
     return __builtin_amdgcn_perm(nw, 0x007FFFFFu, ((4u + (uint32_t)j) << 24) | 0x020100u);
@@ -311,17 +301,49 @@ __device__ __forceinline__ uint32_t encode8_sr_e2m1_short(const float v[8], uint
     return __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
 }
 
+// SR E2M1 of values with any number of significant bits, given as w = 2^23 v.
+// |w| is rounded up to an integer (sign kept): no threshold or bracket end
+// lies strictly between |v| and that integer times 2^-23, so SR rounds both the
+// same way, and the convert is exact for the latter.  The convert then divides
+// by the scale 2^23 itself: for every integer-valued c up to 2^26 this equals
+// converting c * 2^-23, and every |c| of 2^26 or more, infinity included,
+// saturates to the codeword 6 (both checked on the GPU for every such fp32 c,
+// both signs and slots; the first for every u).
+__device__ __forceinline__ uint32_t encode8_sr_e2m1_w(const float w[8], uint32_t rnd0, uint32_t rnd1) {
+    float c[8];
+    #pragma unroll
+    for (int j = 0; j < 8; ++j)
+        c[j] = __uint_as_float((__float_as_uint(w[j]) & 0x80000000u) | __float_as_uint(__builtin_ceilf(fabsf(w[j]))));
+    return encode8_sr_e2m1_short(c, rnd0, rnd1, 0x1p23f);
+}
+
 __device__ __forceinline__ uint32_t encode1_rtn_uniform(float v) {
     const float vc = fminf(fabsf(v), 7.0f);
     const uint32_t k = __float_as_uint(vc + 8388608.0f) - 0x4B000000u;   // RNE to integer
     return k | sign_nibble(v);
 }
 
-__device__ __forceinline__ uint32_t encode1_sr_uniform(float v, uint32_t u) {
-    const float vc = fminf(fabsf(v), 7.0f);
-    const float c = __builtin_fmaf((float)u, 0.00390625f, 0.001953125f);
-    const int k = (int)__builtin_ceilf(vc - c);
-    return (uint32_t)k | sign_nibble(v);
+// SR on the uniform grid: k = ceil(min(|v|, 7) - c), c = (2u+1)/512 (the
+// difference is exact wherever it decides k).  The eight magnitudes are
+// written as bytes straight from the fp32 k (exact integers; odd elements
+// times 16), so one OR packs the nibbles, and the eight sign bits are moved
+// to bit 3 of their nibbles with byte permutes.  A NaN v gives magnitude 0.
+__device__ __forceinline__ uint32_t encode8_sr_uniform(const float v[8], uint32_t rnd0, uint32_t rnd1) {
+    uint32_t e = 0, o = 0;   // bytes k0 k2 k4 k6, and 16 k1 .. 16 k7
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t u = ((j < 4 ? rnd0 : rnd1) >> (8 * (j & 3))) & 0xFFu;
+        const float c = __builtin_fmaf((float)u, 0.00390625f, 0.001953125f);
+        const float k = __builtin_ceilf(__builtin_elementwise_minimum(fabsf(v[j]), 7.0f) - c);
+        if (j & 1) o = __builtin_amdgcn_cvt_pk_u8_f32(k * 16.0f, j >> 1, o);
+        else e = __builtin_amdgcn_cvt_pk_u8_f32(k, j >> 1, e);
+    }
+    const uint32_t* b = reinterpret_cast<const uint32_t*>(v);
+    // byte 3 of a float holds its sign at bit 7: odd elements' sign bytes into
+    // bytes 0..3 give bits 7, 15, 23, 31; even elements', shifted down by 4, bits 3, 11, 19, 27
+    const uint32_t so = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0703u) | __builtin_amdgcn_perm(b[7], b[5], 0x07030C0Cu);
+    const uint32_t se = (__builtin_amdgcn_perm(b[2], b[0], 0x0C0C0703u) | __builtin_amdgcn_perm(b[6], b[4], 0x07030C0Cu)) >> 4;
+    return (e | o) | (so & 0x80808080u) | (se & 0x08080808u);
 }
 
 __device__ __forceinline__ uint32_t encode1_guided_uniform(float v, uint32_t b) {
@@ -335,7 +357,8 @@ __device__ __forceinline__ uint32_t encode1_guided_uniform(float v, uint32_t b) 
 
 // rnd: 8 random bytes for SR (rnd0 bytes 0..3 -> elements 0..3, rnd1 -> 4..7);
 // gbits: 8 guide bits for guided.  SHORT: every |v| has at most 14
-// significant bits (lets SR use the hardware convert).  scale: a power of two
+// significant bits, so E2M1 SR may give v to the hardware convert as it is
+// (otherwise 2^23 v goes through encode8_sr_e2m1_w).  scale: a power of two
 // the E2M1 RTN and short SR paths divide v by inside the convert; every other
 // path takes already scaled values (scale 1).
 template <int GRID, int MODE, bool SHORT = false>
@@ -347,15 +370,19 @@ __device__ __forceinline__ uint32_t encode8(const float v[8], uint32_t rnd0, uin
         return encode8_guided_e2m1(v, gbits);
     } else if constexpr (GRID == 0 && MODE == MODE_SR && SHORT) {
         return encode8_sr_e2m1_short(v, rnd0, rnd1, scale);
+    } else if constexpr (GRID == 0 && MODE == MODE_SR) {
+        float w[8];
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = v[j] * 0x1p23f;   // exact, or an overflow that saturates
+        return encode8_sr_e2m1_w(w, rnd0, rnd1);
+    } else if constexpr (MODE == MODE_SR) {
+        return encode8_sr_uniform(v, rnd0, rnd1);
     } else {
         uint32_t w = 0;
         #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t u = ((j < 4 ? rnd0 : rnd1) >> (8 * (j & 3))) & 0xFFu;
             uint32_t nib;
-            if constexpr (GRID == 0) nib = encode1_sr_e2m1(v[j], u);
-            else if constexpr (MODE == MODE_RTN) nib = encode1_rtn_uniform(v[j]);
-            else if constexpr (MODE == MODE_SR) nib = encode1_sr_uniform(v[j], u);
+            if constexpr (MODE == MODE_RTN) nib = encode1_rtn_uniform(v[j]);
             else nib = encode1_guided_uniform(v[j], (gbits >> j) & 1u);
             w |= nib << (4 * j);
         }

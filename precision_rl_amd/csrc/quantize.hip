@@ -73,13 +73,27 @@ __device__ __forceinline__ uint32_t nonzero_nibbles(uint32_t w) {
     return __builtin_popcount((w | (w >> 1) | (w >> 2) | (w >> 3)) & 0x11111111u);
 }
 
+// NVFP4: the reciprocals inv = RN(1/RN(dec(c)*s_t)) of all 128 scale magnitudes c
+// for one tensor scale, written to LDS by the workgroup (one IEEE division per
+// code instead of one per group).  Every thread of the workgroup must call it.
+template <int FMT>
+__device__ __forceinline__ void build_inv_table(float* tab, const float* ts) {
+    if constexpr (FMT == 0) {
+        if (threadIdx.x < 128u) tab[threadIdx.x] = nvfp4_inv(threadIdx.x, *ts);
+        __syncthreads();
+    }
+}
+
 // One workgroup's share (kChunkGroups groups starting at chunk `wg`) of one tensor.
 // OUT = 0 stores codes, scales (and emitted guide bits); OUT = 1 stores the
 // dequantized bf16 values instead (fake quantization); OUT = 2 (guided only)
 // takes the guide bits from the rollout's full codes and counts, instead of
 // storing anything, how often the guided result differs from those codes.
+// tab: LDS space for the NVFP4 reciprocal table, which the chunk builds once its
+// loads are in flight (OUT = 2: the caller has built it).
 template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG, int OUT = 0>
-__device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg, uint32_t* acc = nullptr) {
+__device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg, float* tab,
+                                               uint32_t* acc = nullptr) {
     constexpr float kGmax = GRID == 0 ? 6.0f : 7.0f;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t q = lane & 1u;
@@ -127,11 +141,20 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     uint32_t n_elem = 0, n_nonadj = 0, n_mism = 0;   // OUT == 2
 
     const uint32_t signs = RHT ? rht_sign_mask(p.rht_seed) : 0u;   // uniform: scalar unit
-    float ts = 1.0f, denom = 1.0f;
+    float ts = 1.0f, denom = 1.0f, rden = 0.0f;
+    bool rden_ok = false;
     if constexpr (FMT == 0) {
+        if constexpr (OUT != 2) build_inv_table<FMT>(tab, p.ts);
         ts = *p.ts;
         denom = kGmax * ts;
+        // t = RN(amax / denom) is first taken as RN(amax * RN(1/denom)), which is
+        // within 3 fp32 steps of it whenever 1/denom is a normal number
+        rden = 1.0f / denom;
+        rden_ok = denom >= 0x1p-125f && denom <= 0x1p125f;
     }
+    // MXFP4 RTN and guided without the RHT convert straight from the bf16 bits;
+    // every other path widens the values, and then takes the amax in fp32
+    constexpr bool kWidened = RHT || FMT == 0 || GRID == 1 || MODE == MODE_SR;
 
     #pragma unroll
     for (int k = 0; k < kG; ++k) {
@@ -152,11 +175,13 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         // block amax key: monotone in the amax (bf16 bits, or fp32 bits with the
         // RHT); NaN and Inf give keys >= 0x7F800000
         uint32_t amax_key;
-        if constexpr (RHT) {
+        if constexpr (kWidened) {
+            // NaN-propagating maximum of the magnitudes: equal to the widened
+            // bf16 maximum when all are finite
             float m = 0.0f;
             #pragma unroll
             for (int j = 0; j < 16; ++j) m = __builtin_elementwise_maximum(m, fabsf(y[j]));
-            amax_key = __float_as_uint(m * 0.25f);
+            amax_key = __float_as_uint(RHT ? m * 0.25f : m);
         } else {
             amax_key = amax_bits16(gw) << 16;
         }
@@ -169,15 +194,24 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             sc = gs[k];
             if constexpr (FMT == 0) {
                 finite = finite && ((sc & 0x7Fu) != 0x7Fu);
-                inv = nvfp4_inv(sc, ts);
+                inv = tab[sc & 0x7Fu];
             } else {
                 finite = finite && (sc != 0xFFu);
                 inv = mx_inv(sc);
             }
         } else if constexpr (FMT == 0) {
-            const float t = __uint_as_float(amax_key) / denom;
+            // The E4M3 code of t changes only at the midpoints between E4M3
+            // values: fp32 patterns whose low 20 bits are 0x80000 (2^-6 and
+            // above; every E4M3 step there is 2^20 patterns).  Where the product
+            // is 4 or more steps from a midpoint and at or above 2^-6 + 4 steps
+            // (or 0), the exact quotient lies on the same side, so both give the
+            // same code; elsewhere the quotient is computed.
+            float t = __uint_as_float(amax_key) * rden;
+            const uint32_t tb = __float_as_uint(t);
+            const bool exact = !rden_ok || tb - 1u < 0x3C800003u || (tb & 0xFFFFFu) - 0x7FFFCu <= 8u;
+            if (__builtin_expect(exact, 0)) t = __uint_as_float(amax_key) / denom;
             sc = e4m3_encode_rne(fminf(t, 448.0f));
-            inv = nvfp4_inv(sc, ts);
+            inv = tab[sc];
             if (!finite) sc = 0x7Fu;
         } else {
             const uint32_t e = amax_key >> 23;
@@ -197,12 +231,27 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         // bits.  Its E2M1 converts take the inputs and divide by 2^e themselves.
         constexpr bool kShort = FMT == 1 && !RHT;
         constexpr bool kInCvt = kShort && GRID == 0;
+        // E2M1 SR of values with up to 24 significant bits takes w = 2^23 v
+        constexpr bool kSrW = GRID == 0 && MODE == MODE_SR && !kShort;
         float v[16];
         float cscale = 1.0f;
         if constexpr (kInCvt) {
             cscale = mx_scale(sc);
             #pragma unroll
             for (int j = 0; j < 16; ++j) v[j] = y[j];
+        } else if constexpr (kSrW) {
+            // RN(y * inv * 2^23), or RN(a * inv * 2^21) with the RHT, equals 2^23 v
+            // wherever v is normal (smaller v round to 0 with their sign either
+            // way); one product where inv times the power of two is exact and finite
+            if (inv < 0x1p100f) {
+                const float m = inv * (RHT ? 0x1p21f : 0x1p23f);
+                #pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = y[j] * m;
+            } else {
+                const float m = RHT ? inv * 0.25f : inv;   // exact: inv >= 2^100
+                #pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = (y[j] * m) * 0x1p23f;
+            }
         } else if constexpr (RHT) {
             // v = RN((a/4) * inv) = RN(a * (inv/4)) when inv/4 is exact: always
             // for MXFP4 (a power of two >= 2^-129), and for NVFP4 unless inv < 2^-124
@@ -225,6 +274,9 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         } else if constexpr (kInCvt && MODE == MODE_GUIDED) {
             c0 = encode8_guided_e2m1_bf16(gw, gb[k] & 0xFFu, cscale);
             c1 = encode8_guided_e2m1_bf16(gw + 4, gb[k] >> 8, cscale);
+        } else if constexpr (kSrW) {
+            c0 = encode8_sr_e2m1_w(v, r0, r1);
+            c1 = encode8_sr_e2m1_w(v + 8, r2, r3);
         } else {
             c0 = encode8<GRID, MODE, kShort>(v, r0, r1, gb[k] & 0xFFu, cscale);
             c1 = encode8<GRID, MODE, kShort>(v + 8, r2, r3, gb[k] >> 8, cscale);
@@ -281,7 +333,8 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
 
 template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_quantize(const QuantParams p) {
-    quantize_chunk<FMT, GRID, MODE, RHT, EMIT, CONTIG>(p, blockIdx.x);
+    __shared__ float tab[128];
+    quantize_chunk<FMT, GRID, MODE, RHT, EMIT, CONTIG>(p, blockIdx.x, tab);
 }
 
 // Several tensors with one configuration in one launch: workgroup b belongs to
@@ -293,10 +346,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize_grouped(const GroupedQuan
     uint32_t t = 0;
     while (t + 1 < gp.n && b >= gp.wg_start[t + 1]) ++t;
     const uint32_t wg = b - gp.wg_start[t];
+    __shared__ float tab[128];
     if ((gp.contig_mask >> t) & 1u)
-        quantize_chunk<FMT, GRID, MODE, RHT, EMIT, true>(gp.t[t], wg);
+        quantize_chunk<FMT, GRID, MODE, RHT, EMIT, true>(gp.t[t], wg, tab);
     else
-        quantize_chunk<FMT, GRID, MODE, RHT, EMIT, false>(gp.t[t], wg);
+        quantize_chunk<FMT, GRID, MODE, RHT, EMIT, false>(gp.t[t], wg, tab);
 }
 
 template <int FMT, int GRID, int MODE, bool RHT, bool EMIT>
@@ -315,8 +369,10 @@ constexpr uint32_t kMismatchBlocks = 1024;
 template <int FMT, int GRID, bool RHT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_guide_mismatch(const QuantParams p, uint32_t nchunks) {
     uint32_t acc[3] = {0u, 0u, 0u};
+    __shared__ float tab[128];
+    build_inv_table<FMT>(tab, p.ts);
     for (uint32_t wg = blockIdx.x; wg < nchunks; wg += gridDim.x)   // the same trip count in a workgroup
-        quantize_chunk<FMT, GRID, MODE_GUIDED, RHT, false, CONTIG, 2>(p, wg, acc);
+        quantize_chunk<FMT, GRID, MODE_GUIDED, RHT, false, CONTIG, 2>(p, wg, tab, acc);
     __shared__ uint32_t red[3][kThreads / 64];
     #pragma unroll
     for (int c = 0; c < 3; ++c) {
@@ -357,7 +413,8 @@ hipError_t launch_mismatch_g(bool rht, bool contig, const QuantParams& p, hipStr
 
 template <int FMT, int GRID, int MODE, bool RHT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_fake_quantize(const QuantParams p) {
-    quantize_chunk<FMT, GRID, MODE, RHT, false, CONTIG, 1>(p, blockIdx.x);
+    __shared__ float tab[128];
+    quantize_chunk<FMT, GRID, MODE, RHT, false, CONTIG, 1>(p, blockIdx.x, tab);
 }
 
 template <int FMT, int GRID, int MODE>

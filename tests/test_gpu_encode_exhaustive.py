@@ -107,7 +107,8 @@ def gpu_breakpoints(fq, g, mode, aux, sign):
 
 
 CASES = [(0, 0, 0), (1, 0, 0), (0, 2, 0), (0, 2, 1), (1, 2, 0), (1, 2, 1),
-         (0, 1, 0), (0, 1, 1), (0, 1, 127), (0, 1, 128), (0, 1, 255), (1, 1, 0), (1, 1, 200)]
+         (0, 1, 0), (0, 1, 1), (0, 1, 2), (0, 1, 64), (0, 1, 127), (0, 1, 128), (0, 1, 191), (0, 1, 254),
+         (0, 1, 255), (1, 1, 0), (1, 1, 1), (1, 1, 127), (1, 1, 200), (1, 1, 255)]
 
 
 @pytest.mark.parametrize("g,mode,aux", CASES)

@@ -240,7 +240,46 @@ def test_guided_with_nan_guide_scales(fq):
         assert (host(s) == oc_s).all() and (host(c) == oc_c).all()
 
 
-@pytest.mark.parametrize("ts", [1.0, 0.37, 1e-3, 2.0 ** -120, 7.5e37 / 2688])
+def _midpoint_blocks(rng):
+    """bf16 rows of 16-element blocks whose amax is an E4M3 rounding midpoint (1 + (2m+1)/16) 2^e,
+    e = -6..8, or one to three bf16 steps either side of it; the other 15 elements are smaller.
+    Six more blocks: all zero, amax 2^-7, 2^-6 and its neighbours (the subnormal-code boundary), 448."""
+    b6 = int(W.f32_to_bf16_rne(np.array([2.0 ** -6], np.float32))[0])
+    amax = [0, b6 - 129, b6 - 1, b6, b6 + 1, 0x43E0]
+    for e in range(-6, 9):
+        for m in range(8):
+            mid = (1 + (2 * m + 1) / 16) * 2.0 ** e
+            if mid > 448:
+                continue
+            b = int(W.f32_to_bf16_rne(np.array([mid], np.float32))[0])
+            amax += [b + d for d in (-3, -2, -1, 0, 1, 2, 3)]
+    amax = np.array(amax, np.uint16)
+    blocks = W.f32_to_bf16_rne((rng.uniform(-1, 1, (len(amax), 16)) *
+                                W.bf16_to_f32(amax)[:, None] * 0.9).astype(np.float32))
+    blocks[np.arange(len(amax)), rng.integers(0, 16, len(amax))] = amax | (rng.integers(0, 2, len(amax)) << 15).astype(np.uint16)
+    return blocks.reshape(-1, 64)
+
+
+# denominators RN(6 s_t) = 1 + k 2^-23 or 1 - k 2^-24: the quotients amax / denom then lie on, or a
+# few fp32 steps below or above, the E4M3 midpoints, where the scale code must come from the exact
+# quotient (ties to even at the midpoint itself)
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 5, -1, -2, -3, -5])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_nvfp4_scale_quotient_near_e4m3_midpoints(fq, k, rnd):
+    denom = np.float32(1 + k * 2.0 ** -23) if k >= 0 else np.float32(1 + k * 2.0 ** -24)
+    ts = np.float32(denom / np.float32(6))
+    assert np.float32(6) * ts == denom or k != 0
+    xh = _midpoint_blocks(np.random.default_rng(40 + k))
+    cfg = fq.Fp4Config(rounding=rnd, sr_seed=5)
+    oc = ocfg(cfg)
+    c, s = fq.fp4_quantize(dev(xh), cfg, torch.tensor([ts], device="cuda"))
+    oc_c, oc_s = O.quantize(oc, rnd, xh, float(ts))
+    bad = np.nonzero(host(s) != oc_s)[0]
+    assert bad.size == 0, [(int(i), int(host(s)[i]), int(oc_s[i])) for i in bad[:8]]
+    assert (host(c) == oc_c).all()
+
+
+@pytest.mark.parametrize("ts", [1.0, 0.37, 1e-3, 2.0 ** -120, 7.5e37 / 2688, 2.0 ** -128, 1e37])
 @pytest.mark.parametrize("rnd", [0, 1])
 def test_nvfp4_extreme_tensor_scales(fq, ts, rnd):
     # 1e-38 rows at ts = 2^-120: block scales S below 2^-128, where 1/S saturates to FLT_MAX
