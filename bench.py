@@ -16,7 +16,10 @@ dependent chain and kernel 5 depends on none of them; ``--streams 2`` runs it
 on a second stream (default priority) beside the chain.  Both orders are timed
 on every run and reported; ``value`` uses the one ``--streams`` selects.
 ``value`` = algorithmic bytes of the step / step time, in GB/s, measured with
-HIP events around K whole steps.  Inputs are resident in HBM before timing; a
+HIP events around K whole steps.  Every timed region is preceded by 100 ms of
+untimed launches of the same work (the shader clock idles low while the host
+generates data, and takes tens of milliseconds of load to climb), then the W
+warm-up steps.  Inputs are resident in HBM before timing; a
 rotating pool of input sets (768 MiB) keeps the 256 MB Infinity Cache from
 serving re-reads across steps.
 
@@ -51,6 +54,7 @@ sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak (no sparsity), TFLOP/s
+SETTLE_MS = 100.0  # untimed load before every timed region (shader clock ramp)
 
 
 def log(*a):
@@ -102,8 +106,24 @@ class KernelTimer:
         return {k: (tot[k] / cnt[k], cnt[k]) for k in tot}
 
 
+def settle(torch, fn, ms=SETTLE_MS):
+    """Untimed calls of fn(i) until the GPU has run them for `ms` milliseconds: the shader clock
+    idles low between workloads (host-side data generation) and needs tens of milliseconds of load
+    to climb, so shorter warm-ups time a partly down-clocked GPU."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(4):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return
+
+
 def back_to_back(torch, fn, reps, warm=2):
-    """Average ms of `fn(i)` over `reps` consecutive launches on the current stream."""
+    """Average ms of `fn(i)` over `reps` consecutive launches on the current stream, after a settle."""
+    settle(torch, fn)
     for i in range(warm):
         fn(i)
     torch.cuda.synchronize()
@@ -115,6 +135,32 @@ def back_to_back(torch, fn, reps, warm=2):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps
+
+
+def graph_time(torch, fn, reps, check):
+    """Average ms per launch of `reps` launches of fn(i) captured in one HIP graph and replayed, so
+    that host-side launch cost (several microseconds per call from Python) does not hide the
+    duration of small kernels.  check() compares the outputs with an eager run; it follows every
+    replay (two untimed, one timed).  Returns (ms, all checks passed)."""
+    settle(torch, fn)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    ok = True
+    for _ in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        ok = ok and bool(check())
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ok = ok and bool(check())
+    del g
+    return a.elapsed_time(b) / reps, ok
 
 
 def source_sha():
@@ -217,6 +263,7 @@ def headline(args, fq, torch, W, ceiling):
                 f[name]()
 
     def timed_steps(streams):
+        settle(torch, lambda k: step(k, streams))
         for k in range(args.warmup):
             step(k, streams)
         torch.cuda.synchronize()
@@ -339,6 +386,28 @@ def other_workloads(args, fq, torch, W, ceiling):
     cnt = torch.empty(3, dtype=torch.int64, device="cuda")
     r["guide_mismatch"] = report(back_to_back(torch, lambda i: fq.fp4_guide_mismatch(xs[i % P], cfg, guides[i % P][0], guides[i % P][1], tss[i % P], out=cnt), it), 2.5625 * n, n, ceiling)
     r["guide_mismatch_counts"] = mismatch_counts(fq, xs[0], cfg, guides[0][0], guides[0][1], tss[0])
+    # the same kernels as one graph of launches: at 16 MiB a call from Python costs about as much
+    # host time as the kernel runs, so the eager figures above are bound by the host
+    gr = max(it, 32)
+    last = (gr - 1) % P
+
+    def same(*pairs):
+        return all(torch.equal(a, b) for a, b in pairs)
+    ms, ok = graph_time(torch, lambda i: fq.fp4_tensor_scale(xs[i % P], cfg, out=tso), gr,
+                        lambda: same((tso, fq.fp4_tensor_scale(xs[last], cfg))))
+    r["tensor_scale_graph"] = dict(report(ms, 2 * n, n, ceiling), replays_match_eager=ok)
+    ms, ok = graph_time(torch, lambda i: fq.fp4_quantize(xs[i % P], cfg, tss[i % P], codes=oc, scales=os_), gr,
+                        lambda: same(*zip((oc, os_), fq.fp4_quantize(xs[last], cfg, tss[last]))))
+    r["quantize_rtn_graph"] = dict(report(ms, 2.5625 * n, n, ceiling), replays_match_eager=ok)
+    ms, ok = graph_time(torch, lambda i: fq.fp4_quantize(xs[i % P], cfg, tss[i % P], emit=True, codes=oc,
+                                                         scales=os_, bits=ob), gr,
+                        lambda: same(*zip((oc, os_, ob), fq.fp4_quantize(xs[last], cfg, tss[last], emit=True))))
+    r["quantize_rtn_emit_graph"] = dict(report(ms, 2.6875 * n, n, ceiling), replays_match_eager=ok)
+    ms, ok = graph_time(torch, lambda i: fq.fp4_quantize_guided(xs[i % P], cfg, guides[i % P][2], guides[i % P][1],
+                                                                tss[i % P], codes=oc, scales=os_), gr,
+                        lambda: same(*zip((oc, os_), fq.fp4_quantize_guided(xs[last], cfg, guides[last][2],
+                                                                             guides[last][1], tss[last]))))
+    r["quantize_guided_graph"] = dict(report(ms, 2.75 * n, n, ceiling), replays_match_eager=ok)
     res["nvfp4_act_4096x2048"] = r
     del xs, xrs, guides
 
