@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the CPU-baseline sample")
     ap.add_argument("--config-iters", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed load before every timed region (shorter under a profiler: fewer dispatches)")
     return ap.parse_args()
 
 
@@ -106,10 +108,11 @@ class KernelTimer:
         return {k: (tot[k] / cnt[k], cnt[k]) for k in tot}
 
 
-def settle(torch, fn, ms=SETTLE_MS):
+def settle(torch, fn, ms=None):
     """Untimed calls of fn(i) until the GPU has run them for `ms` milliseconds: the shader clock
     idles low between workloads (host-side data generation) and needs tens of milliseconds of load
     to climb, so shorter warm-ups time a partly down-clocked GPU."""
+    ms = SETTLE_MS if ms is None else ms
     t0 = time.perf_counter()
     i = 0
     while True:
@@ -531,7 +534,9 @@ def gemm_workload(args, fq, torch, W):
 
 
 def main():
+    global SETTLE_MS
     args = parse()
+    SETTLE_MS = args.settle_ms
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); runs on several GPUs are not "
               "part of this path", file=sys.stderr)

@@ -511,19 +511,27 @@ __device__ __forceinline__ uint32_t rht_sign_mask(uint64_t seed) {
 // 2^-133, so a * 1/4 is always exact; it never needs to be rounded.)
 template <bool RHT, bool QUARTER = true>
 __device__ __forceinline__ void widen16(const uint32_t w[8], uint32_t signs, float y[16]) {
-    #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        y[2 * j] = bf16_lo(w[j]);
-        y[2 * j + 1] = bf16_hi(w[j]);
-    }
     if constexpr (RHT) {
+        // the diagonal's sign bits are the same for every lane: widening and sign
+        // flip in one instruction per element (adding 2^31 flips bit 31)
         #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            y[j] = __uint_as_float(__float_as_uint(y[j]) ^ (((signs >> j) & 1u) << 31));
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t slo = ((signs >> (2 * j)) & 1u) << 31, shi = ((signs >> (2 * j + 1)) & 1u) << 31;
+            uint32_t lo;
+            asm("v_lshl_add_u32 %0, %1, 16, %2" : "=v"(lo) : "v"(w[j]), "s"(slo));
+            y[2 * j] = __uint_as_float(lo);
+            y[2 * j + 1] = __uint_as_float((w[j] & 0xFFFF0000u) ^ shi);
+        }
         butterfly16(y);
         if constexpr (QUARTER) {
             #pragma unroll
             for (int j = 0; j < 16; ++j) y[j] = y[j] * 0.25f;
+        }
+    } else {
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            y[2 * j] = bf16_lo(w[j]);
+            y[2 * j + 1] = bf16_hi(w[j]);
         }
     }
 }

@@ -428,7 +428,7 @@ def test_guide_mismatch_bracket_cases_and_empty(fq):
 # ---------------------------------------------------------------- dequantize, guide, rht
 
 @pytest.mark.parametrize("fmt,grid", [(0, 0), (1, 0), (0, 1), (1, 1)])
-@pytest.mark.parametrize("shape", [(256, 512), (37, 544), (3, 32), (5, 48), (1, 16), (300, 2080)])
+@pytest.mark.parametrize("shape", [(256, 512), (37, 544), (3, 32), (5, 48), (1, 16), (300, 2080), (777, 1040)])
 def test_dequantize_vs_oracle(fq, fmt, grid, shape):
     rows, cols = shape
     B = 32 if fmt else 16
@@ -474,6 +474,14 @@ def test_guide_pack_unpack_vs_oracle(fq, fmt, shape):
     m, so = fq.guide_unpack(gb, gs, cfg, rows, cols)
     o_m, o_so = O.guide_unpack(oc, o_gb, o_gs, rows, cols)
     assert (host(m) == o_m).all() and (host(so) == o_so).all()
+    # scale arrays at odd addresses (the ABI asks for byte alignment only)
+    sbuf = torch.zeros(scales.size + 1, dtype=torch.uint8, device="cuda")
+    sbuf[1:] = torch.from_numpy(scales).cuda()
+    gsbuf = torch.full((scales.size + 3,), 0xA5, dtype=torch.uint8, device="cuda")
+    gb2, gs2 = fq.guide_pack(torch.from_numpy(codes).cuda(), sbuf[1:], cfg, rows, cols,
+                             gscales=gsbuf[3:])
+    assert (host(gb2) == o_gb).all() and (host(gs2) == o_gs).all()
+    assert (host(gsbuf[:3]) == 0xA5).all()
 
 
 @pytest.mark.parametrize("inverse", [False, True])
