@@ -27,14 +27,16 @@ Per kernel, two durations are reported: with events around every launch inside
 the steps, and as back-to-back launches of that kernel alone (events around
 the loop).  The roofline entry is for the kernel with the largest share of the
 step (per-launch events); its achieved rate uses the back-to-back duration,
-which compares directly with rocprofv3's kernel durations.  The other workloads (NVFP4 activation 4096x2048,
+which compares directly with rocprofv3's kernel durations.  Means come with the 10th, 50th and 90th
+percentiles of single launches (and of single steps).  The other workloads (NVFP4 activation 4096x2048,
 KV cache at 131072 tokens, one deep guidance-cache layer, uniform grid + RHT16
 + SR on a 65536x8192 GEMM operand) are timed back to back and reported under
 "workloads", and so is the MXFP4 matrix product of one deep layer's
 activations [8192, 4096] with one expert weight [1536 out, 4096 in], both
 quantized by the library, reported as TFLOP/s against the dense FP4 matrix
 peak.  The CPU baseline is the oracle timed on a bounded row sample of the
-headline step.
+headline step, on one host thread and on all host threads of one GPU's share
+(at most 16, rows split between them).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--streams 1|2]
 """
@@ -64,7 +66,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2))
     ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
@@ -72,7 +74,7 @@ def parse():
                     help="only the MXFP4 matrix product workload (one JSON line of its figures)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the CPU-baseline sample")
-    ap.add_argument("--config-iters", type=int, default=20)
+    ap.add_argument("--config-iters", type=int, default=100)
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
                     help="untimed load before every timed region (shorter under a profiler: fewer dispatches)")
     return ap.parse_args()
@@ -101,11 +103,12 @@ class KernelTimer:
         return out
 
     def summary(self):
-        tot, cnt = {}, {}
+        """name -> (mean ms, launches, (p10, median, p90) ms)."""
+        per = {}
         for name, s, e in self.events:
-            tot[name] = tot.get(name, 0.0) + s.elapsed_time(e)
-            cnt[name] = cnt.get(name, 0) + 1
-        return {k: (tot[k] / cnt[k], cnt[k]) for k in tot}
+            per.setdefault(name, []).append(s.elapsed_time(e))
+        return {k: (sum(v) / len(v), len(v), tuple(float(q) for q in np.percentile(v, [10, 50, 90])))
+                for k, v in per.items()}
 
 
 def settle(torch, fn, ms=None):
@@ -124,8 +127,13 @@ def settle(torch, fn, ms=None):
             return
 
 
+_last_spread = None   # (p10, median, p90) ms of the latest back_to_back, picked up by report()
+
+
 def back_to_back(torch, fn, reps, warm=2):
-    """Average ms of `fn(i)` over `reps` consecutive launches on the current stream, after a settle."""
+    """Average ms of `fn(i)` over `reps` consecutive launches on the current stream, after a settle.
+    A second pass times up to 50 launches one by one between events, for the spread."""
+    global _last_spread
     settle(torch, fn)
     for i in range(warm):
         fn(i)
@@ -137,7 +145,15 @@ def back_to_back(torch, fn, reps, warm=2):
         fn(i)
     b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps
+    ms = a.elapsed_time(b) / reps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(min(reps, 50))]
+    for i, (x, y) in enumerate(ev):
+        x.record()
+        fn(i)
+        y.record()
+    torch.cuda.synchronize()
+    _last_spread = tuple(float(q) for q in np.percentile([x.elapsed_time(y) for x, y in ev], [10, 50, 90]))
+    return ms
 
 
 def graph_time(torch, fn, reps, check):
@@ -190,12 +206,24 @@ def read_traffic(kernel_key: str, sha: str):
     return None
 
 
+def take_spread():
+    """The (p10, median, p90) of the latest back_to_back call, in microseconds, and forget it."""
+    global _last_spread
+    sp, _last_spread = _last_spread, None
+    return None if sp is None else [round(q * 1e3, 2) for q in sp]
+
+
 def report(ms, nbytes, n, ceiling=None):
+    """Rates for a mean launch time ms; with the spread of the back_to_back call that produced it
+    (per-launch events, which add a little time of their own)."""
     gbs = nbytes / (ms * 1e-3) / 1e9
     r = {"us": round(ms * 1e3, 2), "bytes": int(nbytes), "GBps": round(gbs, 1),
          "Gelem_per_s": round(n / (ms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
     if ceiling:
         r["frac_copy_ceiling"] = round(gbs / ceiling, 4)
+    sp = take_spread()
+    if sp is not None:
+        r["us_p10_median_p90_single_launch"] = sp
     return r
 
 
@@ -207,7 +235,8 @@ def copy_ceiling(torch, fq, mib=256, reps=20):
     for b in bufs:
         b.fill_(1)
     ms = back_to_back(torch, lambda i: fq.fp4_stream_copy(bufs[(2 * i) % 4], bufs[(2 * i + 1) % 4]), reps)
-    return {"bytes_per_launch": 2 * n, "us": round(ms * 1e3, 2), "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+    return {"bytes_per_launch": 2 * n, "us": round(ms * 1e3, 2), "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "us_p10_median_p90_single_launch": take_spread()}
 
 
 # ---------------------------------------------------------------- headline step
@@ -283,6 +312,14 @@ def headline(args, fq, torch, W, ceiling):
     ms_serial = timed_steps(1)
     ms_two = timed_steps(2)
     ms_step = ms_two if args.streams == 2 else ms_serial
+    # each step on its own between events (a separate pass): the spread of step times
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record()
+        step(k, args.streams)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    step_pct = [round(float(q) * 1e3, 2) for q in np.percentile([a.elapsed_time(b) for a, b in ev], [10, 50, 90])]
     # events around every kernel inside serialized steps
     timer = KernelTimer()
     for k in range(args.steps):
@@ -290,8 +327,9 @@ def headline(args, fq, torch, W, ceiling):
             timer.run(name, fn)
     torch.cuda.synchronize()
     kernels = {}
-    for name, (ms, cnt) in timer.summary().items():
-        kernels[name] = dict(report(ms, bytes_per[name] * n, n, ceiling), launches=cnt)
+    for name, (ms, cnt, pct) in timer.summary().items():
+        kernels[name] = dict(report(ms, bytes_per[name] * n, n, ceiling), launches=cnt,
+                             us_p10_median_p90=[round(q * 1e3, 2) for q in pct])
     # back-to-back launches of each kernel alone: the roofline figure
     for name in kernels:
         ms = back_to_back(torch, lambda i: step_fns(i)[name](), args.steps)
@@ -299,6 +337,7 @@ def headline(args, fq, torch, W, ceiling):
         kernels[name]["us_back_to_back"] = r["us"]
         kernels[name]["GBps_back_to_back"] = r["GBps"]
         kernels[name]["frac_hbm_peak_back_to_back"] = r["frac_hbm_peak"]
+        kernels[name]["us_p10_median_p90_single_launch"] = r.get("us_p10_median_p90_single_launch")
     # guided fake quantization (quantize -> bf16 in one pass), the QAT forward op
     fqo = [torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     ms = back_to_back(torch, lambda i: fq.fp4_fake_quantize(xs[i % P], cfg_rtn, None, outs[i % P]["gb"],
@@ -313,6 +352,7 @@ def headline(args, fq, torch, W, ceiling):
     diag = dict(report(ms, (2 + 0.5 + 1 / 32) * n, n, ceiling),
                 **mismatch_counts(fq, xs[0], cfg_rtn, outs[0]["rc"], outs[0]["rs"], None))
     return dict(rows=rows, cols=cols, n=n, ms_step=ms_step, ms_serial=ms_serial, ms_two=ms_two, step_bytes=step_bytes,
+                step_us_p10_median_p90=step_pct,
                 kernels=kernels, bytes_per=bytes_per, x_h=x_h, xr_h=xr_h, outs=outs[0], fake=fake, diag=diag)
 
 
@@ -333,25 +373,49 @@ def parity_sample(torch, h, oracle_mod, rows_s=64):
     return bool(ok)
 
 
-def cpu_baseline(args, W, oracle_mod, h):
-    """The oracle (unchanged) on rows [0, R) of the headline step, one host thread."""
-    O = oracle_mod
-    R = min(args.cpu_rows, h["rows"])
+def _oracle_step_rows(O, W, h, r0, r1):
+    """The five kernels of the step, by the oracle, on rows [r0, r1) (the SR counter follows the rows)."""
     cols = h["cols"]
-    x, xr = h["x_h"][:R], h["xr_h"][:R]
+    x, xr = h["x_h"][r0:r1], h["xr_h"][r0:r1]
     oc = O.Cfg(format=O.MXFP4)
-    osr = O.Cfg(format=O.MXFP4, sr_seed=W.C2_SR_SEED)
-    t = time.perf_counter()
+    osr = O.Cfg(format=O.MXFP4, sr_seed=W.C2_SR_SEED, sr_offset=r0 * cols // 16)
+    R = r1 - r0
     rc, rs = O.quantize(oc, O.RTN, xr)
     gb, gs = O.guide_pack(oc, rc, rs, R, cols)
     gc, gsc = O.quantize(oc, O.GUIDED, x, guide_bits=gb, guide_scales=gs)
     O.dequantize(oc, gc, gsc, 1.0, R, cols, out_bf16=True)
     O.quantize(osr, O.SR, x)
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(args, W, oracle_mod, h, threads=1):
+    """The oracle (unchanged) on rows [0, R) of the headline step, on `threads` host threads with the
+    rows split evenly between them (the oracle's C calls release the interpreter lock)."""
+    import concurrent.futures as cf
+    R = min(args.cpu_rows, h["rows"])
+    cols = h["cols"]
+    cuts = [R * k // threads for k in range(threads + 1)]
+    t = time.perf_counter()
+    if threads == 1:
+        _oracle_step_rows(oracle_mod, W, h, 0, R)
+    else:
+        with cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda k: _oracle_step_rows(oracle_mod, W, h, cuts[k], cuts[k + 1]), range(threads)))
     dt = time.perf_counter() - t
     b = sum(h["bytes_per"].values()) * R * cols
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"rows 0..{R} of the 16384x4096 workload ({R * cols} elements), all five kernels "
-                      f"of the step, single thread, {dt:.1f} s"}
+                      f"of the step, {threads} thread(s) over row ranges, {dt:.2f} s; host: "
+                      f"{os.cpu_count()} logical CPUs, {_cpu_model()}"}
 
 
 # ---------------------------------------------------------------- other workloads
@@ -509,7 +573,8 @@ def gemm_workload(args, fq, torch, W):
         out = torch.empty((M, N), dtype=dt, device="cuda")
         ms = back_to_back(torch, lambda i: fq.fp4_gemm_mxfp4(a, asc, b, bsc, M, N, K, out=out), reps, warm=5)
         tf = flops / (ms * 1e-3) / 1e12
-        res[name] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4)}
+        res[name] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
+                     "us_p10_median_p90_single_launch": take_spread()}
     # the same weight shape as 8 routed experts of 1024 tokens each, in one grouped launch
     E = 8
     ws = [fq.fp4_quantize(to_dev(W.f32_to_bf16_rne(W.normal_outliers_f32(N, K, 1020, 2 * e, 0.0, 1.0, sigma=0.02))),
@@ -525,7 +590,8 @@ def gemm_workload(args, fq, torch, W):
     ms = back_to_back(torch, lambda i: fq.lib().fp4_gemm_mxfp4_grouped(E, arr, fq.OUT_BF16, stream), reps, warm=5)
     tf = flops / (ms * 1e-3) / 1e12
     res["grouped_8_experts_bf16_out"] = {"experts": E, "tokens_per_expert": rows, "us": round(ms * 1e3, 2),
-                                         "TFLOPs": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4)}
+                                         "TFLOPs": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
+                                         "us_p10_median_p90_single_launch": take_spread()}
     r = res["bf16_out"]
     res["roofline"] = {"bound": "mfma", "kernel": "k_gemm_mx_lds", "achieved": r["TFLOPs"], "peak": PEAK_FP4_TFLOPS,
                        "unit": "TFLOP/s", "frac": r["frac_fp4_peak"], "traffic": None,
@@ -563,10 +629,12 @@ def main():
     parity = parity_sample(torch, h, oracle_mod)
     if not parity:
         log("PARITY FAILURE on the headline sample")
-    cpu = None
+    cpu = cpu_all = None
     if not (args.quick or args.no_cpu_baseline):
         log("CPU baseline (oracle) ...")
         cpu = cpu_baseline(args, W, oracle_mod, h)
+        # the same sample on all host threads of one GPU's share (at most 16)
+        cpu_all = cpu_baseline(args, W, oracle_mod, h, threads=max(1, min(16, os.cpu_count() or 1)))
     workloads = {} if args.quick else other_workloads(args, fq, torch, W, ceiling["GBps"])
     if not args.quick:
         workloads["mxfp4_gemm_8192x1536x4096"] = gemm_workload(args, fq, torch, W)
@@ -609,6 +677,8 @@ def main():
                      "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": dk["us_back_to_back"],
                      "avg_launch_us_in_step": dk["us"]},
         "cpu_baseline": cpu,
+        "cpu_baseline_all_threads": cpu_all,
+        "step_us_p10_median_p90": h["step_us_p10_median_p90"],
         "copy_ceiling": ceiling,
         "kernels": h["kernels"],
         "fake_quantize_guided_bf16": h["fake"],
