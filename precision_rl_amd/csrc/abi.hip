@@ -214,7 +214,7 @@ fp4_status fp4_quantize_grouped(const fp4_cfg* cfg, int guided, int n, const fp4
         p.sr_offset = cfg->sr_offset;
         p.rht_seed = cfg->rht_seed;
         if (d.ld == d.cols) gp.contig_mask |= 1u << t;
-        wg += fp4q::quantize_chunks((uint32_t)ng);
+        wg += fp4q::quantize_chunks(cfg->format, mode, cfg->rht16 != 0, (uint32_t)ng);
         if (wg >= (1ull << 31)) return fail(FP4_ERR_SHAPE, "grouped call too large");
     }
     gp.wg_start[n] = (uint32_t)wg;

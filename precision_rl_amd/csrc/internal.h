@@ -128,7 +128,7 @@ hipError_t launch_guide_mismatch(int format, int grid, bool rht, bool contig, co
 hipError_t launch_fake_quantize(int format, int grid, int mode, bool rht, bool contig,
                                 const QuantParams& p, hipStream_t s);
 // Workgroups needed to quantize `ngroups` 16-element groups.
-uint32_t quantize_chunks(uint32_t ngroups);
+uint32_t quantize_chunks(int format, int mode, bool rht, uint32_t ngroups);
 hipError_t launch_quantize_grouped(int format, int grid, int mode, bool rht, bool emit,
                                    const GroupedQuantParams& gp, hipStream_t s);
 hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams& p, hipStream_t s);

@@ -31,14 +31,15 @@ namespace fp4q {
 
 namespace {
 
-#ifndef FP4Q_HALVES_PER_LANE
-#define FP4Q_HALVES_PER_LANE 4
-#endif
 // Half-groups per lane (load slots); even, since slots are transposed in pairs.
-constexpr int kH = FP4Q_HALVES_PER_LANE;
-static_assert(kH >= 2 && kH % 2 == 0, "half-groups per lane must be even");
-constexpr int kG = kH / 2;                              // whole groups per lane
-constexpr uint32_t kChunkGroups = kThreads * kG;        // groups per workgroup
+// MXFP4 stochastic rounding without the RHT runs fastest with two (twice the
+// workgroups, so more of them in flight); every other kernel with four
+// (measured; NVFP4 SR and the RHT kernels lose with two).
+template <int FMT, int MODE, bool RHT>
+constexpr int halves_per_lane() { return FMT == 1 && MODE == MODE_SR && !RHT ? 2 : 4; }
+// Groups per workgroup.
+template <int FMT, int MODE, bool RHT>
+constexpr uint32_t chunk_groups() { return kThreads * (halves_per_lane<FMT, MODE, RHT>() / 2); }
 
 // Element offset of half-group hg (logical row-major order) in a tensor with row stride ld.
 template <bool CONTIG>
@@ -95,6 +96,10 @@ template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG, int OUT
 __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg, float* tab,
                                                uint32_t* acc = nullptr) {
     constexpr float kGmax = GRID == 0 ? 6.0f : 7.0f;
+    constexpr int kH = halves_per_lane<FMT, MODE, RHT>();
+    constexpr int kG = kH / 2;                                      // whole groups per lane
+    constexpr uint32_t kChunkGroups = chunk_groups<FMT, MODE, RHT>();
+    static_assert(kH >= 2 && kH % 2 == 0, "half-groups per lane must be even");
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t q = lane & 1u;
     // half-group of slot s: hg0 + 64 s; group owned after transposing slots 2k, 2k+1: gk(k)
@@ -399,6 +404,8 @@ __global__ void k_zero_counts(unsigned long long* c) {
 
 template <int FMT, int GRID>
 hipError_t launch_mismatch_g(bool rht, bool contig, const QuantParams& p, hipStream_t s) {
+    constexpr uint32_t kChunkGroups = chunk_groups<FMT, MODE_GUIDED, false>();
+    static_assert(chunk_groups<FMT, MODE_GUIDED, true>() == kChunkGroups, "one chunk size for the diagnostic");
     const uint32_t chunks = (p.ngroups + kChunkGroups - 1) / kChunkGroups;
     const dim3 b(chunks < kMismatchBlocks ? chunks : kMismatchBlocks), t(kThreads);
     if (rht) {
@@ -419,11 +426,13 @@ __global__ __launch_bounds__(kThreads) void k_fake_quantize(const QuantParams p)
 
 template <int FMT, int GRID, int MODE>
 hipError_t launch_fake_m(bool rht, bool contig, const QuantParams& p, hipStream_t s) {
-    const dim3 b((p.ngroups + kChunkGroups - 1) / kChunkGroups), t(kThreads);
+    const dim3 t(kThreads);
     if (rht) {
+        const dim3 b((p.ngroups + chunk_groups<FMT, MODE, true>() - 1) / chunk_groups<FMT, MODE, true>());
         if (contig) hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, true, true>), b, t, 0, s, p);
         else hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, true, false>), b, t, 0, s, p);
     } else {
+        const dim3 b((p.ngroups + chunk_groups<FMT, MODE, false>() - 1) / chunk_groups<FMT, MODE, false>());
         if (contig) hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, false, true>), b, t, 0, s, p);
         else hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, false, false>), b, t, 0, s, p);
     }
@@ -441,6 +450,7 @@ hipError_t launch_fake_g(int mode, bool rht, bool contig, const QuantParams& p, 
 
 template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG>
 hipError_t launch_t(const QuantParams& p, hipStream_t s) {
+    constexpr uint32_t kChunkGroups = chunk_groups<FMT, MODE, RHT>();
     const uint32_t blocks = (p.ngroups + kChunkGroups - 1) / kChunkGroups;
     hipLaunchKernelGGL((k_quantize<FMT, GRID, MODE, RHT, EMIT, CONTIG>), dim3(blocks), dim3(kThreads),
                        0, s, p);
@@ -505,8 +515,10 @@ hipError_t launch_grouped_m(int mode, bool rht, bool emit, const GroupedQuantPar
 
 }  // namespace
 
-uint32_t quantize_chunks(uint32_t ngroups) {
-    return (ngroups + kChunkGroups - 1) / kChunkGroups;
+uint32_t quantize_chunks(int format, int mode, bool rht, uint32_t ngroups) {
+    const uint32_t c = format == 1 && mode == MODE_SR && !rht ? chunk_groups<1, MODE_SR, false>()
+                                                              : chunk_groups<0, MODE_RTN, false>();
+    return (ngroups + c - 1) / c;
 }
 
 hipError_t launch_quantize_grouped(int format, int grid, int mode, bool rht, bool emit,
