@@ -280,25 +280,42 @@ __device__ __forceinline__ uint32_t sr_word(uint32_t nw, int j) {
     return __builtin_amdgcn_perm(nw, 0x007FFFFFu, ((4u + (uint32_t)j) << 24) | 0x020100u);
 }
 
-// Slot 1 of the convert uses its random word shifted left by one, so a pair
+// The SR convert of the pair p, written into byte SEL of acc (slot 0's code in
+// the byte's low nibble, slot 1's in its high nibble).  The instruction keeps
+// the other three bytes of its destination (checked on the GPU for every byte
+// position), but the builtin does not model that merge, so the destination is
+// tied here in asm.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_sr_byte(uint32_t acc, v2f p, uint32_t R, float scale) {
+    if constexpr (SEL == 0) asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(acc) : "v"(p), "v"(R), "v"(scale));
+    if constexpr (SEL == 1)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]" : "+v"(acc) : "v"(p), "v"(R), "v"(scale));
+    if constexpr (SEL == 2)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]" : "+v"(acc) : "v"(p), "v"(R), "v"(scale));
+    if constexpr (SEL == 3)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]" : "+v"(acc) : "v"(p), "v"(R), "v"(scale));
+    return acc;
+}
+
+// Slot 1 of the convert uses its random word shifted left by one, so each pair
 // (v[2i], v[2i+1]) is converted twice from one register pair: with R for
-// element 2i (low nibble kept) and with R' >> 1 for element 2i+1 (high nibble
-// kept; bit 0 of R' is below the convert's resolution).  Same exhaustive check
-// as slot 0.  The four pair bytes are then gathered with two byte permutes.
+// element 2i, whose code lands in the low nibble of byte i of e, and with
+// R' >> 1 for element 2i+1, whose code lands in the high nibble of byte i of o
+// (bit 0 of R' is below the convert's resolution; same exhaustive check as
+// slot 0).  The other nibbles hold the other slot's code and are masked off.
 __device__ __forceinline__ uint32_t encode8_sr_e2m1_short(const float v[8], uint32_t rnd0, uint32_t rnd1,
                                                           float scale = 1.0f) {
     const uint32_t n0 = ~rnd0, n1 = ~rnd1;
-    uint32_t b[4];
-    #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t nw = i < 2 ? n0 : n1;
-        v2f x = {v[2 * i], v[2 * i + 1]};
-        const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, sr_word(nw, (2 * i) & 3), scale, 0);
-        const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, x, sr_word(nw, (2 * i + 1) & 3) >> 1,
-                                                                        scale, 0);
-        b[i] = (lo & 0x0Fu) | (hi & ~0x0Fu);  // one bitfield insert; byte 0 is what counts
-    }
-    return __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+    uint32_t e = 0u, o = 0u;
+    e = cvt_sr_byte<0>(e, (v2f){v[0], v[1]}, sr_word(n0, 0), scale);
+    o = cvt_sr_byte<0>(o, (v2f){v[0], v[1]}, sr_word(n0, 1) >> 1, scale);
+    e = cvt_sr_byte<1>(e, (v2f){v[2], v[3]}, sr_word(n0, 2), scale);
+    o = cvt_sr_byte<1>(o, (v2f){v[2], v[3]}, sr_word(n0, 3) >> 1, scale);
+    e = cvt_sr_byte<2>(e, (v2f){v[4], v[5]}, sr_word(n1, 0), scale);
+    o = cvt_sr_byte<2>(o, (v2f){v[4], v[5]}, sr_word(n1, 1) >> 1, scale);
+    e = cvt_sr_byte<3>(e, (v2f){v[6], v[7]}, sr_word(n1, 2), scale);
+    o = cvt_sr_byte<3>(o, (v2f){v[6], v[7]}, sr_word(n1, 3) >> 1, scale);
+    return (e & 0x0F0F0F0Fu) | (o & 0xF0F0F0F0u);
 }
 
 // SR E2M1 of values with any number of significant bits, given as w = 2^23 v.
