@@ -112,6 +112,8 @@ CASES = [
     (0, 0, 0, True, "outlier"),
     (1, 1, 1, True, "outlier"),
     (1, 0, 0, True, "student"),
+    (1, 0, 1, True, "student"),
+    (0, 0, 1, True, "outlier"),
 ]
 
 
