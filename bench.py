@@ -397,24 +397,31 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(args, W, oracle_mod, h, threads=1):
+def cpu_baseline(args, W, oracle_mod, h, threads=1, runs=3):
     """The oracle (unchanged) on rows [0, R) of the headline step, on `threads` host threads with the
-    rows split evenly between them (the oracle's C calls release the interpreter lock)."""
+    rows split evenly between them (the oracle's C calls release the interpreter lock); the median
+    of `runs` timed runs after one untimed run."""
     import concurrent.futures as cf
     R = min(args.cpu_rows, h["rows"])
     cols = h["cols"]
     cuts = [R * k // threads for k in range(threads + 1)]
-    t = time.perf_counter()
-    if threads == 1:
-        _oracle_step_rows(oracle_mod, W, h, 0, R)
-    else:
-        with cf.ThreadPoolExecutor(threads) as ex:
-            list(ex.map(lambda k: _oracle_step_rows(oracle_mod, W, h, cuts[k], cuts[k + 1]), range(threads)))
-    dt = time.perf_counter() - t
+
+    def one():
+        t = time.perf_counter()
+        if threads == 1:
+            _oracle_step_rows(oracle_mod, W, h, 0, R)
+        else:
+            with cf.ThreadPoolExecutor(threads) as ex:
+                list(ex.map(lambda k: _oracle_step_rows(oracle_mod, W, h, cuts[k], cuts[k + 1]), range(threads)))
+        return time.perf_counter() - t
+    one()
+    times = sorted(one() for _ in range(runs))
+    dt = times[len(times) // 2]
     b = sum(h["bytes_per"].values()) * R * cols
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"rows 0..{R} of the 16384x4096 workload ({R * cols} elements), all five kernels "
-                      f"of the step, {threads} thread(s) over row ranges, {dt:.2f} s; host: "
+                      f"of the step, {threads} thread(s) over row ranges; median of {runs} runs after one "
+                      f"untimed run: {dt:.2f} s (runs {', '.join(f'{x:.2f}' for x in times)} s); host: "
                       f"{os.cpu_count()} logical CPUs, {_cpu_model()}"}
 
 

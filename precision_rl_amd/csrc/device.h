@@ -8,12 +8,13 @@
 //                                 the lower bracketing codeword; with a word
 //                                 built from the random byte: stochastic
 //                                 rounding, exact for values with at most 14
-//                                 significant bits (MXFP4 without the RHT)
-// all called with scale 1.0, so the instruction sees the already scaled
-// value RN(y * inv).  Stochastic rounding of other values and the uniform
-// grid are computed with plain fp32/integer arithmetic.  Per-block work (scale codes and
-// reciprocals) is written in ordinary IEEE fp32 (correctly rounded division,
-// denormals kept).
+//                                 significant bits (MXFP4 without the RHT) and
+//                                 for multiples of 2^-23 (every other value is
+//                                 first rounded up in magnitude to one)
+// with a power-of-two scale (1.0, 2^e or 2^23) that the instruction divides
+// by exactly.  The uniform grid is computed with plain fp32/integer
+// arithmetic.  Per-block work (scale codes and reciprocals) is written in
+// ordinary IEEE fp32 (correctly rounded division, denormals kept).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
