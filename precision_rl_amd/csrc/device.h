@@ -341,27 +341,41 @@ __device__ __forceinline__ uint32_t encode1_rtn_uniform(float v) {
     return k | sign_nibble(v);
 }
 
-// SR on the uniform grid: k = ceil(min(|v|, 7) - c), c = (2u+1)/512 (the
-// difference is exact wherever it decides k).  The eight magnitudes are
-// written as bytes straight from the fp32 k (exact integers; odd elements
-// times 16), so one OR packs the nibbles, and the eight sign bits are moved
-// to bit 3 of their nibbles with byte permutes.  A NaN v gives magnitude 0.
-__device__ __forceinline__ uint32_t encode8_sr_uniform(const float v[8], uint32_t rnd0, uint32_t rnd1) {
-    uint32_t e = 0, o = 0;   // bytes k0 k2 k4 k6, and 16 k1 .. 16 k7
+// floor(1/2 - a): v_cvt_rpi_i32_f32 (floor(x + 1/2)) of x = -a, one instruction.
+// Checked against floor in double precision for every fp32 a in [0, 1792].
+__device__ __forceinline__ int32_t floor_half_minus(float a) {
+    int32_t r;
+    asm("v_cvt_rpi_i32_f32_e64 %0, -%1" : "=v"(r) : "v"(a));
+    return r;
+}
+
+// SR on the uniform grid, from w = 256 v: k = ceil(m - c) with m = min(|v|, 7)
+// and c = (u + 1/2)/256.  For integer k, k >= m - c exactly when
+// 256 k + u >= ceil(256 m - 1/2) = E, so k = ceil((E - u)/256) =
+// (E + 255 - u) >> 8, where E = -floor(1/2 - 256 m) is one conversion of
+// 256 m = min(|w|, 1792) and 255 - u is a byte of the inverted random word.
+// The results t = E + 255 - u lie in [0, 2047], so k is byte 1 of t: byte
+// permutes gather the even and the odd elements' k into two words that one
+// shift-or merges into nibbles, and the eight sign bits are moved to bit 3 of
+// their nibbles with byte permutes.  A NaN w gives an unspecified magnitude
+// (callers zero the codes of blocks with a non-finite value).
+__device__ __forceinline__ uint32_t encode8_sr_uniform_w(const float w[8], uint32_t rnd0, uint32_t rnd1) {
+    const uint32_t n0 = ~rnd0, n1 = ~rnd1;   // bytes 255 - u
+    uint32_t t[8];
     #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const uint32_t u = ((j < 4 ? rnd0 : rnd1) >> (8 * (j & 3))) & 0xFFu;
-        const float c = __builtin_fmaf((float)u, 0.00390625f, 0.001953125f);
-        const float k = __builtin_ceilf(__builtin_elementwise_minimum(fabsf(v[j]), 7.0f) - c);
-        if (j & 1) o = __builtin_amdgcn_cvt_pk_u8_f32(k * 16.0f, j >> 1, o);
-        else e = __builtin_amdgcn_cvt_pk_u8_f32(k, j >> 1, e);
+        const uint32_t nu = ((j < 4 ? n0 : n1) >> (8 * (j & 3))) & 0xFFu;
+        const float x = __builtin_elementwise_minimum(fabsf(w[j]), 1792.0f);
+        t[j] = nu - (uint32_t)floor_half_minus(x);
     }
-    const uint32_t* b = reinterpret_cast<const uint32_t*>(v);
+    const uint32_t e = __builtin_amdgcn_perm(t[2], t[0], 0x0C0C0501u) | __builtin_amdgcn_perm(t[6], t[4], 0x05010C0Cu);
+    const uint32_t o = __builtin_amdgcn_perm(t[3], t[1], 0x0C0C0501u) | __builtin_amdgcn_perm(t[7], t[5], 0x05010C0Cu);
+    const uint32_t* b = reinterpret_cast<const uint32_t*>(w);
     // byte 3 of a float holds its sign at bit 7: odd elements' sign bytes into
     // bytes 0..3 give bits 7, 15, 23, 31; even elements', shifted down by 4, bits 3, 11, 19, 27
     const uint32_t so = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0703u) | __builtin_amdgcn_perm(b[7], b[5], 0x07030C0Cu);
     const uint32_t se = (__builtin_amdgcn_perm(b[2], b[0], 0x0C0C0703u) | __builtin_amdgcn_perm(b[6], b[4], 0x07030C0Cu)) >> 4;
-    return (e | o) | (so & 0x80808080u) | (se & 0x08080808u);
+    return ((o << 4) | e) | (so & 0x80808080u) | (se & 0x08080808u);
 }
 
 __device__ __forceinline__ uint32_t encode1_guided_uniform(float v, uint32_t b) {
@@ -394,7 +408,10 @@ __device__ __forceinline__ uint32_t encode8(const float v[8], uint32_t rnd0, uin
         for (int j = 0; j < 8; ++j) w[j] = v[j] * 0x1p23f;   // exact, or an overflow that saturates
         return encode8_sr_e2m1_w(w, rnd0, rnd1);
     } else if constexpr (MODE == MODE_SR) {
-        return encode8_sr_uniform(v, rnd0, rnd1);
+        float w[8];
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = v[j] * 256.0f;   // exact, or an overflow that saturates
+        return encode8_sr_uniform_w(w, rnd0, rnd1);
     } else {
         uint32_t w = 0;
         #pragma unroll
@@ -563,6 +580,22 @@ __device__ __forceinline__ uint32_t dpp_swap1(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t dpp_swap2(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+}
+
+// Pair exchange: lane q of a pair holds a (slot 2k) and b (slot 2k+1) and
+// returns lo = its a (q = 0) or the partner's b (q = 1), hi = the partner's a
+// (q = 0) or its b (q = 1).  Each lane sends the one it gives away (b for
+// q = 0, a for q = 1).  The received value feeds both selects, so the DPP move
+// is computed by every lane: a DPP move placed under a lane-dependent branch
+// would read inactive partner lanes.
+__device__ __forceinline__ void pair_exchange(const uint32_t a[4], const uint32_t b[4], uint32_t q,
+                                              uint32_t lo[4], uint32_t hi[4]) {
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t r = dpp_swap1(q ? a[j] : b[j]);
+        lo[j] = q ? r : a[j];
+        hi[j] = q ? b[j] : r;
+    }
 }
 
 // Largest |bf16| bit pattern of 16 values (8 dwords) with sign bits cleared;

@@ -27,6 +27,18 @@ __device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
     return (uint32_t)((t + n) >> f.l);
 }
 
+// Element offset of half-group hg (logical row-major order) in a tensor with row stride ld.
+template <bool CONTIG>
+__device__ __forceinline__ int64_t half_offset(uint32_t hg, const FastDiv& gpr, int64_t ld) {
+    if constexpr (CONTIG) {
+        return (int64_t)hg * 8;
+    } else {
+        const uint32_t g = hg >> 1;
+        const uint32_t row = fastdiv(g, gpr);
+        return (int64_t)row * ld + (int64_t)(g - row * gpr.d) * 16 + (hg & 1u) * 8;
+    }
+}
+
 // 16-element groups are the work unit: group g covers elements 16g..16g+15 of
 // the logical row-major order (rows*cols/16 groups; a row holds cols/16).
 struct QuantParams {

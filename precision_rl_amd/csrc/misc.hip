@@ -19,9 +19,11 @@ __device__ __forceinline__ int64_t row_offset(uint32_t g, FastDiv gpr, int64_t l
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
-// Each lane keeps kAmaxU groups in flight per iteration of a grid-stride loop;
-// the workgroup reduces in LDS and issues one atomic max, so a launch of at
-// most kAmaxBlocks workgroups makes at most that many same-address atomics.
+// Each lane keeps kAmaxU groups (2 kAmaxU half-groups) in flight per iteration
+// of a grid-stride loop; the workgroup reduces in LDS and issues one atomic
+// max, so a launch of at most kAmaxBlocks workgroups makes at most that many
+// same-address atomics.  (Measured on 512M elements: 4 groups and 1024
+// workgroups beat 2 or 8 groups and 2048 or 4096 workgroups.)
 constexpr int kAmaxU = 4;
 constexpr uint32_t kAmaxBlocks = 1024;
 
@@ -30,39 +32,49 @@ __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
     __shared__ uint32_t red[kThreads / 64];
     uint32_t m = 0;
     const uint32_t signs = RHT ? rht_sign_mask(p.rht_seed) : 0u;
-    const uint32_t chunk = kThreads * kAmaxU;
+    const uint32_t lane = threadIdx.x & 63u, q = lane & 1u;
+    const uint64_t nhg = 2ull * p.ngroups;
+    constexpr int kSlots = 2 * kAmaxU;                 // half-groups per lane and iteration
+    const uint32_t chunk = kThreads * kAmaxU;          // groups per workgroup and iteration
     for (uint32_t base = blockIdx.x * chunk; base < p.ngroups; base += gridDim.x * chunk) {
-        uint32_t w[kAmaxU][8];
+        // slot s of a lane reads half-group hg0 + 64 s, so each load instruction
+        // of a wave covers 64 consecutive half-groups; past the end a lane reads
+        // the last one again
+        const uint64_t hg0 = 2ull * base + (threadIdx.x >> 6) * (64u * kSlots) + lane;
+        uint32_t w[kSlots][4];
         #pragma unroll
-        for (int u = 0; u < kAmaxU; ++u) {
-            const uint32_t g = base + u * kThreads + threadIdx.x;
-            if (g < p.ngroups) {
-                const int64_t off = CONTIG ? (int64_t)g * 16 : row_offset(g, p.gpr, p.ld);
-                const uint4* src = reinterpret_cast<const uint4*>(p.x + off);
-                const uint4 a = src[0], b = src[1];
-                w[u][0] = a.x; w[u][1] = a.y; w[u][2] = a.z; w[u][3] = a.w;
-                w[u][4] = b.x; w[u][5] = b.y; w[u][6] = b.z; w[u][7] = b.w;
-            } else {
-                #pragma unroll
-                for (int j = 0; j < 8; ++j) w[u][j] = 0;
-            }
+        for (int s = 0; s < kSlots; ++s) {
+            const uint64_t hg = min(hg0 + 64u * s, nhg - 1u);
+            load16_nt(p.x + half_offset<CONTIG>((uint32_t)hg, p.gpr, p.ld), w[s]);
         }
         #pragma unroll
         for (int u = 0; u < kAmaxU; ++u) {
             if constexpr (RHT) {
+                // whole groups for the transform: after the exchange of slots 2u
+                // and 2u+1 this lane holds group (hg0 + 128 u + 64 q) / 2, which
+                // counts only if it lies inside the tensor
+                uint32_t gw[8];
+                pair_exchange(w[2 * u], w[2 * u + 1], q, gw, gw + 4);
+                const uint64_t g = (hg0 + 128u * u + 64u * q) >> 1;
                 float a[16];   // the transform before its exact factor 1/4
-                widen16<true, false>(w[u], signs, a);
+                widen16<true, false>(gw, signs, a);
+                uint32_t mg = 0;
                 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const uint32_t k = __float_as_uint(a[j]) & 0x7FFFFFFFu;
-                    m = k < 0x7F800000u ? max(m, k) : m;
+                    mg = k < 0x7F800000u ? max(mg, k) : mg;
                 }
+                m = g < p.ngroups ? max(m, mg) : m;
             } else {
+                // a repeated half-group cannot change the maximum
                 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t lo = w[u][j] & 0x7FFFu, hi = (w[u][j] >> 16) & 0x7FFFu;
-                    m = lo < 0x7F80u ? max(m, lo << 16) : m;
-                    m = hi < 0x7F80u ? max(m, hi << 16) : m;
+                for (int s = 2 * u; s < 2 * u + 2; ++s) {
+                    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t lo = w[s][j] & 0x7FFFu, hi = (w[s][j] >> 16) & 0x7FFFu;
+                        m = lo < 0x7F80u ? max(m, lo << 16) : m;
+                        m = hi < 0x7F80u ? max(m, hi << 16) : m;
+                    }
                 }
             }
         }

@@ -41,34 +41,6 @@ constexpr int halves_per_lane() { return FMT == 1 && MODE == MODE_SR && !RHT ? 2
 template <int FMT, int MODE, bool RHT>
 constexpr uint32_t chunk_groups() { return kThreads * (halves_per_lane<FMT, MODE, RHT>() / 2); }
 
-// Element offset of half-group hg (logical row-major order) in a tensor with row stride ld.
-template <bool CONTIG>
-__device__ __forceinline__ int64_t half_offset(uint32_t hg, const FastDiv& gpr, int64_t ld) {
-    if constexpr (CONTIG) {
-        return (int64_t)hg * 8;
-    } else {
-        const uint32_t g = hg >> 1;
-        const uint32_t row = fastdiv(g, gpr);
-        return (int64_t)row * ld + (int64_t)(g - row * gpr.d) * 16 + (hg & 1u) * 8;
-    }
-}
-
-// Pair exchange: lane q of a pair holds a (slot 2k) and b (slot 2k+1) and
-// returns lo = its a (q = 0) or the partner's b (q = 1), hi = the partner's a
-// (q = 0) or its b (q = 1).  Each lane sends the one it gives away (b for
-// q = 0, a for q = 1).  The received value feeds both selects, so the DPP move
-// is computed by every lane: a DPP move placed under a lane-dependent branch
-// would read inactive partner lanes.
-__device__ __forceinline__ void pair_exchange(const uint32_t a[4], const uint32_t b[4], uint32_t q,
-                                              uint32_t lo[4], uint32_t hi[4]) {
-    #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t r = dpp_swap1(q ? a[j] : b[j]);
-        lo[j] = q ? r : a[j];
-        hi[j] = q ? b[j] : r;
-    }
-}
-
 // Number of nonzero nibbles of w.
 __device__ __forceinline__ uint32_t nonzero_nibbles(uint32_t w) {
     return __builtin_popcount((w | (w >> 1) | (w >> 2) | (w >> 3)) & 0x11111111u);
@@ -236,8 +208,10 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         // bits.  Its E2M1 converts take the inputs and divide by 2^e themselves.
         constexpr bool kShort = FMT == 1 && !RHT;
         constexpr bool kInCvt = kShort && GRID == 0;
-        // E2M1 SR of values with up to 24 significant bits takes w = 2^23 v
+        // E2M1 SR of values with up to 24 significant bits takes w = 2^23 v,
+        // uniform SR takes w = 256 v
         constexpr bool kSrW = GRID == 0 && MODE == MODE_SR && !kShort;
+        constexpr bool kUniSr = GRID == 1 && MODE == MODE_SR;
         float v[16];
         float cscale = 1.0f;
         if constexpr (kInCvt) {
@@ -256,6 +230,19 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
                 const float m = RHT ? inv * 0.25f : inv;   // exact: inv >= 2^100
                 #pragma unroll
                 for (int j = 0; j < 16; ++j) v[j] = (y[j] * m) * 0x1p23f;
+            }
+        } else if constexpr (kUniSr) {
+            // RN(y * inv * 256), or RN(a * inv * 64) with the RHT, equals 256 v
+            // wherever v is normal (smaller v give k = 0 and keep their sign either
+            // way); one product where inv times the power of two is exact and
+            // finite (for NVFP4 with the RHT also inv >= 2^-124, as below)
+            if (inv < 0x1p120f && (FMT == 1 || !RHT || inv >= 0x1p-124f)) {
+                const float m = inv * (RHT ? 64.0f : 256.0f);
+                #pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = y[j] * m;
+            } else {
+                #pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = (RHT ? (y[j] * 0.25f) * inv : y[j] * inv) * 256.0f;
             }
         } else if constexpr (RHT) {
             // v = RN((a/4) * inv) = RN(a * (inv/4)) when inv/4 is exact: always
@@ -282,6 +269,9 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         } else if constexpr (kSrW) {
             c0 = encode8_sr_e2m1_w(v, r0, r1);
             c1 = encode8_sr_e2m1_w(v + 8, r2, r3);
+        } else if constexpr (kUniSr) {
+            c0 = encode8_sr_uniform_w(v, r0, r1);
+            c1 = encode8_sr_uniform_w(v + 8, r2, r3);
         } else {
             c0 = encode8<GRID, MODE, kShort>(v, r0, r1, gb[k] & 0xFFu, cscale);
             c1 = encode8<GRID, MODE, kShort>(v + 8, r2, r3, gb[k] >> 8, cscale);
@@ -404,9 +394,8 @@ __global__ void k_zero_counts(unsigned long long* c) {
 
 template <int FMT, int GRID>
 hipError_t launch_mismatch_g(bool rht, bool contig, const QuantParams& p, hipStream_t s) {
-    constexpr uint32_t kChunkGroups = chunk_groups<FMT, MODE_GUIDED, false>();
-    static_assert(chunk_groups<FMT, MODE_GUIDED, true>() == kChunkGroups, "one chunk size for the diagnostic");
-    const uint32_t chunks = (p.ngroups + kChunkGroups - 1) / kChunkGroups;
+    const uint32_t cg = rht ? chunk_groups<FMT, MODE_GUIDED, true>() : chunk_groups<FMT, MODE_GUIDED, false>();
+    const uint32_t chunks = (p.ngroups + cg - 1) / cg;
     const dim3 b(chunks < kMismatchBlocks ? chunks : kMismatchBlocks), t(kThreads);
     if (rht) {
         if (contig) hipLaunchKernelGGL((k_guide_mismatch<FMT, GRID, true, true>), b, t, 0, s, p, chunks);

@@ -498,6 +498,29 @@ def test_rht16_vs_oracle(fq, inverse, bf16, pad):
     assert (g == want.view(np.int16 if bf16 else np.int32)).all()
 
 
+@pytest.mark.parametrize("rht", [False, True])
+@pytest.mark.parametrize("shape,pad", [((3, 16), 0), ((5, 48), 8), ((129, 96), 0), ((1, 16 * 1027), 0)])
+def test_tensor_scale_ragged_tail(fq, rht, shape, pad):
+    # Lanes past the end of the tensor read its last half-group (8 elements)
+    # again.  Here the last group is 8 zeros and then the only large values, so
+    # that half-group doubled would transform to a larger maximum than any real
+    # group: the tensor scale must come from real groups only.
+    rows, cols = shape
+    rng = np.random.default_rng(rows * cols)
+    xf = (rng.standard_normal((rows, cols)) * 1e-3).astype(np.float32)
+    xf[-1, -16:-8] = 0.0
+    xf[-1, -8:] = 3.0
+    xh = W.f32_to_bf16_rne(xf)
+    cfg = fq.Fp4Config(rht16=rht, rht_seed=7)
+    oc = ocfg(cfg)
+    if rht:   # the doubled half-group would indeed give a larger amax than the real last group
+        real = O.rht16(xh[-1:, -16:], 7)
+        fake = O.rht16(np.concatenate([xh[-1, -8:], xh[-1, -8:]])[None, :], 7)
+        assert np.abs(fake).max() > np.abs(real).max()
+    ts = fq.fp4_tensor_scale(dev(xh, pad), cfg)
+    assert f32_bits(host(ts))[0] == f32_bits([O.tensor_scale(oc, xh)])[0]
+
+
 def test_empty_inputs(fq):
     cfg = fq.Fp4Config()
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
