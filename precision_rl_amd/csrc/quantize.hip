@@ -11,11 +11,12 @@
 // G is the pair of slots' first group.  Each lane then works on whole groups:
 // the NVFP4 block, the Philox block of stochastic rounding and the RHT all
 // stay inside the lane, and an MXFP4 block is two lanes apart (quad_perm
-// [2,3,0,1]).  Stores: codes are 8 bytes per lane and the guide bits 2 bytes,
+// [2,3,0,1]; adjacent lanes after the LDS transpose of the RHT kernels).  Stores: codes are 8 bytes per lane and the guide bits 2 bytes,
 // both covering contiguous runs per wave; the bf16 output of fake quantization
 // is transposed back and stored per half-group like the loads.  Every lane
 // runs every DPP step (only stores are predicated).  Kernels with the RHT are
-// bound by arithmetic; they load each group directly and skip the exchange.
+// bound by arithmetic: they load the same way but transpose through LDS, so
+// that lane l owns groups W + l and W + 64 + l of its wave's groups W ...
 //
 // Per block (scale) [FQT-FP4 §3; TETRAJET §3; TRACE-JA "TRACEの仕組み"]:
 //   NVFP4 scale code = E4M3 RNE of amax / RN(Gmax*s_t) (clamped to 448),
@@ -57,6 +58,13 @@ __device__ __forceinline__ void build_inv_table(float* tab, const float* ts) {
     }
 }
 
+// LDS for the RHT kernels' slot transpose: 4 KiB per wave, one array per kernel
+// however many times quantize_chunk is instantiated in it.
+__device__ __forceinline__ v4u32* rht_transpose_lds() {
+    __shared__ v4u32 xt[kThreads / 64 * 256];
+    return xt;
+}
+
 // One workgroup's share (kChunkGroups groups starting at chunk `wg`) of one tensor.
 // OUT = 0 stores codes, scales (and emitted guide bits); OUT = 1 stores the
 // dequantized bf16 values instead (fake quantization); OUT = 2 (guided only)
@@ -77,26 +85,21 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     // half-group of slot s: hg0 + 64 s; group owned after transposing slots 2k, 2k+1: gk(k)
     const uint32_t hg0 = wg * (2u * kChunkGroups) + (threadIdx.x >> 6) * (64u * kH) + lane;
     const uint32_t nhg = 2u * p.ngroups;
-    auto gk = [&](int k) { return (hg0 + 128u * k + 64u * q) >> 1; };
+    // With the RHT the slots go through LDS (see below) and lane l then owns
+    // groups W + l and W + 64 + l of its wave's 128 groups W ..; otherwise the
+    // DPP pair exchange gives lane 2m groups G + m and lane 2m+1 groups G + 32 + m
+    // for each pair of slots.
+    auto gk = [&](int k) {
+        return RHT ? ((hg0 - lane) >> 1) + 64u * k + lane : (hg0 + 128u * k + 64u * q) >> 1;
+    };
 
     // Lanes past the end load the last half-group instead (in bounds, no
-    // branch); their results are never stored.  With the RHT the kernel is
-    // bound by arithmetic, not by memory, so each lane loads its own groups
-    // directly (two 16-byte loads each) and skips the pair exchange.
+    // branch); their results are never stored.
     uint32_t w[kH][4];
-    if constexpr (RHT) {
-        #pragma unroll
-        for (int k = 0; k < kG; ++k) {
-            const uint32_t g = min(gk(k), p.ngroups - 1u);
-            load16_nt(p.x + half_offset<CONTIG>(2u * g, p.gpr, p.ld), w[2 * k]);
-            load16_nt(p.x + half_offset<CONTIG>(2u * g + 1u, p.gpr, p.ld), w[2 * k + 1]);
-        }
-    } else {
-        #pragma unroll
-        for (int s = 0; s < kH; ++s) {
-            const uint32_t hg = min(hg0 + 64u * s, nhg - 1u);
-            load16_nt(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld), w[s]);
-        }
+    #pragma unroll
+    for (int s = 0; s < kH; ++s) {
+        const uint32_t hg = min(hg0 + 64u * s, nhg - 1u);
+        load16_nt(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld), w[s]);
     }
     uint32_t gb[kG], gs[kG];
     v2u32 rc[kG];
@@ -128,6 +131,31 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         // within 3 fp32 steps of it whenever 1/denom is a normal number
         rden = 1.0f / denom;
         rden_ok = denom >= 0x1p-125f && denom <= 0x1p125f;
+    }
+    if constexpr (RHT) {
+        // The RHT kernels are bound by arithmetic: the slots go through LDS,
+        // which costs no VALU instructions, instead of the DPP exchange.  Half-
+        // group h of the wave goes to (h & 1) * 2048 + (h >> 1) * 16, so lane l
+        // then reads groups l and 64 + l as two 16-byte pieces each; the writes
+        // and the reads both touch consecutive 16-byte slots.  The wave's own
+        // LDS operations complete in order, so it needs no workgroup barrier.
+        static_assert(kH == 4, "the LDS transpose assumes four slots");
+        char* base = reinterpret_cast<char*>(rht_transpose_lds() + (threadIdx.x >> 6) * 256);
+        char* wp = base + (lane & 1u) * 2048u + (lane >> 1) * 16u;
+        #pragma unroll
+        for (int s = 0; s < kH; ++s)
+            *reinterpret_cast<v4u32*>(wp + 512 * s) = (v4u32){w[s][0], w[s][1], w[s][2], w[s][3]};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        char* rp = base + lane * 16u;
+        #pragma unroll
+        for (int k = 0; k < kG; ++k) {
+            const v4u32 a = *reinterpret_cast<const v4u32*>(rp + 1024 * k);
+            const v4u32 b = *reinterpret_cast<const v4u32*>(rp + 2048 + 1024 * k);
+            w[2 * k][0] = a.x; w[2 * k][1] = a.y; w[2 * k][2] = a.z; w[2 * k][3] = a.w;
+            w[2 * k + 1][0] = b.x; w[2 * k + 1][1] = b.y; w[2 * k + 1][2] = b.z; w[2 * k + 1][3] = b.w;
+        }
     }
     // MXFP4 RTN and guided without the RHT convert straight from the bf16 bits;
     // every other path widens the values, and then takes the amax in fp32
@@ -162,7 +190,9 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         } else {
             amax_key = amax_bits16(gw) << 16;
         }
-        if constexpr (FMT == 1) amax_key = max(amax_key, dpp_swap2(amax_key));
+        // an MXFP4 block is groups 2b and 2b+1: in lanes l and l ^ 1 after the LDS
+        // transpose (RHT), in lanes l and l ^ 2 after the pair exchange
+        if constexpr (FMT == 1) amax_key = max(amax_key, RHT ? dpp_swap1(amax_key) : dpp_swap2(amax_key));
         bool finite = amax_key < 0x7F800000u;
 
         uint32_t sc;
