@@ -41,6 +41,12 @@ constexpr int halves_per_lane() { return FMT == 1 && MODE == MODE_SR && !RHT ? 2
 // Groups per workgroup.
 template <int FMT, int MODE, bool RHT>
 constexpr uint32_t chunk_groups() { return kThreads * (halves_per_lane<FMT, MODE, RHT>() / 2); }
+// A single-tensor launch that would have fewer workgroups than this (8 per
+// compute unit) uses two slots instead of four: twice the workgroups, so more
+// loads in flight across the chip (measured on 4096 x 2048 NVFP4: RTN 5.35
+// against 5.78 us, guided 5.82 against 6.56 us; four slots stay faster on
+// large tensors and in the grouped launches).
+constexpr uint32_t kSmallLaunchBlocks = 2048;
 
 // Number of nonzero nibbles of w.
 __device__ __forceinline__ uint32_t nonzero_nibbles(uint32_t w) {
@@ -72,13 +78,14 @@ __device__ __forceinline__ v4u32* rht_transpose_lds() {
 // storing anything, how often the guided result differs from those codes.
 // tab: LDS space for the NVFP4 reciprocal table, which the chunk builds once its
 // loads are in flight (OUT = 2: the caller has built it).
-template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG, int OUT = 0>
+template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG, int OUT = 0,
+          int KH = halves_per_lane<FMT, MODE, RHT>()>
 __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg, float* tab,
                                                uint32_t* acc = nullptr) {
     constexpr float kGmax = GRID == 0 ? 6.0f : 7.0f;
-    constexpr int kH = halves_per_lane<FMT, MODE, RHT>();
+    constexpr int kH = KH;
     constexpr int kG = kH / 2;                                      // whole groups per lane
-    constexpr uint32_t kChunkGroups = chunk_groups<FMT, MODE, RHT>();
+    constexpr uint32_t kChunkGroups = kThreads * kG;
     static_assert(kH >= 2 && kH % 2 == 0, "half-groups per lane must be even");
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t q = lane & 1u;
@@ -356,10 +363,10 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     }
 }
 
-template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG>
+template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG, int KH>
 __global__ __launch_bounds__(kThreads) void k_quantize(const QuantParams p) {
     __shared__ float tab[128];
-    quantize_chunk<FMT, GRID, MODE, RHT, EMIT, CONTIG>(p, blockIdx.x, tab);
+    quantize_chunk<FMT, GRID, MODE, RHT, EMIT, CONTIG, 0, KH>(p, blockIdx.x, tab);
 }
 
 // Several tensors with one configuration in one launch: workgroup b belongs to
@@ -469,9 +476,18 @@ hipError_t launch_fake_g(int mode, bool rht, bool contig, const QuantParams& p, 
 
 template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG>
 hipError_t launch_t(const QuantParams& p, hipStream_t s) {
+    constexpr int kH = halves_per_lane<FMT, MODE, RHT>();
     constexpr uint32_t kChunkGroups = chunk_groups<FMT, MODE, RHT>();
     const uint32_t blocks = (p.ngroups + kChunkGroups - 1) / kChunkGroups;
-    hipLaunchKernelGGL((k_quantize<FMT, GRID, MODE, RHT, EMIT, CONTIG>), dim3(blocks), dim3(kThreads),
+    if constexpr (kH == 4 && !RHT) {   // the RHT kernels' LDS transpose is written for four slots
+        if (blocks < kSmallLaunchBlocks) {
+            const uint32_t b2 = (p.ngroups + kThreads - 1) / kThreads;
+            hipLaunchKernelGGL((k_quantize<FMT, GRID, MODE, RHT, EMIT, CONTIG, 2>), dim3(b2), dim3(kThreads),
+                               0, s, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((k_quantize<FMT, GRID, MODE, RHT, EMIT, CONTIG, kH>), dim3(blocks), dim3(kThreads),
                        0, s, p);
     return hipGetLastError();
 }

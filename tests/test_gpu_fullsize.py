@@ -189,3 +189,33 @@ def test_c5_uniform_rht16_sr_65536x8192(fq):
     idx = sample_rows(rows, k=32)
     check_rows(fq, cfg, O.SR, xh, c, s, o_ts, idx, tag="c5")
     say(f"C5 bit-exact on {len(idx)} rows ({time.time() - t:.1f} s)")
+
+
+@pytest.mark.parametrize("rows", [8191, 8192])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_both_slot_counts_at_the_small_launch_threshold(fq, fmt, rows):
+    # A single-tensor launch below 2048 workgroups of four slots takes two slots
+    # per lane: 8191 x 2048 (NVFP4: 2047 workgroups of four) launches two, 8192 x 2048
+    # launches four.  Both equal the oracle in every mode, on the whole tensor.
+    cols = 2048
+    say("slot threshold", fmt, rows, cols)
+    xh = W.c1_x(rows, cols, seed=21)
+    xrh = W.c1_rollout(rows, cols, seed=21)
+    cfg = fq.Fp4Config(format=fmt)
+    oc = O.Cfg(format=fmt)
+    x, xr = dev(xh), dev(xrh)
+    ts_t = fq.fp4_tensor_scale(xr, cfg) if fmt == 0 else None
+    ts = O.tensor_scale(oc, xrh) if fmt == 0 else 1.0
+    if fmt == 0:
+        assert f32bits(ts_t.item()) == f32bits(ts)
+    rc, rs, rb = fq.fp4_quantize(xr, cfg, ts_t, emit=True)
+    o_rc, o_rs, o_rb = O.quantize(oc, O.RTN, xrh, ts, emit=True)
+    assert (rc.cpu().numpy() == o_rc).all() and (rs.cpu().numpy() == o_rs).all()
+    assert (rb.cpu().numpy() == o_rb).all()
+    gc, gs = fq.fp4_quantize_guided(x, cfg, rb, rs, ts_t)
+    o_gc, o_gs = O.quantize(oc, O.GUIDED, xh, ts, guide_bits=o_rb, guide_scales=o_rs)
+    assert (gc.cpu().numpy() == o_gc).all() and (gs.cpu().numpy() == o_gs).all()
+    scfg = fq.Fp4Config(format=fmt, rounding=fq.SR, sr_seed=5, sr_offset=9)
+    sc, ss = fq.fp4_quantize(x, scfg, ts_t)
+    o_sc, o_ss = O.quantize(O.Cfg(format=fmt, sr_seed=5, sr_offset=9), O.SR, xh, ts)
+    assert (sc.cpu().numpy() == o_sc).all() and (ss.cpu().numpy() == o_ss).all()
