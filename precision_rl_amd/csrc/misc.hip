@@ -19,23 +19,28 @@ __device__ __forceinline__ int64_t row_offset(uint32_t g, FastDiv gpr, int64_t l
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
-// Each lane keeps kAmaxU groups (2 kAmaxU half-groups) in flight per iteration
-// of a grid-stride loop; the workgroup reduces in LDS and issues one atomic
-// max, so a launch of at most kAmaxBlocks workgroups makes at most that many
-// same-address atomics.  (Measured on 512M elements: 4 groups and 1024
-// workgroups beat 2 or 8 groups and 2048 or 4096 workgroups.)
+// Each lane keeps U groups (2U half-groups) in flight per iteration of a
+// grid-stride loop; the workgroup reduces in LDS and issues one atomic max, so
+// a launch of at most kAmaxBlocks workgroups makes at most that many
+// same-address atomics.  Those are device-scope, across the XCDs, and cost
+// roughly 10-15 ns each: a tensor that fits one pass of 1024 workgroups of
+// 4 groups per lane takes 8 groups per lane instead, with half the workgroups
+// (4096 x 2048: 10.2 against 12.6 us for the whole tensor scale).  Larger
+// tensors keep 4 groups and 1024 workgroups (measured on 512M elements against
+// 2 or 8 groups and 256 to 4096 workgroups).
 constexpr int kAmaxU = 4;
+constexpr int kAmaxUSmall = 8;
 constexpr uint32_t kAmaxBlocks = 1024;
 
-template <bool RHT, bool CONTIG>
+template <bool RHT, bool CONTIG, int U>
 __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
     __shared__ uint32_t red[kThreads / 64];
     uint32_t m = 0;
     const uint32_t signs = RHT ? rht_sign_mask(p.rht_seed) : 0u;
     const uint32_t lane = threadIdx.x & 63u, q = lane & 1u;
     const uint64_t nhg = 2ull * p.ngroups;
-    constexpr int kSlots = 2 * kAmaxU;                 // half-groups per lane and iteration
-    const uint32_t chunk = kThreads * kAmaxU;          // groups per workgroup and iteration
+    constexpr int kSlots = 2 * U;                 // half-groups per lane and iteration
+    const uint32_t chunk = kThreads * U;          // groups per workgroup and iteration
     for (uint32_t base = blockIdx.x * chunk; base < p.ngroups; base += gridDim.x * chunk) {
         // slot s of a lane reads half-group hg0 + 64 s, so each load instruction
         // of a wave covers 64 consecutive half-groups; past the end a lane reads
@@ -48,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
             load16_nt(p.x + half_offset<CONTIG>((uint32_t)hg, p.gpr, p.ld), w[s]);
         }
         #pragma unroll
-        for (int u = 0; u < kAmaxU; ++u) {
+        for (int u = 0; u < U; ++u) {
             if constexpr (RHT) {
                 // whole groups for the transform: after the exchange of slots 2u
                 // and 2u+1 this lane holds group (hg0 + 128 u + 64 q) / 2, which
@@ -327,15 +332,25 @@ inline uint32_t blocks_for(uint32_t n) { return (n + kThreads - 1) / kThreads; }
 
 hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams& p, hipStream_t s) {
     hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, reinterpret_cast<uint32_t*>(p.acc), 0u);
-    uint32_t blocks = (p.ngroups + kThreads * kAmaxU - 1) / (kThreads * kAmaxU);
-    if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
-    if (blocks > 0) {
+    if (p.ngroups <= kAmaxBlocks * kThreads * kAmaxU) {   // one pass: the small-tensor shape
+        const uint32_t blocks = (p.ngroups + kThreads * kAmaxUSmall - 1) / (kThreads * kAmaxUSmall);
+        if (blocks > 0) {
+            if (rht) {
+                if (contig) hipLaunchKernelGGL((k_amax<true, true, kAmaxUSmall>), dim3(blocks), dim3(kThreads), 0, s, p);
+                else hipLaunchKernelGGL((k_amax<true, false, kAmaxUSmall>), dim3(blocks), dim3(kThreads), 0, s, p);
+            } else {
+                if (contig) hipLaunchKernelGGL((k_amax<false, true, kAmaxUSmall>), dim3(blocks), dim3(kThreads), 0, s, p);
+                else hipLaunchKernelGGL((k_amax<false, false, kAmaxUSmall>), dim3(blocks), dim3(kThreads), 0, s, p);
+            }
+        }
+    } else {
+        const uint32_t blocks = kAmaxBlocks;
         if (rht) {
-            if (contig) hipLaunchKernelGGL((k_amax<true, true>), dim3(blocks), dim3(kThreads), 0, s, p);
-            else hipLaunchKernelGGL((k_amax<true, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+            if (contig) hipLaunchKernelGGL((k_amax<true, true, kAmaxU>), dim3(blocks), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((k_amax<true, false, kAmaxU>), dim3(blocks), dim3(kThreads), 0, s, p);
         } else {
-            if (contig) hipLaunchKernelGGL((k_amax<false, true>), dim3(blocks), dim3(kThreads), 0, s, p);
-            else hipLaunchKernelGGL((k_amax<false, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+            if (contig) hipLaunchKernelGGL((k_amax<false, true, kAmaxU>), dim3(blocks), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((k_amax<false, false, kAmaxU>), dim3(blocks), dim3(kThreads), 0, s, p);
         }
     }
     hipLaunchKernelGGL(k_ts_finalize, dim3(1), dim3(1), 0, s, p.acc, grid == 0 ? 2688.0f : 3136.0f);
