@@ -149,6 +149,11 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         static_assert(kH == 4, "the LDS transpose assumes four slots");
         char* base = reinterpret_cast<char*>(rht_transpose_lds() + (threadIdx.x >> 6) * 256);
         char* wp = base + (lane & 1u) * 2048u + (lane >> 1) * 16u;
+        // the diagnostic kernel calls this once per chunk: the previous chunk's
+        // reads come before these writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         #pragma unroll
         for (int s = 0; s < kH; ++s)
             *reinterpret_cast<v4u32*>(wp + 512 * s) = (v4u32){w[s][0], w[s][1], w[s][2], w[s][3]};

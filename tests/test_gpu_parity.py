@@ -408,6 +408,28 @@ def test_guide_mismatch_vs_oracle(fq, fmt, grid, rht, shape, pad):
     assert want[1] > 0
 
 
+@pytest.mark.parametrize("fmt,grid,rht", [(0, 1, True), (1, 0, True), (0, 0, False)])
+def test_guide_mismatch_several_chunks_per_workgroup(fq, fmt, grid, rht):
+    # More chunks than the diagnostic's 1024 workgroups: each workgroup walks
+    # several, reusing its LDS (the RHT transpose) and its counters.
+    rows, cols = 1088, 8192   # 557,056 groups: 1088 chunks of 512
+    x_h = W.c1_x(rows, cols, seed=3)
+    xr_h = W.c1_rollout(rows, cols, seed=3)
+    xr_h[::5] = W.f32_to_bf16_rne(W.bf16_to_f32(x_h[::5]) * np.float32(1.7))
+    cfg = fq.Fp4Config(format=fmt, grid=grid, rht16=rht, rht_seed=7)
+    oc = ocfg(cfg)
+    xr = dev(xr_h)
+    ts_t = fq.fp4_tensor_scale(xr, cfg) if fmt == 0 else None
+    ts = O.tensor_scale(oc, xr_h) if fmt == 0 else 1.0
+    rc, rs = fq.fp4_quantize(xr, cfg, ts_t)
+    o_rc, o_rs = O.quantize(oc, O.RTN, xr_h, ts)
+    assert (host(rc) == o_rc).all() and (host(rs) == o_rs).all()
+    counts = fq.fp4_guide_mismatch(dev(x_h), cfg, rc, rs, ts_t)
+    want = O.guide_mismatch(oc, x_h, ts, o_rc, o_rs)
+    assert tuple(int(v) for v in host(counts)) == want
+    assert want[1] > 0
+
+
 def test_guide_mismatch_bracket_cases_and_empty(fq):
     cases = [(2.4, 5), (2.4, 6), (2.4, 0xD), (2.0, 5), (2.0, 4), (-0.3, 9), (0.3, 8), (7.0, 6)] + [(1.0, 2)] * 8
     x = np.array([[v for v, _ in cases] * 3], dtype=np.float32)
