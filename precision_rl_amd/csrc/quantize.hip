@@ -125,7 +125,7 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             gs[k] = p.gscales[FMT == 0 ? g : (g >> 1)];
         }
     }
-    uint32_t n_elem = 0, n_nonadj = 0, n_mism = 0;   // OUT == 2
+    uint32_t n_skip = 0, n_nonadj = 0, n_mism = 0;   // OUT == 2
 
     const uint32_t signs = RHT ? rht_sign_mask(p.rht_seed) : 0u;   // uniform: scalar unit
     float ts = 1.0f, denom = 1.0f, rden = 0.0f;
@@ -321,11 +321,14 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         if (!finite) { c0 = 0; c1 = 0; }
 
         if constexpr (OUT == 2) {
-            if (finite && g < p.ngroups) {   // blocks guided rounding encodes
-                const uint32_t d0 = c0 ^ rc[k].x, d1 = c1 ^ rc[k].y;
-                n_elem += 16u;
-                n_nonadj += nonzero_nibbles(d0 & 0x77777777u) + nonzero_nibbles(d1 & 0x77777777u);
-                n_mism += nonzero_nibbles(d0) + nonzero_nibbles(d1);
+            if (g < p.ngroups) {
+                if (finite) {   // blocks guided rounding encodes
+                    const uint32_t d0 = c0 ^ rc[k].x, d1 = c1 ^ rc[k].y;
+                    n_nonadj += nonzero_nibbles(d0 & 0x77777777u) + nonzero_nibbles(d1 & 0x77777777u);
+                    n_mism += nonzero_nibbles(d0) + nonzero_nibbles(d1);
+                } else {
+                    n_skip += 16u;
+                }
             }
         } else if constexpr (OUT == 1) {
             float dv[16];
@@ -362,7 +365,7 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     }
 
     if constexpr (OUT == 2) {
-        acc[0] += n_elem;
+        acc[0] += n_skip;
         acc[1] += n_nonadj;
         acc[2] += n_mism;
     }
@@ -399,8 +402,11 @@ hipError_t launch_grouped_t(const GroupedQuantParams& gp, hipStream_t s) {
 }
 
 // At most kMismatchBlocks workgroups, each looping over chunks with its counts
-// in registers, then one atomic per counter and workgroup: thousands of
-// same-address atomics (one per chunk) would serialize and dominate.
+// in registers, then at most one atomic per counter and workgroup: thousands
+// of same-address atomics (one per chunk) would serialize and dominate.  The
+// element count starts at the whole tensor and workgroups subtract the
+// elements of blocks guided rounding does not encode, so, like the other two
+// counts, it takes an atomic only where something is counted.
 constexpr uint32_t kMismatchBlocks = 1024;
 
 template <int FMT, int GRID, bool RHT, bool CONTIG>
@@ -425,13 +431,13 @@ __global__ __launch_bounds__(kThreads) void k_guide_mismatch(const QuantParams p
         unsigned long long t = 0;
         #pragma unroll
         for (int wv = 0; wv < kThreads / 64; ++wv) t += red[threadIdx.x][wv];
-        if (t) atomicAdd(p.counts + threadIdx.x, t);
+        if (t) atomicAdd(p.counts + threadIdx.x, threadIdx.x == 0 ? 0ull - t : t);   // count 0: subtract
     }
 }
 
-// Clears the three diagnostic counters (vector stores, one lane each).
-__global__ void k_zero_counts(unsigned long long* c) {
-    if (threadIdx.x < 3) c[threadIdx.x] = 0ull;
+// Sets the three diagnostic counters to (all elements, 0, 0) (vector stores, one lane each).
+__global__ void k_zero_counts(unsigned long long* c, unsigned long long elements) {
+    if (threadIdx.x < 3) c[threadIdx.x] = threadIdx.x == 0 ? elements : 0ull;
 }
 
 template <int FMT, int GRID>
@@ -572,7 +578,7 @@ hipError_t launch_quantize_grouped(int format, int grid, int mode, bool rht, boo
 }
 
 hipError_t launch_guide_mismatch(int format, int grid, bool rht, bool contig, const QuantParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(64), 0, s, p.counts);
+    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(64), 0, s, p.counts, 16ull * p.ngroups);
     if (p.ngroups == 0) return hipGetLastError();
     if (format == 0) {
         return grid == 0 ? launch_mismatch_g<0, 0>(rht, contig, p, s) : launch_mismatch_g<0, 1>(rht, contig, p, s);
