@@ -101,6 +101,17 @@ __global__ void k_ts_finalize(float* acc, float gmax448) {
     *acc = a == 0.0f ? 1.0f : a / gmax448;
 }
 
+template <int U>
+void launch_amax(bool rht, bool contig, uint32_t blocks, const AmaxParams& p, hipStream_t s) {
+    if (rht) {
+        if (contig) hipLaunchKernelGGL((k_amax<true, true, U>), dim3(blocks), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_amax<true, false, U>), dim3(blocks), dim3(kThreads), 0, s, p);
+    } else {
+        if (contig) hipLaunchKernelGGL((k_amax<false, true, U>), dim3(blocks), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_amax<false, false, U>), dim3(blocks), dim3(kThreads), 0, s, p);
+    }
+}
+
 // ---------------------------------------------------------------- dequantize
 // Work unit: 16 bytes of output, i.e. 8 elements to bf16 (one dword of codes)
 // or 4 elements to fp32 (16 bits of codes).  In each of its kDqSlots slots the
@@ -332,26 +343,11 @@ inline uint32_t blocks_for(uint32_t n) { return (n + kThreads - 1) / kThreads; }
 
 hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams& p, hipStream_t s) {
     hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, reinterpret_cast<uint32_t*>(p.acc), 0u);
-    if (p.ngroups <= kAmaxBlocks * kThreads * kAmaxU) {   // one pass: the small-tensor shape
+    if (p.ngroups <= kAmaxBlocks * kThreads * kAmaxU) {   // fits one pass: the small-tensor shape
         const uint32_t blocks = (p.ngroups + kThreads * kAmaxUSmall - 1) / (kThreads * kAmaxUSmall);
-        if (blocks > 0) {
-            if (rht) {
-                if (contig) hipLaunchKernelGGL((k_amax<true, true, kAmaxUSmall>), dim3(blocks), dim3(kThreads), 0, s, p);
-                else hipLaunchKernelGGL((k_amax<true, false, kAmaxUSmall>), dim3(blocks), dim3(kThreads), 0, s, p);
-            } else {
-                if (contig) hipLaunchKernelGGL((k_amax<false, true, kAmaxUSmall>), dim3(blocks), dim3(kThreads), 0, s, p);
-                else hipLaunchKernelGGL((k_amax<false, false, kAmaxUSmall>), dim3(blocks), dim3(kThreads), 0, s, p);
-            }
-        }
+        if (blocks > 0) launch_amax<kAmaxUSmall>(rht, contig, blocks, p, s);
     } else {
-        const uint32_t blocks = kAmaxBlocks;
-        if (rht) {
-            if (contig) hipLaunchKernelGGL((k_amax<true, true, kAmaxU>), dim3(blocks), dim3(kThreads), 0, s, p);
-            else hipLaunchKernelGGL((k_amax<true, false, kAmaxU>), dim3(blocks), dim3(kThreads), 0, s, p);
-        } else {
-            if (contig) hipLaunchKernelGGL((k_amax<false, true, kAmaxU>), dim3(blocks), dim3(kThreads), 0, s, p);
-            else hipLaunchKernelGGL((k_amax<false, false, kAmaxU>), dim3(blocks), dim3(kThreads), 0, s, p);
-        }
+        launch_amax<kAmaxU>(rht, contig, kAmaxBlocks, p, s);
     }
     hipLaunchKernelGGL(k_ts_finalize, dim3(1), dim3(1), 0, s, p.acc, grid == 0 ? 2688.0f : 3136.0f);
     return hipGetLastError();
