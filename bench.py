@@ -26,8 +26,9 @@ serving re-reads across steps.
 Per kernel, two durations are reported: with events around every launch inside
 the steps, and as back-to-back launches of that kernel alone (events around
 the loop).  The roofline entry is for the kernel with the largest share of the
-step (per-launch events); its achieved rate uses the back-to-back duration,
-which compares directly with rocprofv3's kernel durations.  Means come with the 10th, 50th and 90th
+step, by its back-to-back duration, which compares directly with rocprofv3's
+kernel durations; a second entry covers the largest workload's quantize kernel
+(uniform grid + RHT16 + SR, 65536x8192).  Means come with the 10th, 50th and 90th
 percentiles of single launches (and of single steps).  The other workloads (NVFP4 activation 4096x2048,
 KV cache at 131072 tokens, one deep guidance-cache layer, uniform grid + RHT16
 + SR on a 65536x8192 GEMM operand) are timed back to back and reported under
@@ -39,6 +40,7 @@ headline step, on one host thread and on all host threads of one GPU's share
 (at most 16, rows split between them).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--streams 1|2]
+                       [--workload all|c1|c3|c4|c5|gemm]
 """
 from __future__ import annotations
 
@@ -70,8 +72,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2))
     ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
-    ap.add_argument("--gemm-only", action="store_true",
-                    help="only the MXFP4 matrix product workload (one JSON line of its figures)")
+    ap.add_argument("--gemm-only", action="store_true", help="same as --workload gemm")
+    ap.add_argument("--workload", default="all", choices=("all", "c1", "c3", "c4", "c5", "gemm"),
+                    help="all: the headline step, then every other workload; otherwise only that workload "
+                         "(one JSON line of its figures, for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the CPU-baseline sample")
     ap.add_argument("--config-iters", type=int, default=100)
@@ -434,12 +438,14 @@ def mismatch_counts(fq, x, cfg, rcodes, rscales, ts):
             "non_adjacent_frac": nonadj / max(n, 1), "mismatched_frac": mism / max(n, 1)}
 
 
-def other_workloads(args, fq, torch, W, ceiling):
-    res = {}
-    it = args.config_iters
-    u8 = lambda k: torch.empty(k, dtype=torch.uint8, device="cuda")
+def _u8(torch):
+    return lambda k: torch.empty(k, dtype=torch.uint8, device="cuda")
 
-    # NVFP4 activation 4096x2048 (16 MiB): a pool of 32 copies keeps it out of the caches
+
+def wl_c1(args, fq, torch, W, ceiling):
+    """NVFP4 activation 4096x2048 (16 MiB): a pool of 32 copies keeps it out of the caches."""
+    it = args.config_iters
+    u8 = _u8(torch)
     rows, cols = W.c1_shape()
     n = rows * cols
     log("NVFP4 activation 4096x2048 ...")
@@ -482,10 +488,38 @@ def other_workloads(args, fq, torch, W, ceiling):
                         lambda: same(*zip((oc, os_), fq.fp4_quantize_guided(xs[last], cfg, guides[last][2],
                                                                              guides[last][1], tss[last]))))
     r["quantize_guided_graph"] = dict(report(ms, 2.75 * n, n, ceiling), replays_match_eager=ok)
-    res["nvfp4_act_4096x2048"] = r
-    del xs, xrs, guides
+    # the tensor scale in one launch (workspace), alone and followed by the RTN quantize that uses it:
+    # end to end, both passes over x (2 + 2.5625 bytes per element)
+    ws = fq.tensor_scale_workspace()
+    ts1 = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(P)]
+    ms, ok = graph_time(torch, lambda i: fq.fp4_tensor_scale_ws(xs[i % P], cfg, ws, out=tso), gr,
+                        lambda: same((tso, fq.fp4_tensor_scale(xs[last], cfg))))
+    r["tensor_scale_one_launch_graph"] = dict(report(ms, 2 * n, n, ceiling), replays_match_eager=ok)
 
-    # KV cache: K and V each (131072*8) x 128, NVFP4 along head_dim; K and V in one grouped launch
+    def ts_rtn(i, one_launch):
+        if one_launch:
+            fq.fp4_tensor_scale_ws(xs[i % P], cfg, ws, out=ts1[i % P])
+        else:
+            fq.fp4_tensor_scale(xs[i % P], cfg, out=ts1[i % P])
+        fq.fp4_quantize(xs[i % P], cfg, ts1[i % P], codes=oc, scales=os_)
+
+    def ts_rtn_check():
+        t = fq.fp4_tensor_scale(xs[last], cfg)
+        return same((ts1[last], t), *zip((oc, os_), fq.fp4_quantize(xs[last], cfg, t)))
+    ms, ok = graph_time(torch, lambda i: ts_rtn(i, True), gr, ts_rtn_check)
+    r["tensor_scale_plus_rtn_graph"] = dict(report(ms, 4.5625 * n, n, ceiling), replays_match_eager=ok,
+                                            launches=2)
+    ms, ok = graph_time(torch, lambda i: ts_rtn(i, False), gr, ts_rtn_check)
+    r["tensor_scale_three_launches_plus_rtn_graph"] = dict(report(ms, 4.5625 * n, n, ceiling),
+                                                           replays_match_eager=ok, launches=4)
+    return r
+
+
+def wl_c3(args, fq, torch, W, ceiling):
+    """KV cache: K and V each (131072*8) x 128, NVFP4 along head_dim; K and V in one grouped launch."""
+    it = args.config_iters
+    u8 = _u8(torch)
+    cfg = fq.Fp4Config()
     rows, cols = W.c3_shape()
     n = rows * cols
     log("KV cache 131072 tokens ...")
@@ -494,17 +528,25 @@ def other_workloads(args, fq, torch, W, ceiling):
     kv_out = [(u8(n // 2), u8(n // 16)), (u8(n // 2), u8(n // 16))]
     kd = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
     vd = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
-    r = {}
+    # the grouped launch once, checked against single-tensor launches before it is timed
+    fq.fp4_quantize_grouped([K, V], cfg, [tk, tv], outs=kv_out)
+    single = [fq.fp4_quantize(K, cfg, tk), fq.fp4_quantize(V, cfg, tv)]
+    r = {"grouped_matches_single": all(torch.equal(a, b) for o, s_ in zip(kv_out, single) for a, b in zip(o, s_))}
+    del single
     r["quantize_kv_grouped"] = report(back_to_back(torch, lambda i: fq.fp4_quantize_grouped([K, V], cfg, [tk, tv], outs=kv_out), it), 2 * 2.5625 * n, 2 * n, ceiling)
 
     def deq(i):
         fq.fp4_dequantize(kv_out[0][0], kv_out[0][1], cfg, rows, cols, tk, out=kd)
         fq.fp4_dequantize(kv_out[1][0], kv_out[1][1], cfg, rows, cols, tv, out=vd)
     r["dequantize_kv_bf16"] = report(back_to_back(torch, deq, it), 2 * 2.5625 * n, 2 * n, ceiling)
-    res["nvfp4_kv_131072x8x128"] = r
-    del K, V, kd, vd
+    return r
 
-    # one deep guidance-cache layer: 8 expert slices 4096x1536 + activations 8192x4096, grouped
+
+def wl_c4(args, fq, torch, W, ceiling):
+    """One deep guidance-cache layer: 8 expert slices 4096x1536 + activations 8192x4096, grouped."""
+    it = args.config_iters
+    u8 = _u8(torch)
+    cfg = fq.Fp4Config()
     log("guidance-cache layer ...")
     xs, xrs, shapes = [], [], []
     for name, rr, cc, sigma, seed, stream in W.c4_tensors(20):
@@ -523,7 +565,16 @@ def other_workloads(args, fq, torch, W, ceiling):
     def pack(i):
         for (rr, cc), o, p in zip(shapes, roll, pk):
             fq.guide_pack(o[0], o[1], cfg, rr, cc, bits=p[0], gscales=p[1])
-    r = {}
+    # each grouped launch once, checked against single-tensor launches before it is timed
+    ok = True
+    fq.fp4_quantize_grouped(xs, cfg, tss, guides=guides, outs=tr)
+    fq.guide_pack_grouped([(o[0], o[1], rr, cc) for (rr, cc), o in zip(shapes, roll)], cfg, outs=pk)
+    for t in range(len(shapes)):
+        rr, cc = shapes[t]
+        ok = ok and all(torch.equal(a, b) for a, b in zip(roll[t], fq.fp4_quantize(xrs[t], cfg, tss[t], emit=True)))
+        ok = ok and all(torch.equal(a, b) for a, b in zip(tr[t], fq.fp4_quantize_guided(xs[t], cfg, *guides[t], tss[t])))
+        ok = ok and all(torch.equal(a, b) for a, b in zip(pk[t], fq.guide_pack(roll[t][0], roll[t][1], cfg, rr, cc)))
+    r = {"grouped_matches_single": bool(ok)}
     r["rollout_rtn_emit_grouped"] = report(back_to_back(torch, lambda i: fq.fp4_quantize_grouped(xrs, cfg, tss, emit=True, outs=roll), it), 2.6875 * n_layer, n_layer, ceiling)
     r["trainer_guided_grouped"] = report(back_to_back(torch, lambda i: fq.fp4_quantize_grouped(xs, cfg, tss, guides=guides, outs=tr), it), 2.75 * n_layer, n_layer, ceiling)
     r["guide_pack_9_launches"] = report(back_to_back(torch, pack, it), 0.75 * n_layer, n_layer, ceiling)
@@ -540,10 +591,13 @@ def other_workloads(args, fq, torch, W, ceiling):
     r["cache_bytes_20_deep_layers"] = per_layer_guide * 20
     r["full_codes_scales_40_layers"] = per_layer_full * 40
     r["cache_ratio"] = round(per_layer_guide * 20 / (per_layer_full * 40), 6)
-    res["guide_cache_layer_8x4096x1536_plus_8192x4096"] = r
-    del xs, xrs, roll, tr, guides, pk
+    return r
 
-    # uniform grid + RHT16 + SR on a 65536x8192 GEMM operand (1 GiB)
+
+def wl_c5(args, fq, torch, W, ceiling):
+    """Uniform grid + RHT16 + SR on a 65536x8192 GEMM operand (1 GiB)."""
+    it = args.config_iters
+    u8 = _u8(torch)
     rows, cols = W.c5_shape()
     n = rows * cols
     log("uniform + RHT16 + SR 65536x8192 (generating 1 GiB) ...")
@@ -556,9 +610,45 @@ def other_workloads(args, fq, torch, W, ceiling):
     r = {}
     r["tensor_scale_rht"] = report(back_to_back(torch, lambda i: fq.fp4_tensor_scale(x, cfg5, out=tso), k5), 2 * n, n, ceiling)
     r["quantize_rht_sr_uniform"] = report(back_to_back(torch, lambda i: fq.fp4_quantize(x, cfg5, ts, codes=c5c, scales=c5s), k5), 2.5625 * n, n, ceiling)
-    res["uniform_rht16_sr_65536x8192"] = r
-    del x
+    return r
+
+
+# --workload name -> (key under "workloads", function)
+WORKLOADS = {
+    "c1": ("nvfp4_act_4096x2048", wl_c1),
+    "c3": ("nvfp4_kv_131072x8x128", wl_c3),
+    "c4": ("guide_cache_layer_8x4096x1536_plus_8192x4096", wl_c4),
+    "c5": ("uniform_rht16_sr_65536x8192", wl_c5),
+}
+
+
+def other_workloads(args, fq, torch, W, ceiling, names=("c1", "c3", "c4", "c5")):
+    res = {}
+    for name in names:
+        key, fn = WORKLOADS[name]
+        res[key] = fn(args, fq, torch, W, ceiling)
+        torch.cuda.empty_cache()
     return res
+
+
+# the main kernel of each workload, whose roofline a single-workload run reports
+ROOFLINE_KERNEL = {
+    "c1": "tensor_scale_plus_rtn_graph",
+    "c3": "quantize_kv_grouped",
+    "c4": "trainer_guided_grouped",
+    "c5": "quantize_rht_sr_uniform",
+}
+
+
+def workload_roofline(name, r, sha):
+    """HBM roofline entry of a workload's main kernel (back-to-back or graph launch duration)."""
+    if not r or name not in ROOFLINE_KERNEL:
+        return None
+    k = ROOFLINE_KERNEL[name]
+    e = r[k]
+    return {"bound": "hbm", "kernel": k, "achieved": e["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(e["GBps"] / PEAK_HBM_GBS, 4), "traffic": read_traffic(f"{k}@{name}", sha),
+            "algorithmic_bytes_per_launch": e["bytes"], "avg_launch_us": e["us"]}
 
 
 def gemm_workload(args, fq, torch, W):
@@ -622,6 +712,19 @@ def main():
     fq.lib()
     torch.cuda.set_device(0)
     if args.gemm_only:
+        args.workload = "gemm"
+    if args.workload in WORKLOADS:
+        ceiling = copy_ceiling(torch, fq)
+        key, fn = WORKLOADS[args.workload]
+        r = fn(args, fq, torch, W, ceiling["GBps"])
+        line = {"metric": f"{key} kernels", "workload": key, "n_gpus": 1, "data": "synthetic",
+                "copy_ceiling": ceiling, "results": r, "source_sha": source_sha()}
+        rl = workload_roofline(args.workload, r, source_sha())
+        if rl:
+            line["roofline"] = rl
+        print(json.dumps(line), flush=True)
+        return
+    if args.workload == "gemm":
         g = gemm_workload(args, fq, torch, W)
         print(json.dumps({"metric": "MXFP4 GEMM TFLOP/s", "value": g["bf16_out"]["TFLOPs"], "unit": "TFLOP/s",
                           "n_gpus": 1, "higher_is_better": True, "dtype": "fp4 x fp4 -> f32 (bf16 out)",
@@ -648,7 +751,9 @@ def main():
 
     n = h["n"]
     value = h["step_bytes"] / (h["ms_step"] * 1e-3) / 1e9
-    dom = max(h["kernels"], key=lambda k: h["kernels"][k]["us"])   # largest share of the step
+    # the kernel with the largest share of the step, by its back-to-back duration (the figure rocprofv3's
+    # kernel trace reports; the in-step per-launch events include the event overhead)
+    dom = max(h["kernels"], key=lambda k: h["kernels"][k]["us_back_to_back"])
     dk = h["kernels"][dom]
     ach = dk["GBps_back_to_back"]
     sha = source_sha()
@@ -683,6 +788,7 @@ def main():
                      "traffic": read_traffic(f"{dom}@c2", sha),
                      "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": dk["us_back_to_back"],
                      "avg_launch_us_in_step": dk["us"]},
+        "roofline_c5": workload_roofline("c5", workloads.get(WORKLOADS["c5"][0]), sha),
         "cpu_baseline": cpu,
         "cpu_baseline_all_threads": cpu_all,
         "step_us_p10_median_p90": h["step_us_p10_median_p90"],

@@ -94,6 +94,21 @@ typedef struct {
 fp4_status fp4_tensor_scale(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
                             int64_t ld, float* tensor_scale_out, hipStream_t stream);
 
+/* The same tensor scale in one launch [FQT-FP4 §3]: every workgroup publishes its
+ * partial maximum in `workspace`, and the last one to finish reduces them and
+ * writes s_t, bit for bit equal to fp4_tensor_scale.
+ *   workspace        device memory of at least fp4_tensor_scale_workspace_bytes()
+ *                    (FP4_TENSOR_SCALE_WORKSPACE_BYTES), 256-byte aligned, owned by the
+ *                    caller and zero-filled before its first use; every call leaves it
+ *                    ready for the next one (its arrival counters return to 0).  Calls
+ *                    that may run at the same time need workspaces of their own.
+ *   workspace_bytes  its size; FP4_ERR_ARG when too small. */
+#define FP4_TENSOR_SCALE_WORKSPACE_BYTES 8192
+fp4_status fp4_tensor_scale_ws(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
+                               int64_t ld, float* tensor_scale_out, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+size_t fp4_tensor_scale_workspace_bytes(void);
+
 /* Block quantization with round-to-nearest-even or stochastic rounding
  * [FQT-FP4 §3; TRACE-KO].  Per block: NVFP4 scale code = E4M3 RNE of
  * amax / RN(Gmax*s_t), saturating at 448, elements multiplied by

@@ -107,6 +107,21 @@ struct AmaxParams {
     float* acc;                 // receives max finite |y| (as bits, atomic max)
 };
 
+// Workspace of the one-launch tensor scale, in 32-bit words from a 256-byte
+// aligned base, each word on a 256-byte line of its own: the slot maxima and
+// slot arrival counters (kTsSlots of each), the top maximum and the top counter.
+// All must be 0 before the first call; every completed call leaves them 0.
+constexpr uint32_t kTsSlots = 8;
+constexpr uint32_t kTsLine = 64;                        // words per 256-byte line
+constexpr uint32_t kTsMaxWorkgroups = 1024;
+constexpr uint32_t kTsSlotMax = 0;
+constexpr uint32_t kTsSlotCtr = kTsSlots * kTsLine;
+constexpr uint32_t kTsTopMax = 2 * kTsSlots * kTsLine;
+constexpr uint32_t kTsTopCtr = kTsTopMax + kTsLine;
+constexpr uint32_t kTsWords = kTsTopCtr + kTsLine;
+constexpr size_t kTsWorkspaceBytes = 8192;
+static_assert(kTsWords * 4 <= kTsWorkspaceBytes, "tensor-scale workspace layout");
+
 struct EncodeParams {
     const float* v;
     const uint8_t* aux;
@@ -144,6 +159,9 @@ uint32_t quantize_chunks(int format, int mode, bool rht, uint32_t ngroups);
 hipError_t launch_quantize_grouped(int format, int grid, int mode, bool rht, bool emit,
                                    const GroupedQuantParams& gp, hipStream_t s);
 hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams& p, hipStream_t s);
+// One-launch tensor scale with its workspace (kTsWorkspaceBytes, 256-byte aligned, counters 0).
+hipError_t launch_tensor_scale_1(int grid, bool rht, bool contig, const AmaxParams& p, uint32_t* ws,
+                                 hipStream_t s);
 hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantParams& p,
                              hipStream_t s);
 hipError_t launch_guide_pack(int format, const GuideParams& p, hipStream_t s);

@@ -32,9 +32,10 @@ constexpr int kAmaxU = 4;
 constexpr int kAmaxUSmall = 8;
 constexpr uint32_t kAmaxBlocks = 1024;
 
+// This thread's share of the amax: the largest finite |y| as fp32 bits over the
+// groups it loads (0 if none).
 template <bool RHT, bool CONTIG, int U>
-__global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
-    __shared__ uint32_t red[kThreads / 64];
+__device__ __forceinline__ uint32_t amax_thread(const AmaxParams& p) {
     uint32_t m = 0;
     const uint32_t signs = RHT ? rht_sign_mask(p.rht_seed) : 0u;
     const uint32_t lane = threadIdx.x & 63u, q = lane & 1u;
@@ -85,6 +86,11 @@ __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
         }
     }
     if constexpr (RHT) m = __float_as_uint(__uint_as_float(m) * 0.25f);   // exact: max |y| = max |a| / 4
+    return m;
+}
+
+// Maximum of m over the workgroup, valid in thread 0.  red: kThreads/64 words of LDS.
+__device__ __forceinline__ uint32_t wg_max_t0(uint32_t m, uint32_t* red) {
     #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -92,13 +98,67 @@ __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
     if (threadIdx.x == 0) {
         #pragma unroll
         for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
-        if (m != 0) atomicMax(reinterpret_cast<unsigned int*>(p.acc), m);
     }
+    return m;
+}
+
+template <bool RHT, bool CONTIG, int U>
+__global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
+    __shared__ uint32_t red[kThreads / 64];
+    const uint32_t m = wg_max_t0(amax_thread<RHT, CONTIG, U>(p), red);
+    if (threadIdx.x == 0 && m != 0) atomicMax(reinterpret_cast<unsigned int*>(p.acc), m);
+}
+
+__device__ __forceinline__ float ts_from_amax(uint32_t amax_bits, float gmax448) {
+    const float a = __uint_as_float(amax_bits);
+    return a == 0.0f ? 1.0f : a / gmax448;
+}
+
+// ---------------------------------------------------------------- one-launch tensor scale
+// Each workgroup folds its maximum into the maximum of its slot (b % 8) and then
+// counts itself in at that slot.  The last arrival of a slot takes the slot
+// maximum (leaving 0 behind), folds it into the top maximum and counts itself in
+// at the top; the last arrival there takes the top maximum and writes s_t.  The
+// counters wrap to 0 with their last arrival (atomic inc), so each call leaves
+// the workspace as it found it.
+// Every shared word is touched only by atomics that return their old value, and
+// each one's value is used before the next is issued, so it has been performed
+// where its address is held; atomics on one address are performed there one at a
+// time, so the arrival that completes a count comes after every maximum folded
+// in by the workgroups it counts.  No cache writeback or invalidate is involved:
+// agent-scope release/acquire fences (an L2 writeback and invalidate per
+// workgroup) cost more than the whole pass over a 16 MiB tensor, and so do
+// hundreds of atomics on one address, which is why there are eight slots.
+__device__ __forceinline__ uint32_t fetch_max_agent(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t take_agent(uint32_t* p) {
+    return __hip_atomic_exchange(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Returns true for the arrival that completes the count n (the counter is then 0 again).
+__device__ __forceinline__ bool arrive(uint32_t* ctr, uint32_t n) {
+    return __builtin_amdgcn_atomic_inc32(ctr, n - 1u, __ATOMIC_RELAXED, "agent") == n - 1u;
+}
+// Makes the atomic that produced v complete (its value is in a register) before
+// any later memory operation is issued.
+__device__ __forceinline__ void completed(uint32_t v) { asm volatile("" ::"v"(v) : "memory"); }
+
+template <bool RHT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void k_tensor_scale_1(const AmaxParams p, uint32_t* ws, float gmax448) {
+    __shared__ uint32_t red[kThreads / 64];
+    const uint32_t b = blockIdx.x, nwg = gridDim.x, slot = b % kTsSlots;
+    const uint32_t m = wg_max_t0(amax_thread<RHT, CONTIG, kAmaxU>(p), red);
+    if (threadIdx.x != 0) return;
+    uint32_t* smax = ws + kTsSlotMax + kTsLine * slot;
+    completed(fetch_max_agent(smax, m));
+    if (!arrive(ws + kTsSlotCtr + kTsLine * slot, (nwg - slot + kTsSlots - 1) / kTsSlots)) return;
+    completed(fetch_max_agent(ws + kTsTopMax, take_agent(smax)));
+    if (!arrive(ws + kTsTopCtr, min(nwg, kTsSlots))) return;
+    *p.acc = ts_from_amax(take_agent(ws + kTsTopMax), gmax448);
 }
 
 __global__ void k_ts_finalize(float* acc, float gmax448) {
-    const float a = *acc;                     // amax (bits were accumulated in place)
-    *acc = a == 0.0f ? 1.0f : a / gmax448;
+    *acc = ts_from_amax(__float_as_uint(*acc), gmax448);   // amax bits were accumulated in place
 }
 
 template <int U>
@@ -350,6 +410,22 @@ hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams
         launch_amax<kAmaxU>(rht, contig, kAmaxBlocks, p, s);
     }
     hipLaunchKernelGGL(k_ts_finalize, dim3(1), dim3(1), 0, s, p.acc, grid == 0 ? 2688.0f : 3136.0f);
+    return hipGetLastError();
+}
+
+// One launch of at most kTsMaxWorkgroups workgroups of kAmaxU groups per lane
+// (a 16 MiB tensor gets 512: measured faster than 256 once no address takes more
+// than a sixty-fourth of the atomics); an empty tensor still gets one workgroup,
+// which writes s_t = 1.
+hipError_t launch_tensor_scale_1(int grid, bool rht, bool contig, const AmaxParams& p, uint32_t* ws, hipStream_t s) {
+    const float g448 = grid == 0 ? 2688.0f : 3136.0f;
+    const uint32_t per_wg = kThreads * kAmaxU;
+    uint32_t blocks = (p.ngroups + per_wg - 1) / per_wg;
+    blocks = blocks < 1u ? 1u : (blocks > kTsMaxWorkgroups ? kTsMaxWorkgroups : blocks);
+#define FP4Q_TS1(R, C) hipLaunchKernelGGL((k_tensor_scale_1<R, C>), dim3(blocks), dim3(kThreads), 0, s, p, ws, g448)
+    if (rht) { if (contig) FP4Q_TS1(true, true); else FP4Q_TS1(true, false); }
+    else { if (contig) FP4Q_TS1(false, true); else FP4Q_TS1(false, false); }
+#undef FP4Q_TS1
     return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ class _CTensor(C.Structure):
 MAX_GROUP = 16
 
 _lib = None
-EXPORTS = ("fp4_tensor_scale", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
+EXPORTS = ("fp4_tensor_scale", "fp4_tensor_scale_ws", "fp4_tensor_scale_workspace_bytes", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
            "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_pack_grouped",
            "guide_unpack",
            "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_rht16",
@@ -101,6 +101,7 @@ def lib():
     CP = C.POINTER(_CCfg)
     sigs = {
         "fp4_tensor_scale": [CP, P, I64, I64, I64, P, P],
+        "fp4_tensor_scale_ws": [CP, P, I64, I64, I64, P, P, C.c_size_t, P],
         "fp4_quantize": [CP, P, I64, I64, I64, P, P, P, P, P],
         "fp4_quantize_guided": [CP, P, I64, I64, I64, P, P, P, P, P, P],
         "fp4_quantize_grouped": [CP, I, I, C.POINTER(_CTensor), P],
@@ -120,6 +121,8 @@ def lib():
         f = getattr(L, name)
         f.argtypes = args
         f.restype = C.c_int
+    L.fp4_tensor_scale_workspace_bytes.argtypes = []
+    L.fp4_tensor_scale_workspace_bytes.restype = C.c_size_t
     for name in ("fp4_codes_bytes",):
         getattr(L, name).argtypes = [I64, I64]
         getattr(L, name).restype = C.c_size_t
@@ -164,18 +167,43 @@ def _matrix(x: torch.Tensor):
     return rows, cols, ld
 
 
+def _alloc(shape, dtype, device) -> torch.Tensor:
+    """Every output the binding allocates for a caller comes from here (uninitialised memory: the
+    kernels write every element)."""
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _u8(n: int, like: torch.Tensor) -> torch.Tensor:
-    return torch.empty(n, dtype=torch.uint8, device=like.device)
+    return _alloc(n, torch.uint8, like.device)
 
 
 # ---------------------------------------------------------------- entry points
 def fp4_tensor_scale(x: torch.Tensor, cfg: Fp4Config, out: torch.Tensor | None = None) -> torch.Tensor:
     _on_gpu(x, out)
     rows, cols, ld = _matrix(x)
-    out = torch.empty(1, dtype=torch.float32, device=x.device) if out is None else out
+    out = _alloc(1, torch.float32, x.device) if out is None else out
     c = cfg.c()
     _check(lib().fp4_tensor_scale(C.byref(c), _ptr(x), rows, cols, ld, _ptr(out), _stream(x)),
            "fp4_tensor_scale")
+    return out
+
+
+def tensor_scale_workspace(device=None) -> torch.Tensor:
+    """A zero-filled workspace for fp4_tensor_scale_ws (reusable by one stream of calls at a time)."""
+    n = lib().fp4_tensor_scale_workspace_bytes()
+    return torch.zeros(n, dtype=torch.uint8, device=device if device is not None else "cuda")
+
+
+def fp4_tensor_scale_ws(x: torch.Tensor, cfg: Fp4Config, workspace: torch.Tensor,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp4_tensor_scale in one launch, with a workspace from tensor_scale_workspace()."""
+    _on_gpu(x, workspace, out)
+    rows, cols, ld = _matrix(x)
+    out = _alloc(1, torch.float32, x.device) if out is None else out
+    c = cfg.c()
+    _check(lib().fp4_tensor_scale_ws(C.byref(c), _ptr(x), rows, cols, ld, _ptr(out), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(x)),
+           "fp4_tensor_scale_ws")
     return out
 
 
@@ -260,7 +288,7 @@ def fp4_fake_quantize(x: torch.Tensor, cfg: Fp4Config, tensor_scale: torch.Tenso
     _on_gpu(x, tensor_scale, guide_bits, guide_scales, out)
     rows, cols, ld = _matrix(x)
     if out is None:
-        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+        out = _alloc((rows, cols), torch.bfloat16, x.device)
     ld_out = out.stride(0) if rows > 1 else cols
     guided = guide_bits is not None
     c = cfg.c()
@@ -277,7 +305,7 @@ def fp4_guide_mismatch(x: torch.Tensor, cfg: Fp4Config, rollout_codes: torch.Ten
     _on_gpu(x, rollout_codes, rollout_scales, tensor_scale, out)
     rows, cols, ld = _matrix(x)
     if out is None:
-        out = torch.empty(3, dtype=torch.int64, device=x.device)
+        out = _alloc(3, torch.int64, x.device)
     c = cfg.c()
     _check(lib().fp4_guide_mismatch(C.byref(c), _ptr(x), rows, cols, ld, _ptr(tensor_scale), _ptr(rollout_codes),
                                     _ptr(rollout_scales), _ptr(out), _stream(x)), "fp4_guide_mismatch")
@@ -289,7 +317,7 @@ def fp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, cfg: Fp4Config, ro
                    out: torch.Tensor | None = None) -> torch.Tensor:
     _on_gpu(codes, scales, tensor_scale, out)
     if out is None:
-        out = torch.empty((rows, cols), dtype=dtype, device=codes.device)
+        out = _alloc((rows, cols), dtype, codes.device)
     ld_out = out.stride(0) if rows > 1 else cols
     kind = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
     if out.dtype not in (torch.bfloat16, torch.float32):
@@ -305,7 +333,7 @@ def fp4_gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch
     """C[M, N] = A * B^T from the MXFP4 codes and scales of A [M, K] and B [N, K] (blocks along K)."""
     _on_gpu(a_codes, a_scales, b_codes, b_scales, out)
     if out is None:
-        out = torch.empty((M, N), dtype=dtype, device=a_codes.device)
+        out = _alloc((M, N), dtype, a_codes.device)
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("gemm output must be bfloat16 or float32")
     ldc = out.stride(0) if M > 1 else N
@@ -324,7 +352,7 @@ def fp4_gemm_mxfp4_grouped(products, dtype=torch.bfloat16, outs=None):
     res = []
     for i, (ac, asc, bc, bsc, M, N, K) in enumerate(products):
         _on_gpu(ac, asc, bc, bsc)
-        out = outs[i] if outs is not None else torch.empty((M, N), dtype=dtype, device=ac.device)
+        out = outs[i] if outs is not None else _alloc((M, N), dtype, ac.device)
         _on_gpu(out)
         ldc = out.stride(0) if M > 1 else N
         arr[i] = _CGemm(_ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), M, N, K, _ptr(out), ldc)
@@ -386,7 +414,7 @@ def fp4_rht16(x: torch.Tensor, seed: int, inverse: bool = False, dtype=torch.flo
               out: torch.Tensor | None = None) -> torch.Tensor:
     _on_gpu(x, out)
     rows, cols, ld = _matrix(x)
-    out = torch.empty((rows, cols), dtype=dtype, device=x.device) if out is None else out
+    out = _alloc((rows, cols), dtype, x.device) if out is None else out
     kind = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
     _check(lib().fp4_rht16(_ptr(x), rows, cols, ld, seed, int(inverse), _ptr(out), kind, _stream(x)),
            "fp4_rht16")

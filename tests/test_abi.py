@@ -181,3 +181,19 @@ def test_grouped_host_side_errors(fq):
     assert L.fp4_quantize_grouped(C.byref(cfg), 0, 2, arr, None) == 1
     arr[1] = fq._CTensor(A, 4, 32, 32, A, A, A, None, None)
     assert L.fp4_quantize_grouped(C.byref(cfg), 1, 2, arr, None) == 1  # guided needs guides
+
+
+def test_tensor_scale_workspace_errors(fq):
+    L = fq.lib()
+    A = 1 << 20
+    p = C.c_void_p(A)
+    c = fq.Fp4Config().c()
+    n = L.fp4_tensor_scale_workspace_bytes()
+    assert n == 8192
+    f = L.fp4_tensor_scale_ws
+    assert f(C.byref(c), p, 4, 32, 32, p, None, n, None) == 1              # no workspace
+    assert f(C.byref(c), p, 4, 32, 32, p, C.c_void_p(A + 16), n, None) == 3  # not 256-byte aligned
+    assert f(C.byref(c), p, 4, 32, 32, p, p, n - 1, None) == 1              # too small
+    assert "workspace" in L.fp4_last_error().decode()
+    assert f(C.byref(c), p, 4, 24, 24, p, p, n, None) == 2                  # cols % 16
+    assert f(C.byref(c), p, 4, 32, 32, None, p, n, None) == 1               # no output

@@ -81,3 +81,32 @@ def test_straight_through_gradient(fq):
     assert torch.equal(y.detach(), ref)
     (y.float() * w.float()).sum().backward()
     assert torch.equal(x.grad, w)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_guided_straight_through_vs_oracle(fq, fmt):
+    # The guided QAT path through autograd: the forward value is the oracle's guided rounding of x
+    # under the rollout's guide (its bits, block scales and, for NVFP4, tensor scale); the backward
+    # pass hands the incoming gradient through unchanged.  Guided NVFP4 without the guide's tensor
+    # scale is refused.
+    from precision_rl_amd.autograd import fake_quantize_ste
+    rows, cols = 96, 1024
+    x_h, xr_h = W.c1_x(rows, cols, seed=12), W.c1_rollout(rows, cols, seed=12)
+    cfg = fq.Fp4Config(format=fmt)
+    oc = O.Cfg(format=fmt)
+    xr = dev(xr_h)
+    ts = fq.fp4_tensor_scale(xr, cfg) if fmt == 0 else None
+    _, rs, gb = fq.fp4_quantize(xr, cfg, ts, emit=True)
+    x = dev(x_h).clone().requires_grad_(True)
+    y = fake_quantize_ste(x, cfg, ts, gb, rs)
+    o_ts = O.tensor_scale(oc, xr_h) if fmt == 0 else 1.0
+    _, o_rs, o_gb = O.quantize(oc, O.RTN, xr_h, o_ts, emit=True)
+    gc, gs = O.quantize(oc, O.GUIDED, x_h, o_ts, guide_bits=o_gb, guide_scales=o_rs)
+    want = O.dequantize(oc, gc, gs, o_ts, rows, cols, out_bf16=True)
+    assert (y.detach().view(torch.int16).cpu().numpy().reshape(-1) == want.view(np.int16)).all()
+    g = torch.randn(rows, cols, device="cuda").to(torch.bfloat16)
+    y.backward(g)
+    assert torch.equal(x.grad, g)
+    if fmt == 0:
+        with pytest.raises(ValueError):
+            fake_quantize_ste(x, cfg, None, gb, rs)

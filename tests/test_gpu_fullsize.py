@@ -43,8 +43,10 @@ def sample_rows(rows, k=48, seed=0):
     return sorted(set(range(min(k, rows))) | set(range(max(0, rows - k), rows)) | set(int(r) for r in mid))
 
 
-def check_rows(fq, cfg, mode, xh, codes, scales, ts, rows_idx, gb=None, gs=None, bits=None, tag=""):
-    """Oracle on each sampled row (whole-tensor index via row0) vs the GPU output rows."""
+def check_rows(fq, cfg, mode, xh, codes, scales, ts, rows_idx, rollout=None, bits=None, tag=""):
+    """Oracle on each sampled row (whole-tensor index via row0) vs the GPU output rows.  Guided
+    mode takes its guide from the oracle's own RTN quantization of the same row of `rollout`
+    (host bf16), so no GPU output feeds the oracle.  Returns the oracle's (codes, scales) per row."""
     cols = xh.shape[1]
     B = 32 if cfg.format else 16
     oc = O.Cfg(format=cfg.format, grid=cfg.grid, rht16=cfg.rht16, rht_seed=cfg.rht_seed,
@@ -52,17 +54,21 @@ def check_rows(fq, cfg, mode, xh, codes, scales, ts, rows_idx, gb=None, gs=None,
     c = codes.cpu().numpy().reshape(-1, cols // 2)
     s = scales.cpu().numpy().reshape(-1, cols // B)
     b = bits.cpu().numpy().reshape(-1, cols // 8) if bits is not None else None
-    gbr = gb.reshape(-1, cols // 8) if gb is not None else None
-    gsr = gs.reshape(-1, cols // B) if gs is not None else None
+    want = {}
     for r in rows_idx:
         kw = {}
         if mode == O.GUIDED:
-            kw = dict(guide_bits=gbr[r], guide_scales=gsr[r])
+            rc, rs = O.quantize(O.Cfg(format=cfg.format, grid=cfg.grid, rht16=cfg.rht16, rht_seed=cfg.rht_seed),
+                                O.RTN, rollout[r:r + 1], ts, row0=r)
+            gb, gs = O.guide_pack(oc, rc, rs, 1, cols)
+            kw = dict(guide_bits=gb, guide_scales=gs)
         out = O.quantize(oc, mode, xh[r:r + 1], ts, row0=r, emit=b is not None, **kw)
         assert (out[1] == s[r]).all(), (tag, "scales", r)
         assert (out[0] == c[r]).all(), (tag, "codes", r)
         if b is not None:
             assert (out[2] == b[r]).all(), (tag, "bits", r)
+        want[r] = out[:2]
+    return want
 
 
 def f32bits(x):
@@ -117,8 +123,7 @@ def test_c2_mxfp4_moe_activations_16384x4096(fq, mode):
         gb, gs = fq.guide_pack(rc, rs, cfg, rows, cols)
         gc, gsc = fq.fp4_quantize_guided(x, cfg, gb, gs, None)
         assert torch.equal(gsc, rs)
-        check_rows(fq, cfg, O.GUIDED, x_h, gc, gsc, 1.0, idx, gb=gb.cpu().numpy(), gs=gs.cpu().numpy(),
-                   tag="c2 guided")
+        check_rows(fq, cfg, O.GUIDED, x_h, gc, gsc, 1.0, idx, rollout=xr_h, tag="c2 guided")
     say(f"C2 {mode}: {len(idx)} rows bit-exact ({time.time() - t:.1f} s)")
 
 
@@ -135,13 +140,12 @@ def test_c3_kv_cache_131072_tokens(fq):
         assert f32bits(ts.item()) == f32bits(o_ts)
         c, s = fq.fp4_quantize(x, cfg, ts)
         idx = sample_rows(rows, k=64, seed=which)
-        check_rows(fq, cfg, O.RTN, xh, c, s, o_ts, idx, tag=f"c3 {which}")
+        want = check_rows(fq, cfg, O.RTN, xh, c, s, o_ts, idx, tag=f"c3 {which}")
         dq = fq.fp4_dequantize(c, s, cfg, rows, cols, ts, dtype=torch.bfloat16)
         dqh = dq.view(torch.int16).cpu().numpy()
-        cn, sn = c.cpu().numpy().reshape(rows, -1), s.cpu().numpy().reshape(rows, -1)
         for r in idx:
-            want = O.dequantize(oc, cn[r], sn[r], o_ts, 1, cols, out_bf16=True)
-            assert (dqh[r] == want.view(np.int16)).all()
+            d = O.dequantize(oc, want[r][0], want[r][1], o_ts, 1, cols, out_bf16=True)
+            assert (dqh[r] == d.view(np.int16)).all()
         del x
     say(f"C3 K and V bit-exact on sampled rows ({time.time() - t:.1f} s)")
 
@@ -163,8 +167,8 @@ def test_c4_guidance_cache_layer(fq):
         o_ts = O.tensor_scale(oc, xrh)
         assert f32bits(ts.item()) == f32bits(o_ts)
         idx = sample_rows(r, k=8, seed=stream)
-        check_rows(fq, cfg, O.GUIDED, xh, gc, gsc, o_ts, idx, gb=gb.cpu().numpy(), gs=gs.cpu().numpy(),
-                   tag=f"c4 {name}")
+        check_rows(fq, cfg, O.RTN, xrh, rc, rs, o_ts, idx, bits=eb, tag=f"c4 {name} rollout")
+        check_rows(fq, cfg, O.GUIDED, xh, gc, gsc, o_ts, idx, rollout=xrh, tag=f"c4 {name}")
     guide = 20 * (n_layer // 8 + n_layer // 16)
     full = 40 * (n_layer // 2 + n_layer // 16)
     assert guide == 314_572_800 and full == 1_887_436_800 and 6 * guide == full
