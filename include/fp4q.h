@@ -109,6 +109,20 @@ fp4_status fp4_tensor_scale_ws(const fp4_cfg* cfg, const void* x_bf16, int64_t r
                                size_t workspace_bytes, hipStream_t stream);
 size_t fp4_tensor_scale_workspace_bytes(void);
 
+/* fp4_tensor_scale_ws without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static array of
+ * FP4_TENSOR_SCALE_WORKSPACE_BYTES that the library holds on each GPU it runs on
+ * until the process ends; this call allocates nothing.  That size serves every
+ * input the other entry points accept (the launch has at most 1024 workgroups);
+ * larger inputs fail with FP4_ERR_SHAPE as everywhere.  Calls on one GPU share
+ * its array: every completed call leaves it zeroed for the next, and calls that
+ * overlap in time on one GPU (several streams, several host threads) race, with
+ * undefined results for them and for later calls.  Same result as
+ * fp4_tensor_scale, bit for bit. */
+fp4_status fp4_tensor_scale_noalloc(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
+                                    int64_t ld, float* tensor_scale_out, hipStream_t stream);
+
 /* Block quantization with round-to-nearest-even or stochastic rounding
  * [FQT-FP4 §3; TRACE-KO].  Per block: NVFP4 scale code = E4M3 RNE of
  * amax / RN(Gmax*s_t), saturating at 448, elements multiplied by

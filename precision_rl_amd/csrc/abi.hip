@@ -146,6 +146,29 @@ fp4_status fp4_tensor_scale_ws(const fp4_cfg* cfg, const void* x_bf16, int64_t r
                       "fp4_tensor_scale_ws launch");
 }
 
+fp4_status fp4_tensor_scale_noalloc(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
+                                    int64_t ld, float* tensor_scale_out, hipStream_t stream) {
+    FP4Q_TRY(check_cfg(cfg));
+    uint64_t ng = 0;
+    FP4Q_TRY(check_matrix(rows, cols, ld, 16, x_bf16, &ng));
+    FP4Q_TRY(need(tensor_scale_out, 4, "tensor_scale_out"));
+    // the launch never exceeds kTsMaxWorkgroups workgroups, whose shared words fit
+    // the static workspace whatever the input size
+    static_assert(fp4q::kTsWords * 4 <= fp4q::kTsWorkspaceBytes, "static workspace too small");
+    hipError_t e = hipSuccess;
+    uint32_t* ws = fp4q::static_ts_workspace(&e);
+    if (!ws) return hip_status(e, "fp4_tensor_scale_noalloc: static workspace lookup");
+    fp4q::AmaxParams p{};
+    p.x = static_cast<const uint16_t*>(x_bf16);
+    p.ld = ld;
+    p.ngroups = (uint32_t)ng;
+    p.gpr = fp4q::make_fastdiv(cols > 0 ? (uint32_t)(cols / 16) : 1u);
+    p.rht_seed = cfg->rht_seed;
+    p.acc = tensor_scale_out;
+    return hip_status(fp4q::launch_tensor_scale_1(cfg->grid, cfg->rht16 != 0, ld == cols, p, ws, stream),
+                      "fp4_tensor_scale_noalloc launch");
+}
+
 static fp4_status quantize_common(const fp4_cfg* cfg, int mode, const void* x_bf16, int64_t rows,
                                   int64_t cols, int64_t ld, const float* ts, void* codes, void* scales,
                                   void* bits_out, const void* gbits, const void* gscales,

@@ -162,6 +162,10 @@ hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams
 // One-launch tensor scale with its workspace (kTsWorkspaceBytes, 256-byte aligned, counters 0).
 hipError_t launch_tensor_scale_1(int grid, bool rht, bool contig, const AmaxParams& p, uint32_t* ws,
                                  hipStream_t s);
+// Device address of the library's static tensor-scale workspace (kTsWorkspaceBytes)
+// on the current device, looked up once per device; NULL with the error in *err
+// when the lookup fails.
+uint32_t* static_ts_workspace(hipError_t* err);
 hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantParams& p,
                              hipStream_t s);
 hipError_t launch_guide_pack(int format, const GuideParams& p, hipStream_t s);

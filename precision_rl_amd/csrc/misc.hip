@@ -1,5 +1,7 @@
 // misc.hip -- tensor scale, dequantization, guide pack/unpack, standalone RHT16
 // and the element-encode entry, for gfx950.
+#include <mutex>
+
 #include "device.h"
 #include "internal.h"
 
@@ -427,6 +429,37 @@ hipError_t launch_tensor_scale_1(int grid, bool rht, bool contig, const AmaxPara
     else { if (contig) FP4Q_TS1(false, true); else FP4Q_TS1(false, false); }
 #undef FP4Q_TS1
     return hipGetLastError();
+}
+
+// Workspace of fp4_tensor_scale_noalloc, for callers that cannot allocate: one
+// array per device, zero when the code object is loaded and left zero by every
+// completed call.  Host code reaches it only through the device address that
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+static __device__ __align__(256) uint32_t scratch[kTsWorkspaceBytes / sizeof(uint32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+uint32_t* static_ts_workspace(hipError_t* err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {   // set-up, once per device, with that device current
+        void* p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+    }
+    return g_scratch_ptr[dev];
 }
 
 hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantParams& p, hipStream_t s) {

@@ -69,7 +69,8 @@ class _CTensor(C.Structure):
 MAX_GROUP = 16
 
 _lib = None
-EXPORTS = ("fp4_tensor_scale", "fp4_tensor_scale_ws", "fp4_tensor_scale_workspace_bytes", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
+EXPORTS = ("fp4_tensor_scale", "fp4_tensor_scale_ws", "fp4_tensor_scale_workspace_bytes",
+           "fp4_tensor_scale_noalloc", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
            "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_pack_grouped",
            "guide_unpack",
            "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_rht16",
@@ -102,6 +103,7 @@ def lib():
     sigs = {
         "fp4_tensor_scale": [CP, P, I64, I64, I64, P, P],
         "fp4_tensor_scale_ws": [CP, P, I64, I64, I64, P, P, C.c_size_t, P],
+        "fp4_tensor_scale_noalloc": [CP, P, I64, I64, I64, P, P],
         "fp4_quantize": [CP, P, I64, I64, I64, P, P, P, P, P],
         "fp4_quantize_guided": [CP, P, I64, I64, I64, P, P, P, P, P, P],
         "fp4_quantize_grouped": [CP, I, I, C.POINTER(_CTensor), P],
@@ -204,6 +206,17 @@ def fp4_tensor_scale_ws(x: torch.Tensor, cfg: Fp4Config, workspace: torch.Tensor
     _check(lib().fp4_tensor_scale_ws(C.byref(c), _ptr(x), rows, cols, ld, _ptr(out), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(x)),
            "fp4_tensor_scale_ws")
+    return out
+
+
+def fp4_tensor_scale_noalloc(x: torch.Tensor, cfg: Fp4Config, out: torch.Tensor) -> torch.Tensor:
+    """fp4_tensor_scale in one launch with the library's static workspace: nothing is allocated
+    (out is required).  Calls that overlap on one GPU race."""
+    _on_gpu(x, out)
+    rows, cols, ld = _matrix(x)
+    c = cfg.c()
+    _check(lib().fp4_tensor_scale_noalloc(C.byref(c), _ptr(x), rows, cols, ld, _ptr(out), _stream(x)),
+           "fp4_tensor_scale_noalloc")
     return out
 
 
