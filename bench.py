@@ -689,6 +689,29 @@ def gemm_workload(args, fq, torch, W):
     res["grouped_8_experts_bf16_out"] = {"experts": E, "tokens_per_expert": rows, "us": round(ms * 1e3, 2),
                                          "TFLOPs": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
                                          "us_p10_median_p90_single_launch": take_spread()}
+    # producer-side fusion: the product's epilogue writes the MXFP4 codes, scales and guide bits of the
+    # bf16-rounded C (the next layer's quantized input and the rollout's guide) instead of C; against the
+    # plain product with bf16 output followed by fp4_quantize with emission
+    qc, qs, qb = (torch.empty(M * N // d, dtype=torch.uint8, device="cuda") for d in (2, 32, 8))
+    cb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    fq.fp4_gemm_mxfp4_quantize(a, asc, b, bsc, M, N, K, codes=qc, scales=qs, bits=qb)
+    ref = fq.fp4_quantize(fq.fp4_gemm_mxfp4(a, asc, b, bsc, M, N, K, out=cb), cfg, emit=True)
+    same = all(torch.equal(x, y) for x, y in zip((qc, qs, qb), ref))
+    ms_f = back_to_back(torch, lambda i: fq.fp4_gemm_mxfp4_quantize(a, asc, b, bsc, M, N, K, codes=qc, scales=qs,
+                                                                    bits=qb), reps, warm=5)
+    sp_f = take_spread()
+
+    def two_step(i):
+        fq.fp4_gemm_mxfp4(a, asc, b, bsc, M, N, K, out=cb)
+        fq.fp4_quantize(cb, cfg, emit=True, codes=qc, scales=qs, bits=qb)
+    ms_2 = back_to_back(torch, two_step, reps, warm=5)
+    res["fused_quantize_epilogue"] = {
+        "us": round(ms_f * 1e3, 2), "TFLOPs": round(flops / (ms_f * 1e-3) / 1e12, 1),
+        "us_p10_median_p90_single_launch": sp_f,
+        "us_product_bf16_then_quantize_emit": round(ms_2 * 1e3, 2),
+        "speedup_vs_two_launches": round(ms_2 / ms_f, 3),
+        "equals_product_then_quantize": bool(same),
+        "bytes_written": M * N // 2 + M * N // 32 + M * N // 8, "bytes_of_bf16_c_not_written": 2 * M * N}
     r = res["bf16_out"]
     res["roofline"] = {"bound": "mfma", "kernel": "k_gemm_mx_lds", "achieved": r["TFLOPs"], "peak": PEAK_FP4_TFLOPS,
                        "unit": "TFLOP/s", "frac": r["frac_fp4_peak"], "traffic": None,

@@ -273,6 +273,23 @@ fp4_status fp4_gemm_mxfp4(const void* a_codes, const void* a_scales, const void*
                           int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, fp4_dtype dtype,
                           hipStream_t stream);
 
+/* The MXFP4 product with the rollout's quantization of its result fused into
+ * the producing kernel [TRACE-JA "量子化情報キャッシュ": the rollout records the
+ * codeword it chose at each quantization point; "実験結果": collecting it costs
+ * about as much as plain FP4 rollout; TETRAJET section 4: the next linear
+ * layer takes MXFP4 inputs]: C = A * B^T exactly as fp4_gemm_mxfp4 computes it,
+ * rounded to bf16, then quantized along its rows as fp4_quantize does with
+ * format MXFP4, the E2M1 grid and round to nearest: codes [M, N/2], E8M0 scales
+ * [M, N/32] and, when c_guide_bits is not NULL, the guide bitplane [M, N/8].
+ * C itself is never written.  Bit for bit equal to fp4_gemm_mxfp4 with bf16
+ * output followed by fp4_quantize (MXFP4, RTN, emission) of that output.
+ *   N % 32 == 0 (FP4_ERR_SHAPE); K a positive multiple of 512 and both scale
+ *   pointers 16-byte aligned (FP4_ERR_UNSUPPORTED otherwise); M == 0 or
+ *   N == 0 is a no-op.  c_codes and c_guide_bits 16-byte aligned. */
+fp4_status fp4_gemm_mxfp4_quantize(const void* a_codes, const void* a_scales, const void* b_codes,
+                                   const void* b_scales, int64_t M, int64_t N, int64_t K, void* c_codes,
+                                   void* c_scales, void* c_guide_bits, hipStream_t stream);
+
 /* One product of a grouped call (fields as in fp4_gemm_mxfp4). */
 typedef struct {
     const void* a_codes;

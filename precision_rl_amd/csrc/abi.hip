@@ -434,7 +434,7 @@ namespace {
 // when M or N is 0 (nothing to do).
 fp4_status gemm_params(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
                        int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, fp4_dtype dtype, fp4q::GemmParams* p,
-                       bool* empty) {
+                       bool* empty, bool store_c = true) {
     if (dtype != FP4_OUT_F32 && dtype != FP4_OUT_BF16) return fail(FP4_ERR_ARG, "unknown dtype %d", (int)dtype);
     if (M < 0 || N < 0 || K < 0)
         return fail(FP4_ERR_ARG, "negative shape M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
@@ -445,10 +445,12 @@ fp4_status gemm_params(const void* a_codes, const void* a_scales, const void* b_
         return fail(FP4_ERR_SHAPE, "shape too large M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
     if ((uint64_t)((M + 127) / 128) * (uint64_t)((N + 127) / 128) >= (1ull << 31))
         return fail(FP4_ERR_SHAPE, "too many 128 x 128 tiles of C");
-    if (ldc < N) return fail(FP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
-    // the stores address a 256-row band of C with 32-bit offsets
-    if (ldc > (1ll << 21)) return fail(FP4_ERR_SHAPE, "ldc=%lld too large", (long long)ldc);
-    FP4Q_TRY(need(c, dtype == FP4_OUT_BF16 ? 2 : 4, "c"));
+    if (store_c) {
+        if (ldc < N) return fail(FP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+        // the stores address a 256-row band of C with 32-bit offsets
+        if (ldc > (1ll << 21)) return fail(FP4_ERR_SHAPE, "ldc=%lld too large", (long long)ldc);
+        FP4Q_TRY(need(c, dtype == FP4_OUT_BF16 ? 2 : 4, "c"));
+    }
     if (K > 0) {
         FP4Q_TRY(need(a_codes, 16, "a_codes"));
         FP4Q_TRY(need(a_scales, 1, "a_scales"));
@@ -481,6 +483,30 @@ fp4_status fp4_gemm_mxfp4(const void* a_codes, const void* a_scales, const void*
     FP4Q_TRY(gemm_params(a_codes, a_scales, b_codes, b_scales, M, N, K, c, ldc, dtype, &p, &empty));
     if (empty) return ok();
     return hip_status(fp4q::launch_gemm_mx(dtype == FP4_OUT_BF16, p, stream), "gemm launch");
+}
+
+fp4_status fp4_gemm_mxfp4_quantize(const void* a_codes, const void* a_scales, const void* b_codes,
+                                   const void* b_scales, int64_t M, int64_t N, int64_t K, void* c_codes,
+                                   void* c_scales, void* c_guide_bits, hipStream_t stream) {
+    fp4q::GemmParams p{};
+    bool empty = false;
+    FP4Q_TRY(gemm_params(a_codes, a_scales, b_codes, b_scales, M, N, K, nullptr, 0, FP4_OUT_BF16, &p, &empty, false));
+    if (N % 32 != 0)
+        return fail(FP4_ERR_SHAPE, "N=%lld is not a multiple of 32 (the blocks of the result's quantization)",
+                    (long long)N);
+    if (empty) return ok();
+    if ((uint64_t)M * (uint64_t)N / 16 >= (1ull << 31))
+        return fail(FP4_ERR_SHAPE, "result too large to quantize (%lld x %lld)", (long long)M, (long long)N);
+    FP4Q_TRY(need(c_codes, 16, "c_codes"));
+    FP4Q_TRY(need(c_scales, 1, "c_scales"));
+    if (c_guide_bits) FP4Q_TRY(need(c_guide_bits, 16, "c_guide_bits"));
+    if (!fp4q::gemm_quant_supported(p))
+        return fail(FP4_ERR_UNSUPPORTED, "the quantizing product needs K a positive multiple of 512 (K=%lld) and "
+                                         "16-byte aligned scales", (long long)K);
+    p.qcodes = static_cast<uint8_t*>(c_codes);
+    p.qscales = static_cast<uint8_t*>(c_scales);
+    p.qbits = static_cast<uint8_t*>(c_guide_bits);
+    return hip_status(fp4q::launch_gemm_mx_quant(p, stream), "quantizing gemm launch");
 }
 
 fp4_status fp4_gemm_mxfp4_grouped(int n, const fp4_gemm_desc* products, fp4_dtype dtype, hipStream_t stream) {

@@ -10,19 +10,26 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in E2M1 (format code 4)
 // reads, in lane l, row (l mod 32) and K block (l / 32) of the 64-wide K slice:
 // 32 values, which are 16 bytes of our codes in our nibble order, plus that
-// block's E8M0 scale in byte 0 of the lane's scale operand.  Result element j
-// of lane l is C[8 (j / 4) + 4 (l / 32) + j % 4][l mod 32].  (Layout checked
-// on the GPU against a host product of random codes and scales.)
+// block's E8M0 scale in the byte of the lane's scale operand that op_sel picks.
+// Result element j of lane l is C[8 (j / 4) + 4 (l / 32) + j % 4][l mod 32].
+// (Layout checked on the GPU against a host product of random codes and scales.)
 //
-// Tiling: a workgroup of 4 waves computes a 128 x 128 tile of C, each wave a
-// 64 x 64 quarter as 2 x 2 MFMA tiles.  K advances 128 values (4 scale blocks)
-// per stage: the A and B tiles (128 rows x 64 bytes each) are staged in LDS
-// with an 80-byte row pitch -- the 16 bytes of padding put the 16-byte
-// operand reads of 8 consecutive rows on distinct banks -- and each row's
-// four scale bytes in one dword.  The next stage is loaded into registers
-// while the MFMAs run and written to the other LDS buffer afterwards, so one
-// barrier per stage suffices.  Rows past M or N are clamped on load (their
-// results are not stored); K blocks past K load as zero codes.
+// Main path (K % 512 == 0, scales 16-byte aligned), gemm_tile below: a
+// workgroup of 4 waves (2 x 2) computes a 256 x 192 tile of C when there are
+// enough such tiles to give every compute unit one, else 128 x 128.  K advances
+// 256 values per stage (128 bytes of codes per row, one whole cache line); both
+// operands stream from memory straight into LDS by buffer-to-LDS loads, double
+// buffered, with the pieces of each staged row permuted so that the rows lanes
+// read together sit on distinct bank groups.  Each stage is four MFMA K slices
+// whose operands are read from LDS two slices ahead.  Whole tiles of C are
+// turned around in LDS and written as 16-byte row pieces; edge tiles store
+// element by element through a buffer range that drops what lies outside C.
+// The same K loop can instead end in the MXFP4 quantization of the
+// bf16-rounded product (the producer-side epilogue): C is then not written,
+// only its codes, scales and guide bits.
+//
+// Other K (multiples of 32), k_gemm_mx_any: 128 x 128 tiles, K advancing 128
+// values per stage through registers into LDS rows padded to 80 bytes.
 #include "device.h"
 #include "internal.h"
 
@@ -348,8 +355,84 @@ __device__ __forceinline__ void store_c(__amdgpu_buffer_rsrc_t rc, int voff, flo
     }
 }
 
-// Tile (tm, tn) of the product p, computed by the calling workgroup.
-template <int WM, int WN, bool BF16>
+// MXFP4 round-to-nearest quantization of one 32-element block of bf16 values
+// (16 dwords, element 2j in the low half of w[j]), as the MXFP4 quantizer does
+// it without the RHT: scale code max(E(amax) - 2, 0) from the largest bf16
+// magnitude, codes by the scaled RNE convert of the bf16 words; a block holding
+// a non-finite value gets scale 0xFF and zero codes.  Returns the scale code;
+// c receives the 16 bytes of codes.
+__device__ __forceinline__ uint32_t quantize_block32_bf16(const uint32_t w[16], uint32_t c[4]) {
+    const uint32_t key = max(amax_bits16(w), amax_bits16(w + 8)) << 16;
+    const uint32_t e = key >> 23;
+    uint32_t sc = e > 2u ? e - 2u : 0u;
+    const float cs = mx_scale(sc);
+    #pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = pack_rne8_bf16(w + 4 * k, cs);
+    if (key >= 0x7F800000u) {
+        sc = 0xFFu;
+        #pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = 0u;
+    }
+    return sc;
+}
+
+// Producer-side epilogue: the wave's quarter of C, rounded to bf16, goes through
+// LDS half its rows at a time (as the staged store does); then each lane takes
+// one 32-element block of a row, quantizes it to MXFP4 with round to nearest and
+// writes its 16 bytes of codes, its scale byte and, when asked for, its 32 guide
+// bits.  N % 32 == 0, so a block lies wholly inside or outside C.
+template <int WM, int WN>
+__device__ __forceinline__ void quantize_epilogue(const GemmParams& p, const v16f (&acc)[WM][WN], uint8_t* smem,
+                                                  int wave, int lane, int kc, int r32, int64_t row0, int64_t col0) {
+    constexpr int HR = 16 * WM;              // rows per half
+    constexpr int PITCH = 32 * WN * 2;       // bytes per staged row of bf16
+    constexpr int NB = HR * WN;              // 32-element blocks per half
+    static_assert(NB % 64 == 0, "whole wave instructions per half");
+    uint8_t* st = smem + wave * HR * PITCH;
+    const int64_t cb = p.N / 2, sb = p.N / 32, bb = p.N / 8;   // bytes per row of codes, scales, bits
+    barrier_only();   // every wave is done with the K loop's LDS
+    #pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        #pragma unroll
+        for (int i = 0; i < WM / 2; ++i)
+            #pragma unroll
+            for (int j = 0; j < WN; ++j)
+                #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    uint8_t* d = st + (32 * i + 8 * (r >> 2) + 4 * kc + (r & 3)) * PITCH + (32 * j + r32) * 2;
+                    const bf16x2 b = __builtin_convertvector((v2f){acc[h * (WM / 2) + i][j][r], 0.0f}, bf16x2);
+                    *reinterpret_cast<uint16_t*>(d) = (uint16_t)(__builtin_bit_cast(uint32_t, b) & 0xFFFFu);
+                }
+        // this wave's LDS writes complete before its reads (LDS operations of a wave run in order)
+        #pragma unroll
+        for (int q = 0; q < NB / 64; ++q) {
+            const int c = q * 64 + lane, r = c / WN, blk = c - r * WN;
+            uint32_t w[16];
+            #pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const v4u32 v = *reinterpret_cast<const v4u32*>(st + r * PITCH + blk * 64 + 16 * k);
+                w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+            }
+            uint32_t codes[4];
+            const uint32_t sc = quantize_block32_bf16(w, codes);
+            const int64_t row = row0 + h * HR + r, col = col0 + 32 * blk;
+            if (row < p.M && col < p.N) {
+                *reinterpret_cast<v4u32*>(p.qcodes + row * cb + col / 2) = (v4u32){codes[0], codes[1], codes[2], codes[3]};
+                p.qscales[row * sb + col / 32] = (uint8_t)sc;
+                if (p.qbits) {
+                    const uint32_t bits = gather_nibble_lsbs(codes[0]) | (gather_nibble_lsbs(codes[1]) << 8) |
+                                          (gather_nibble_lsbs(codes[2]) << 16) | (gather_nibble_lsbs(codes[3]) << 24);
+                    *reinterpret_cast<uint32_t*>(p.qbits + row * bb + col / 8) = bits;
+                }
+            }
+        }
+    }
+}
+
+// Tile (tm, tn) of the product p, computed by the calling workgroup.  QUANT: the
+// epilogue quantizes the bf16-rounded tile (p.qcodes, p.qscales, p.qbits)
+// instead of storing C.
+template <int WM, int WN, bool BF16, bool QUANT = false>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint32_t tn, uint8_t* smem) {
     using T = LdsTile<WM, WN>;
     const int t = threadIdx.x, lane = t & 63;
@@ -464,6 +547,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint
     }
     // the loads issued past the last stage must land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
+    if constexpr (QUANT) {
+        quantize_epilogue<WM, WN>(p, acc, smem, wave, lane, kc, r32, m0 + wm * 32 * WM, n0 + wn * 32 * WN);
+        return;
+    }
 
     // C: result r of MFMA tile (i, j) in this lane is row 32 i + 8 (r / 4) + 4 kc + r % 4, column
     // 32 j + r32 of the wave's quarter.  Stores go through a buffer resource whose range ends at
@@ -537,12 +624,12 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t remap) {
     return bid;
 }
 
-template <int WM, int WN, bool BF16>
+template <int WM, int WN, bool BF16, bool QUANT = false>
 __global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const uint32_t bid = xcd_tile(p.xcd_remap);
     const uint32_t tm = bid / p.tiles_n, tn = bid - tm * p.tiles_n;
-    gemm_tile<WM, WN, BF16>(p, tm, tn, smem);
+    gemm_tile<WM, WN, BF16, QUANT>(p, tm, tn, smem);
 }
 
 // Several products in one launch: the tiles of product i are workgroups
@@ -560,7 +647,7 @@ __global__ __launch_bounds__(256) void k_gemm_mx_lds_grouped(const GroupedGemmPa
 }
 
 template <int WM, int WN>
-static hipError_t launch_lds(bool bf16_out, GemmParams p, hipStream_t s) {
+static hipError_t launch_lds(bool bf16_out, GemmParams p, hipStream_t s, bool quant = false) {
     using T = LdsTile<WM, WN>;
     const uint32_t tiles_m = (uint32_t)((p.M + T::RA - 1) / T::RA);
     p.tiles_n = (uint32_t)((p.N + T::RB - 1) / T::RB);
@@ -568,7 +655,8 @@ static hipError_t launch_lds(bool bf16_out, GemmParams p, hipStream_t s) {
     p.xcd_remap = g % 8 == 0 ? 1u : 0u;
     const int esz = bf16_out ? 2 : 4;
     p.staged = ((uintptr_t)p.c & 15) == 0 && (p.ldc * esz) % 16 == 0 ? 1u : 0u;
-    if (bf16_out) hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, true>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
+    if (quant) hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, true, true>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
+    else if (bf16_out) hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, true>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
     else hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, false>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
     return hipGetLastError();
 }
@@ -617,6 +705,13 @@ hipError_t launch_gemm_mx_grouped(bool bf16_out, const GroupedGemmParams& gp, hi
     }
     if (big >= 256) return launch_lds_grouped<4, 3>(bf16_out, gp, s);
     return launch_lds_grouped<2, 2>(bf16_out, gp, s);
+}
+
+bool gemm_quant_supported(const GemmParams& p) { return main_path_ok(p); }
+
+hipError_t launch_gemm_mx_quant(const GemmParams& p, hipStream_t s) {
+    if (gemm_config(p.M, p.N) == 1) return launch_lds<4, 3>(true, p, s, true);
+    return launch_lds<2, 2>(true, p, s, true);
 }
 
 hipError_t launch_gemm_mx(bool bf16_out, const GemmParams& p, hipStream_t s) {

@@ -142,6 +142,9 @@ struct GemmParams {
     uint32_t tiles_n;           // column tiles of C
     uint32_t xcd_remap;         // 1: hand out tiles XCD by XCD (grid size a multiple of 8)
     uint32_t staged;            // 1: C and its rows 16-byte aligned (whole tiles stored through LDS)
+    uint8_t* qcodes;            // quantize epilogue: MXFP4 codes of the bf16-rounded C, [M, N/2]
+    uint8_t* qscales;           // ... E8M0 scales [M, N/32]
+    uint8_t* qbits;             // ... guide bits [M, N/8], or null
 };
 
 // Launchers (return hipGetLastError() of the launch).
@@ -180,6 +183,10 @@ hipError_t launch_rht16(bool inverse, bool bf16_out, bool contig, const RhtParam
 hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n16, hipStream_t s);
 hipError_t launch_encode_values(int grid, int mode, const EncodeParams& p, hipStream_t s);
 hipError_t launch_gemm_mx(bool bf16_out, const GemmParams& p, hipStream_t s);
+// The same product ending in the MXFP4 RTN quantization of its bf16-rounded
+// result (p.qcodes, p.qscales, p.qbits); only where gemm_quant_supported(p).
+bool gemm_quant_supported(const GemmParams& p);
+hipError_t launch_gemm_mx_quant(const GemmParams& p, hipStream_t s);
 
 // Up to kMaxGemmGroup products in one launch (one launch per product when
 // some product's K is not a multiple of 512).

@@ -73,7 +73,7 @@ EXPORTS = ("fp4_tensor_scale", "fp4_tensor_scale_ws", "fp4_tensor_scale_workspac
            "fp4_tensor_scale_noalloc", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
            "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_pack_grouped",
            "guide_unpack",
-           "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_rht16",
+           "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_gemm_mxfp4_quantize", "fp4_rht16",
            "fp4_encode_values", "fp4_stream_copy", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
            "fp4_status_str", "fp4_last_error")
 
@@ -115,6 +115,7 @@ def lib():
         "guide_unpack": [CP, P, P, I64, I64, P, P, P],
         "fp4_gemm_mxfp4": [P, P, P, P, I64, I64, I64, P, I64, I, P],
         "fp4_gemm_mxfp4_grouped": [I, C.POINTER(_CGemm), I, P],
+        "fp4_gemm_mxfp4_quantize": [P, P, P, P, I64, I64, I64, P, P, P, P],
         "fp4_rht16": [P, I64, I64, I64, C.c_uint64, I, P, I, P],
         "fp4_encode_values": [I, I, P, P, I64, P, P],
         "fp4_stream_copy": [P, P, C.c_size_t, P],
@@ -354,6 +355,23 @@ def fp4_gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch
     _check(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
                                 _ptr(out), ldc, kind, _stream(a_codes)), "fp4_gemm_mxfp4")
     return out
+
+
+def fp4_gemm_mxfp4_quantize(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor,
+                            b_scales: torch.Tensor, M: int, N: int, K: int, emit: bool = True,
+                            codes=None, scales=None, bits=None):
+    """MXFP4 codes, scales (and guide bits) of the bf16-rounded C = A * B^T, quantized in the product's
+    epilogue (C itself is not written).  Returns (codes, scales[, bits])."""
+    _on_gpu(a_codes, a_scales, b_codes, b_scales, codes, scales, bits)
+    n = M * N
+    codes = _u8(n // 2, a_codes) if codes is None else codes
+    scales = _u8(n // 32, a_codes) if scales is None else scales
+    if emit and bits is None:
+        bits = _u8(n // 8, a_codes)
+    _check(lib().fp4_gemm_mxfp4_quantize(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
+                                         _ptr(codes), _ptr(scales), _ptr(bits) if emit else None,
+                                         _stream(a_codes)), "fp4_gemm_mxfp4_quantize")
+    return (codes, scales, bits) if emit else (codes, scales)
 
 
 def fp4_gemm_mxfp4_grouped(products, dtype=torch.bfloat16, outs=None):

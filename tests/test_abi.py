@@ -197,3 +197,17 @@ def test_tensor_scale_workspace_errors(fq):
     assert "workspace" in L.fp4_last_error().decode()
     assert f(C.byref(c), p, 4, 24, 24, p, p, n, None) == 2                  # cols % 16
     assert f(C.byref(c), p, 4, 32, 32, None, p, n, None) == 1               # no output
+
+
+def test_gemm_quantize_host_side_errors(fq):
+    g = fq.lib().fp4_gemm_mxfp4_quantize
+    A = 1 << 20
+    p = C.c_void_p(A)
+    assert g(p, p, p, p, 64, 48, 512, p, p, p, None) == 2            # N % 32
+    assert g(p, p, p, p, 64, 64, 544, p, p, p, None) == 4            # K not a multiple of 512
+    assert g(p, p, p, p, 64, 64, 0, p, p, p, None) == 4              # K == 0
+    assert g(p, p, p, p, 64, 64, 512, None, p, p, None) == 1         # no codes
+    assert g(p, p, p, p, 64, 64, 512, C.c_void_p(A + 8), p, p, None) == 3   # misaligned codes
+    assert g(p, p, p, p, 64, 64, 512, p, p, C.c_void_p(A + 4), None) == 3   # misaligned bits
+    assert g(p, p, p, p, 0, 64, 512, None, None, None, None) == 0    # empty: no-op
+    assert g(p, p, C.c_void_p(A + 1), p, 64, 64, 512, p, p, p, None) == 3   # misaligned B codes

@@ -1,0 +1,87 @@
+"""The MXFP4 product with its result quantized in the producing kernel
+(fp4_gemm_mxfp4_quantize): codes, E8M0 scales and guide bits of the bf16-rounded
+C = A * B^T, as the MXFP4 quantizer (round to nearest, with emission) writes
+them.
+
+Oracle parity uses operands whose products and partial sums are exact in fp32
+(E8M0 scales 126..128: every product is a multiple of 2^-4 of magnitude at most
+144, so any sum of up to 4096 of them is exact), so the oracle alone fixes C, its
+bf16 rounding and its quantization, whatever order the matrix cores sum in.
+Shapes cover both tile configurations (128 x 128 and 256 x 192), partial tiles
+in M and N, and the full 8192 x 1536 x 4096 product (sampled rows).  On
+Gaussian activations and weights quantized by the library, the fused kernel
+equals the plain product with bf16 output followed by fp4_quantize, bit for bit
+over whole tensors.  Outputs start as 0xA5 bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from precision_rl_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fq():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from precision_rl_amd import fp4q
+    fp4q.lib()
+    return fp4q
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x).ravel()).cuda()
+
+
+def sample(M, k=24, seed=0):
+    if M <= 3 * k:
+        return list(range(M))
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(k, M - k), size=k, replace=False)
+    return sorted(set(range(k)) | set(range(M - k, M)) | set(int(r) for r in mid))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 192, 512), (300, 160, 1024), (1, 32, 512), (129, 992, 1536),
+                                   (8192, 1536, 4096)])
+def test_fused_quantize_vs_oracle_on_exact_products(fq, M, N, K):
+    a, asc = W.mx_operand(M, K, seed=M + 7, stream=0, scale_lo=126, scale_hi=128)
+    b, bsc = W.mx_operand(N, K, seed=N + 9, stream=2, scale_lo=126, scale_hi=128)
+    A, As, B, Bs = dev(a), dev(asc), dev(b), dev(bsc)
+    codes, scales, bits = fq.fp4_gemm_mxfp4_quantize(A, As, B, Bs, M, N, K)
+    c32 = fq.fp4_gemm_mxfp4(A, As, B, Bs, M, N, K, dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = sample(M, seed=K)
+    exact, _ = O.gemm_mx(a.reshape(M, -1)[rows], asc.reshape(M, -1)[rows], b, bsc, len(rows), N, K)
+    # the operands make every partial sum exact: the plain product equals the exact one
+    assert (c32.cpu().numpy()[rows].astype(np.float64) == exact).all()
+    xb = W.f32_to_bf16_rne(exact.astype(np.float32))          # C rounded to bf16, from the exact C
+    oc = O.Cfg(format=O.MXFP4)
+    gc = codes.cpu().numpy().reshape(M, N // 2)
+    gs = scales.cpu().numpy().reshape(M, N // 32)
+    gb = bits.cpu().numpy().reshape(M, N // 8)
+    for i, r in enumerate(rows):
+        wc, ws, wb = O.quantize(oc, O.RTN, xb[i:i + 1], row0=r, emit=True)
+        assert (gs[r] == ws).all(), ("scales", r)
+        assert (gc[r] == wc).all(), ("codes", r)
+        assert (gb[r] == wb).all(), ("bits", r)
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 1536, 4096), (1000, 608, 2048), (256, 192, 512)])
+def test_fused_equals_product_then_quantize(fq, M, N, K):
+    cfg = fq.Fp4Config(format=fq.MXFP4)
+    xa = W.f32_to_bf16_rne(W.normal_outliers_f32(M, K, 1020, 16, 0.0, 1.0))
+    xb = W.f32_to_bf16_rne(W.normal_outliers_f32(N, K, 1020, 0, 0.0, 1.0, sigma=0.02))
+    tod = lambda h: torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).cuda()
+    a, asc = fq.fp4_quantize(tod(xa), cfg)
+    b, bsc = fq.fp4_quantize(tod(xb), cfg)
+    fused = fq.fp4_gemm_mxfp4_quantize(a, asc, b, bsc, M, N, K)
+    c = fq.fp4_gemm_mxfp4(a, asc, b, bsc, M, N, K, dtype=torch.bfloat16)
+    two_step = fq.fp4_quantize(c, cfg, emit=True)
+    no_bits = fq.fp4_gemm_mxfp4_quantize(a, asc, b, bsc, M, N, K, emit=False)
+    torch.cuda.synchronize()
+    for f, t in zip(fused, two_step):
+        assert torch.equal(f, t)
+    assert torch.equal(no_bits[0], fused[0]) and torch.equal(no_bits[1], fused[1])
