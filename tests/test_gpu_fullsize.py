@@ -33,8 +33,14 @@ def fq():
     return fp4q
 
 
-def dev(u16):
-    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+def dev(u16, pad=0):
+    t = torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16)
+    if pad:   # padded rows (ld = cols + pad), the padding NaN
+        rows, cols = u16.shape
+        buf = torch.full((rows, cols + pad), float("nan"), dtype=torch.bfloat16)
+        buf[:, :cols] = t
+        return buf.cuda()[:, :cols]
+    return t.cuda()
 
 
 def sample_rows(rows, k=48, seed=0):
@@ -195,19 +201,22 @@ def test_c5_uniform_rht16_sr_65536x8192(fq):
     say(f"C5 bit-exact on {len(idx)} rows ({time.time() - t:.1f} s)")
 
 
-@pytest.mark.parametrize("rows", [8191, 8192])
+@pytest.mark.parametrize("rows,pad", [(8191, 0), (8192, 0), (8193, 24)])
+@pytest.mark.parametrize("grid", [0, 1])
 @pytest.mark.parametrize("fmt", [0, 1])
-def test_both_slot_counts_at_the_small_launch_threshold(fq, fmt, rows):
+def test_both_slot_counts_at_the_small_launch_threshold(fq, fmt, grid, rows, pad):
     # A single-tensor launch below 2048 workgroups of four slots takes two slots
     # per lane: 8191 x 2048 (NVFP4: 2047 workgroups of four) launches two, 8192 x 2048
-    # launches four.  Both equal the oracle in every mode, on the whole tensor.
+    # launches four, and 8193 x 2048 with padded rows launches four with a ragged
+    # last chunk.  All equal the oracle in every mode and on both grids, on the
+    # whole tensor.
     cols = 2048
-    say("slot threshold", fmt, rows, cols)
+    say("slot threshold", fmt, grid, rows, cols, pad)
     xh = W.c1_x(rows, cols, seed=21)
     xrh = W.c1_rollout(rows, cols, seed=21)
-    cfg = fq.Fp4Config(format=fmt)
-    oc = O.Cfg(format=fmt)
-    x, xr = dev(xh), dev(xrh)
+    cfg = fq.Fp4Config(format=fmt, grid=grid)
+    oc = O.Cfg(format=fmt, grid=grid)
+    x, xr = dev(xh, pad), dev(xrh, pad)
     ts_t = fq.fp4_tensor_scale(xr, cfg) if fmt == 0 else None
     ts = O.tensor_scale(oc, xrh) if fmt == 0 else 1.0
     if fmt == 0:
@@ -219,7 +228,7 @@ def test_both_slot_counts_at_the_small_launch_threshold(fq, fmt, rows):
     gc, gs = fq.fp4_quantize_guided(x, cfg, rb, rs, ts_t)
     o_gc, o_gs = O.quantize(oc, O.GUIDED, xh, ts, guide_bits=o_rb, guide_scales=o_rs)
     assert (gc.cpu().numpy() == o_gc).all() and (gs.cpu().numpy() == o_gs).all()
-    scfg = fq.Fp4Config(format=fmt, rounding=fq.SR, sr_seed=5, sr_offset=9)
+    scfg = fq.Fp4Config(format=fmt, grid=grid, rounding=fq.SR, sr_seed=5, sr_offset=9)
     sc, ss = fq.fp4_quantize(x, scfg, ts_t)
-    o_sc, o_ss = O.quantize(O.Cfg(format=fmt, sr_seed=5, sr_offset=9), O.SR, xh, ts)
+    o_sc, o_ss = O.quantize(O.Cfg(format=fmt, grid=grid, sr_seed=5, sr_offset=9), O.SR, xh, ts)
     assert (sc.cpu().numpy() == o_sc).all() and (ss.cpu().numpy() == o_ss).all()
