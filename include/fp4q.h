@@ -327,6 +327,12 @@ fp4_status fp4_rht16(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld,
 fp4_status fp4_encode_values(int grid, int mode, const float* v, const uint8_t* aux, int64_t n,
                              uint8_t* out, hipStream_t stream);
 
+/* The NVFP4 block-scale rounding on its own, for exhaustive verification
+ * [FQT-FP4 §3: E4M3 block scales]: out[i] = OCP E4M3FN code of min(t[i], 448)
+ * rounded to nearest even, for t[i] >= 0 (a NaN gives the code of 448).
+ * n % 4 == 0; t 16-byte aligned, out 4-byte aligned. */
+fp4_status fp4_encode_scales(const float* t, int64_t n, uint8_t* out, hipStream_t stream);
+
 /* Plain streaming copy of `bytes` (a multiple of 16) from src to dst, one
  * 16-byte load and store per lane: the practical HBM bandwidth reference the
  * quantize kernels are measured against.  Both pointers 16-byte aligned;

@@ -548,6 +548,15 @@ fp4_status fp4_rht16(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld,
                       "rht16 launch");
 }
 
+fp4_status fp4_encode_scales(const float* t, int64_t n, uint8_t* out, hipStream_t stream) {
+    if (n < 0 || n % 4 != 0) return fail(FP4_ERR_SHAPE, "n=%lld must be a non-negative multiple of 4", (long long)n);
+    if (n / 4 >= (1ll << 31)) return fail(FP4_ERR_SHAPE, "n too large");
+    if (n == 0) return ok();
+    FP4Q_TRY(need(t, 16, "t"));
+    FP4Q_TRY(need(out, 4, "out"));
+    return hip_status(fp4q::launch_encode_scales(t, out, (uint32_t)(n / 4), stream), "encode_scales launch");
+}
+
 fp4_status fp4_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
     if (bytes == 0) return ok();
     if (bytes % 16 != 0) return fail(FP4_ERR_SHAPE, "bytes=%zu is not a multiple of 16", bytes);

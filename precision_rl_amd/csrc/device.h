@@ -59,6 +59,16 @@ __device__ __forceinline__ void st_out4(void* base, int64_t idx, uint32_t a, uin
     st_out(reinterpret_cast<v4u32*>(base) + idx, v);
 }
 
+// Non-temporal 16-byte store, for an output several times larger than its
+// input that streams out (a dequantized tensor): measured with the five-kernel
+// 16384 x 4096 MXFP4 step, dequantizing with these stores made the whole step
+// 7% faster (127 -> 118 us), since the 128 MiB of bf16 no longer evict the codes
+// and guides the next kernels read; for the quantize kernels, whose outputs the
+// next kernel reads, non-temporal stores made the step 3% slower.
+__device__ __forceinline__ void st_stream4(void* base, int64_t idx, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    __builtin_nontemporal_store((v4u32){a, b, c, d}, reinterpret_cast<v4u32*>(base) + idx);
+}
+
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -66,14 +76,18 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // ---------------------------------------------------------------- E4M3 / E8M0
 
-// E4M3FN code of t in [0, 448] (callers clamp), round to nearest even.
+// E4M3FN code of t in [0, 448] (callers clamp), round to nearest even: the gfx950
+// fp8 convert (OCP E4M3FN, bias 7, subnormal step 2^-9), one instruction.  It
+// equals the rounding rule on every fp32 value in [0, 448] (checked on the GPU
+// over all of them through fp4_encode_scales).  The second converted value is 0,
+// so byte 1 of the result is 0 and the code needs no mask.
 __device__ __forceinline__ uint32_t e4m3_encode_rne(float t) {
-    uint32_t b = __float_as_uint(t);
-    if (t < 0.015625f) {                        // below 2^-6: step 2^-9
-        return (uint32_t)__builtin_rintf(t * 512.0f);  // 0..8; 8 is the smallest normal
-    }
-    b += 0x7FFFFu + ((b >> 20) & 1u);           // keep 3 mantissa bits, ties to even
-    return (b >> 20) - (120u << 3);             // rebias exponent 127 -> 7
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.0f, 0, false);
+}
+
+// min(t, 448) for t >= 0 or NaN, on the bit patterns (a NaN gives 448).
+__device__ __forceinline__ float clamp448(float t) {
+    return __uint_as_float(min(__float_as_uint(t), 0x43E00000u));
 }
 
 // Exact fp32 value of an E4M3FN magnitude code (sign bit ignored, 0x7F not special).

@@ -182,6 +182,8 @@ hipError_t launch_guide_pack_grouped(int format, GroupedGuideParams gp, hipStrea
 hipError_t launch_rht16(bool inverse, bool bf16_out, bool contig, const RhtParams& p, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n16, hipStream_t s);
 hipError_t launch_encode_values(int grid, int mode, const EncodeParams& p, hipStream_t s);
+// E4M3 codes of n4 * 4 values t (NVFP4 block-scale rounding, t clamped to 448).
+hipError_t launch_encode_scales(const float* t, uint8_t* out, uint32_t n4, hipStream_t s);
 hipError_t launch_gemm_mx(bool bf16_out, const GemmParams& p, hipStream_t s);
 // The same product ending in the MXFP4 RTN quantization of its bf16-rounded
 // result (p.qcodes, p.qscales, p.qbits); only where gemm_quant_supported(p).

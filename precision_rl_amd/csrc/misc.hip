@@ -216,12 +216,12 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) 
         if constexpr (BF16) {
             uint32_t o[4];
             to_bf16x8(v, ok, o);
-            st_out4(reinterpret_cast<uint16_t*>(p.out) + off, 0, o[0], o[1], o[2], o[3]);
+            st_stream4(reinterpret_cast<uint16_t*>(p.out) + off, 0, o[0], o[1], o[2], o[3]);
         } else {
             uint32_t o[4];
             #pragma unroll
             for (int j = 0; j < 4; ++j) o[j] = ok ? __float_as_uint(v[j]) : 0x7FC00000u;
-            st_out4(reinterpret_cast<float*>(p.out) + off, 0, o[0], o[1], o[2], o[3]);
+            st_stream4(reinterpret_cast<float*>(p.out) + off, 0, o[0], o[1], o[2], o[3]);
         }
     }
 }
@@ -391,6 +391,18 @@ __global__ __launch_bounds__(kThreads) void k_encode_values(const EncodeParams p
     reinterpret_cast<uint2*>(p.out)[t] = make_uint2(lo, hi);
 }
 
+// ---------------------------------------------------------------- block-scale encode
+// The NVFP4 block-scale rounding on its own (exhaustive verification): the E4M3
+// code of each t, four per lane.
+__global__ __launch_bounds__(kThreads) void k_encode_scales(const float* t, uint8_t* out, uint32_t n4) {
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n4) return;
+    const float4 v = reinterpret_cast<const float4*>(t)[i];
+    const uint32_t c = e4m3_encode_rne(clamp448(v.x)) | e4m3_encode_rne(clamp448(v.y)) << 8 |
+                       e4m3_encode_rne(clamp448(v.z)) << 16 | e4m3_encode_rne(clamp448(v.w)) << 24;
+    reinterpret_cast<uint32_t*>(out)[i] = c;
+}
+
 // ---------------------------------------------------------------- reference copy
 
 __global__ __launch_bounds__(kThreads) void k_stream_copy(const v4u32* __restrict__ src,
@@ -525,6 +537,11 @@ hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n16, hipStrea
     const uint64_t blocks = (n16 + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(k_stream_copy, dim3((uint32_t)blocks), dim3(kThreads), 0, s,
                        static_cast<const v4u32*>(src), static_cast<v4u32*>(dst), n16);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_scales(const float* t, uint8_t* out, uint32_t n4, hipStream_t s) {
+    hipLaunchKernelGGL(k_encode_scales, dim3(blocks_for(n4)), dim3(kThreads), 0, s, t, out, n4);
     return hipGetLastError();
 }
 

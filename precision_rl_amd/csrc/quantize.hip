@@ -229,7 +229,7 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             const uint32_t tb = __float_as_uint(t);
             const bool exact = !rden_ok || tb - 1u < 0x3C800003u || (tb & 0xFFFFFu) - 0x7FFFCu <= 8u;
             if (__builtin_expect(exact, 0)) t = __uint_as_float(amax_key) / denom;
-            sc = e4m3_encode_rne(fminf(t, 448.0f));
+            sc = e4m3_encode_rne(clamp448(t));   // t >= 0; NaN only for a non-finite block
             inv = tab[sc];
             if (!finite) sc = 0x7Fu;
         } else {

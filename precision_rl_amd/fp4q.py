@@ -74,7 +74,7 @@ EXPORTS = ("fp4_tensor_scale", "fp4_tensor_scale_ws", "fp4_tensor_scale_workspac
            "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_pack_grouped",
            "guide_unpack",
            "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_gemm_mxfp4_quantize", "fp4_rht16",
-           "fp4_encode_values", "fp4_stream_copy", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
+           "fp4_encode_values", "fp4_encode_scales", "fp4_stream_copy", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
            "fp4_status_str", "fp4_last_error")
 
 
@@ -118,6 +118,7 @@ def lib():
         "fp4_gemm_mxfp4_quantize": [P, P, P, P, I64, I64, I64, P, P, P, P],
         "fp4_rht16": [P, I64, I64, I64, C.c_uint64, I, P, I, P],
         "fp4_encode_values": [I, I, P, P, I64, P, P],
+        "fp4_encode_scales": [P, I64, P, P],
         "fp4_stream_copy": [P, P, C.c_size_t, P],
     }
     for name, args in sigs.items():
@@ -461,6 +462,17 @@ def fp4_encode_values(v: torch.Tensor, grid: int, mode: int, aux: torch.Tensor |
     out = _u8(n, v) if out is None else out
     _check(lib().fp4_encode_values(grid, mode, _ptr(v), _ptr(aux), n, _ptr(out), _stream(v)),
            "fp4_encode_values")
+    return out
+
+
+def fp4_encode_scales(t: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """E4M3 block-scale codes of the values t (>= 0, clamped to 448), round to nearest even."""
+    _on_gpu(t, out)
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError("t must be a contiguous float32 tensor")
+    n = t.numel()
+    out = _u8(n, t) if out is None else out
+    _check(lib().fp4_encode_scales(_ptr(t), n, _ptr(out), _stream(t)), "fp4_encode_scales")
     return out
 
 

@@ -126,3 +126,45 @@ def test_encode_breakpoints_over_all_fp32(fq, g, mode, aux, sign):
         vb = struct.unpack("<f", struct.pack("<I", p - 1))[0]
         assert (O.encode(g, mode, abs(v), aux) | s8) == k, hex(p)
         assert (O.encode(g, mode, abs(vb), aux) | s8) != k, hex(p - 1)
+
+
+def test_e4m3_scale_encode_over_all_fp32_up_to_448(fq):
+    # The NVFP4 block-scale code: E4M3FN round to nearest even of t in [0, 448]
+    # (the kernels clamp t to 448 first).  The GPU encodes every fp32 pattern from
+    # +0 to 448 and the code changes exactly at the midpoints of consecutive E4M3
+    # values (a midpoint itself goes to the even code), which the oracle's decode
+    # table gives; the oracle's encode agrees at every change and just before it.
+    # Values above 448, infinity and NaN give the code of 448.
+    hi = bits(448.0)
+    got_bp, first = [], None
+    prev_last = None
+    for s in range(0, hi + 1, CHUNK):
+        e = min(s + CHUNK, hi + 1)
+        m = e - s
+        pad = (-m) % 4
+        idx = torch.arange(s, e + pad, dtype=torch.int64, device="cuda")
+        v = (idx & 0xFFFFFFFF).to(torch.int32).view(torch.float32)
+        c = fq.fp4_encode_scales(v)[:m]
+        if first is None:
+            first = int(c[0])
+        if prev_last is not None and int(c[0]) != prev_last:
+            got_bp.append((s, int(c[0])))
+        ch = torch.nonzero(c[1:] != c[:-1]).flatten()
+        if ch.numel():
+            got_bp += [(s + int(p) + 1, int(k)) for p, k in zip(ch.cpu().numpy(), c[ch + 1].cpu().numpy())]
+        prev_last = int(c[-1])
+        del idx, v, c
+    exp = []
+    for code in range(0x7E):
+        mid = (Fraction(O.e4m3_decode(code)) + Fraction(O.e4m3_decode(code + 1))) / 2
+        p = bits(float(mid))
+        assert Fraction(struct.unpack("<f", struct.pack("<I", p))[0]) == mid   # midpoints are exact fp32 values
+        exp.append((p if (code + 1) % 2 == 0 else p + 1, code + 1))
+    assert first == 0
+    assert got_bp == exp, (got_bp[:6], exp[:6])
+    for p, k in exp:
+        v = struct.unpack("<f", struct.pack("<I", p))[0]
+        vb = struct.unpack("<f", struct.pack("<I", p - 1))[0]
+        assert O.e4m3_encode(v) == k and O.e4m3_encode(vb) == k - 1, hex(p)
+    big = torch.tensor([448.0, 449.0, 464.0, 1e30, float("inf"), float("nan"), 3.4e38, 500.0], device="cuda")
+    assert (fq.fp4_encode_scales(big).cpu().numpy() == 0x7E).all()
