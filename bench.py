@@ -758,6 +758,22 @@ def gemm_workload(args, fq, torch, W):
         "speedup_vs_two_launches": round(ms_2 / ms_f, 3),
         "equals_product_then_quantize": bool(same),
         "bytes_written": M * N // 2 + M * N // 32 + M * N // 8, "bytes_of_bf16_c_not_written": 2 * M * N}
+    del qc, qs, qb, cb, ref, outs, ws, prods, arr
+    # a square product, 16384^3 with bf16 out (256 x 256 tiles, 16 rounds): random E2M1 codes and
+    # E8M0 scales 120..130, drawn on the device
+    S = 16384
+    g = torch.Generator(device="cuda").manual_seed(3)
+    sa_ = torch.randint(0, 256, (S * S // 2,), dtype=torch.uint8, device="cuda", generator=g)
+    sas = torch.randint(120, 131, (S * S // 32,), dtype=torch.uint8, device="cuda", generator=g)
+    sb_ = torch.randint(0, 256, (S * S // 2,), dtype=torch.uint8, device="cuda", generator=g)
+    sbs = torch.randint(120, 131, (S * S // 32,), dtype=torch.uint8, device="cuda", generator=g)
+    sc = torch.empty((S, S), dtype=torch.bfloat16, device="cuda")
+    ms = back_to_back(torch, lambda i: fq.fp4_gemm_mxfp4(sa_, sas, sb_, sbs, S, S, S, out=sc), max(5, reps // 4), warm=2)
+    tf = 2.0 * S ** 3 / (ms * 1e-3) / 1e12
+    res["square_16384_bf16_out"] = {"M": S, "N": S, "K": S, "us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+                                    "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
+                                    "us_p10_median_p90_single_launch": take_spread()}
+    del sa_, sas, sb_, sbs, sc
     r = res["bf16_out"]
     res["roofline"] = {"bound": "mfma", "kernel": "k_gemm_mx_lds", "achieved": r["TFLOPs"], "peak": PEAK_FP4_TFLOPS,
                        "unit": "TFLOP/s", "frac": r["frac_fp4_peak"], "traffic": None,

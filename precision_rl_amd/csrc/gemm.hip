@@ -15,15 +15,21 @@
 // (Layout checked on the GPU against a host product of random codes and scales.)
 //
 // Main path (K % 512 == 0, scales 16-byte aligned), gemm_tile below: a
-// workgroup of 4 waves (2 x 2) computes a 256 x 192 tile of C when there are
-// enough such tiles to give every compute unit one, else 128 x 128.  K advances
-// 256 values per stage (128 bytes of codes per row, one whole cache line); both
-// operands stream from memory straight into LDS by buffer-to-LDS loads, double
-// buffered, with the pieces of each staged row permuted so that the rows lanes
-// read together sit on distinct bank groups.  Each stage is four MFMA K slices
-// whose operands are read from LDS two slices ahead.  Whole tiles of C are
-// turned around in LDS and written as 16-byte row pieces; edge tiles store
-// element by element through a buffer range that drops what lies outside C.
+// workgroup of 4 waves (2 x 2) computes a 256 x 256 or 256 x 192 tile of C,
+// whichever finishes the product in fewer tile-times counting whole rounds of
+// one tile per compute unit, or 128 x 128 when there are too few 256 x 192
+// tiles to give every compute unit one.  Tiles go out in groups of four row
+// tiles, XCD by XCD, so that the tiles one XCD runs together share operand
+// rows in its L2.  K advances 256 values per stage (128 bytes of codes per
+// row, one whole cache line); both operands stream from memory straight into
+// LDS by buffer-to-LDS loads, double buffered, with the pieces of each staged
+// row permuted so that the rows lanes read together sit on distinct bank
+// groups.  Each stage is four MFMA K slices whose operands are read from LDS
+// two slices ahead (one for 256 x 256 tiles, whose accumulators fill the
+// accumulation registers); the reads and loads are spread between the MFMAs.
+// Whole tiles of C are turned around in LDS and written as 16-byte row pieces;
+// edge tiles store element by element through a buffer range that drops what
+// lies outside C.
 // The same K loop can instead end in the MXFP4 quantization of the
 // bf16-rounded product (the producer-side epilogue): C is then not written,
 // only its codes, scales and guide bits.
@@ -192,7 +198,8 @@ __global__ __launch_bounds__(256) void k_gemm_mx_any(const GemmParams p) {
 // (one per scale block) sit in the order blk ^ swz(row), which puts the 16
 // rows that 16 consecutive lanes read at one block on 16 distinct 16-byte
 // bank groups (and any 8 consecutive rows on 8).  The scales of four stages
-// (32 bytes of a row) come in with one load per row.  Loads of rows past M or
+// (32 bytes of a row; of two stages for 256 x 256 tiles, whose LDS has no room
+// for more) come in with one load per row.  Loads of rows past M or
 // N fall outside the buffer range and return zeros.
 
 // Piece order of a staged row of 8 pieces: low 3 bits of row ^ (row >> 3).
@@ -200,17 +207,20 @@ static __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) &
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kScaleChunk = 4;   // stages whose scales one load per row brings
-
 template <int WM, int WN>
 struct LdsTile {
     static constexpr int RA = 64 * WM, RB = 64 * WN;      // rows of A and B per tile
     static constexpr int ROWS = RA + RB;                  // stacked: A rows, then B rows
     static constexpr int CODE_BYTES = ROWS * 128;         // one stage of codes
-    static constexpr int SCALE_BYTES = ROWS * 32;         // one chunk of scales (4 stages x 8 blocks)
+    // Stages whose scales one load per row brings: 4 (32 bytes of a row), or 2
+    // where double-buffered chunks of 4 would not fit in LDS beside the codes.
+    static constexpr int CHUNK = 2 * CODE_BYTES + 2 * ROWS * 32 + 4 * ((ROWS / 32 + 3) / 4) * 1024 <= 160 * 1024 ? 4 : 2;
+    static constexpr int SPITCH = 8 * CHUNK;              // bytes of a row's scales in one chunk
+    static constexpr int SROWS = 1024 / SPITCH;           // rows per wave load of scales (64 lanes x 16 bytes)
+    static constexpr int SCALE_BYTES = ROWS * SPITCH;     // one chunk of scales
     static constexpr int NCODE = ROWS / 8;                // wave loads of codes per stage (8 rows each)
     static constexpr int NCW = NCODE / 4;                 // ... per wave: 2 (WM + WN)
-    static constexpr int NSCALE = ROWS / 32;              // wave loads of scales per chunk (32 rows each)
+    static constexpr int NSCALE = ROWS / SROWS;           // wave loads of scales per chunk
     static constexpr int NSQ = (NSCALE + 3) / 4;          // scale loads every wave issues per stage
     static constexpr int BATCH = NCW + NSQ;               // loads every wave issues per stage
     // scale loads with nothing to load (not the first stage of a chunk, or
@@ -218,6 +228,7 @@ struct LdsTile {
     static constexpr int SINK_BYTES = 4 * NSQ * 1024;
     static constexpr int LDS_BYTES = 2 * CODE_BYTES + 2 * SCALE_BYTES + SINK_BYTES;
     static_assert(NCODE % 4 == 0, "code loads split evenly over the 4 waves");
+    static_assert(RA % SROWS == 0, "a wave load of scales lies within A or within B");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
 };
 
@@ -235,10 +246,18 @@ __device__ __forceinline__ void barrier_only() {
     asm volatile("" ::: "memory");
 }
 
-// 1: 256 x 192 tiles, when there are enough of them to give every compute
-// unit one; 0: 128 x 128 tiles.
+// 0: 128 x 128 tiles, when there are too few 256 x 192 tiles to give every
+// compute unit one; else 1: 256 x 192 or 2: 256 x 256 tiles, whichever
+// finishes first counting whole rounds of 256 tiles (one per compute unit) and
+// a 256 x 256 tile's time as (256 x 256) / (256 x 192) / kSpeed44 that of a
+// 256 x 192 tile (it loads 64 KiB per 64 MFMAs of each wave and stage, where
+// the 256 x 192 tile loads 56 KiB per 48).
+constexpr double kSpeed44 = 1.1;
 static int gemm_config(int64_t M, int64_t N) {
-    return ((M + 255) / 256) * ((N + 191) / 192) >= 256 ? 1 : 0;
+    const int64_t t43 = ((M + 255) / 256) * ((N + 191) / 192), t44 = ((M + 255) / 256) * ((N + 255) / 256);
+    if (t43 < 256) return 0;
+    const double r43 = (double)((t43 + 255) / 256), r44 = (double)((t44 + 255) / 256);
+    return r44 * (256.0 / 192.0) / kSpeed44 < r43 ? 2 : 1;
 }
 
 __device__ __forceinline__ int clamp31(int64_t v) { return (int)(v > 0x7FFFFFFF ? 0x7FFFFFFF : v); }
@@ -279,14 +298,15 @@ __device__ __forceinline__ void issue_stage(uint8_t* smem, const Bases& bs, cons
                                                  vo, t * 128, 0, 0);
     }
     if constexpr (PART == 2) return;
-    const bool chunk = live && (t & (kScaleChunk - 1)) == 0;
-    uint8_t* sb = smem + 2 * T::CODE_BYTES + ((t / kScaleChunk) & 1) * T::SCALE_BYTES;
+    const bool chunk = live && (t & (T::CHUNK - 1)) == 0;
+    uint8_t* sb = smem + 2 * T::CODE_BYTES + ((t / T::CHUNK) & 1) * T::SCALE_BYTES;
     uint8_t* sink = smem + 2 * T::CODE_BYTES + 2 * T::SCALE_BYTES;
     #pragma unroll
     for (int q = 0; q < T::NSQ; ++q) {
         const int j = wave + 4 * q;
         const bool real = chunk && j < T::NSCALE;
-        const __amdgpu_buffer_rsrc_t r = j < 2 * WM ? rsrc(bs.as, real ? bs.nas : 0) : rsrc(bs.bs, real ? bs.nbs : 0);
+        const __amdgpu_buffer_rsrc_t r =
+            j * T::SROWS < T::RA ? rsrc(bs.as, real ? bs.nas : 0) : rsrc(bs.bs, real ? bs.nbs : 0);
         const int so = soff[q];
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)((real ? sb : sink) + j * 1024), 16, so, t * 8, 0, 0);
     }
@@ -312,31 +332,35 @@ __device__ __forceinline__ void read_ops(const uint8_t* smem, int st, const int 
 }
 
 // Both scale words of stage st for this wave's rows (word w: blocks 4 w ..
-// 4 w + 3), moved down by 8 kc bits so that byte 2 (ks & 1) of word ks / 2 is
-// the lane's block 2 ks + kc.  One 8-byte read per row: rows lie 32 bytes
-// apart, so narrower reads would cost the same bank conflicts twice.
+// 4 w + 3).  One 8-byte read per row: rows lie 16 or 32 bytes apart, so
+// narrower reads would cost the same bank conflicts twice.
 template <int WM, int WN>
-__device__ __forceinline__ void read_scales(const uint8_t* sbase, int st, int scA, int scB, int kc,
+__device__ __forceinline__ void read_scales(const uint8_t* sbase, int st, int scA, int scB,
                                             v2u32 (&sa)[WM], v2u32 (&sb)[WN]) {
-    const uint8_t* sc = sbase + ((st / kScaleChunk) & 1) * LdsTile<WM, WN>::SCALE_BYTES + 8 * (st & (kScaleChunk - 1));
+    using T = LdsTile<WM, WN>;
+    const uint8_t* sc = sbase + ((st / T::CHUNK) & 1) * T::SCALE_BYTES + 8 * (st & (T::CHUNK - 1));
     #pragma unroll
-    for (int i = 0; i < WM; ++i) sa[i] = *reinterpret_cast<const v2u32*>(sc + scA + i * 32 * 32) >> (8 * kc);
+    for (int i = 0; i < WM; ++i) sa[i] = *reinterpret_cast<const v2u32*>(sc + scA + i * 32 * T::SPITCH);
     #pragma unroll
-    for (int j = 0; j < WN; ++j) sb[j] = *reinterpret_cast<const v2u32*>(sc + scB + j * 32 * 32) >> (8 * kc);
+    for (int j = 0; j < WN; ++j) sb[j] = *reinterpret_cast<const v2u32*>(sc + scB + j * 32 * T::SPITCH);
 }
 
-// The WM x WN MFMAs of K slice KS with the stage's scale words ua, ub.
+// The WM x WN MFMAs of K slice KS with the stage's scale words ua, ub, each
+// moved down by 8 kc bits here, at its use, so that byte 2 (KS & 1) of word
+// KS / 2 is the lane's block 2 KS + kc.  (Shifted where they are read, the
+// words of the next stage would make the MFMAs that follow the read wait for
+// it.)
 template <int WM, int WN, int KS>
 __device__ __forceinline__ void mfmas(v16f (&acc)[WM][WN], const v4u32 (&a)[WM], const v4u32 (&b)[WN],
-                                      const v2u32 (&ua)[WM], const v2u32 (&ub)[WN]) {
+                                      const v2u32 (&ua)[WM], const v2u32 (&ub)[WN], int kc) {
     #pragma unroll
     for (int i = 0; i < WM; ++i) {
         const v8i av = (v8i){(int)a[i].x, (int)a[i].y, (int)a[i].z, (int)a[i].w, 0, 0, 0, 0};
-        const int sa = (int)(KS < 2 ? ua[i].x : ua[i].y);
+        const int sa = (int)((KS < 2 ? ua[i].x : ua[i].y) >> (8 * kc));
         #pragma unroll
         for (int j = 0; j < WN; ++j) {
             const v8i bv = (v8i){(int)b[j].x, (int)b[j].y, (int)b[j].z, (int)b[j].w, 0, 0, 0, 0};
-            const int sb = (int)(KS < 2 ? ub[j].x : ub[j].y);
+            const int sb = (int)((KS < 2 ? ub[j].x : ub[j].y) >> (8 * kc));
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 4, 4, 2 * (KS & 1), sa,
                                                                       2 * (KS & 1), sb);
         }
@@ -429,6 +453,22 @@ __device__ __forceinline__ void quantize_epilogue(const GemmParams& p, const v16
     }
 }
 
+// Instruction order of a K-loop region: its NM MFMAs spread out, the first ND
+// of them each followed by one LDS read and the first NV by one memory load
+// (PER > 0: the LDS reads go with the first ND of every PER MFMAs instead), so
+// that the wave issues its reads and loads while the matrix core works, not
+// in batches that leave it idle.
+template <int NM, int ND, int NV, int PER = 0>
+__device__ __forceinline__ void interleave() {
+    #pragma unroll
+    for (int k = 0; k < NM; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (PER ? (k % PER) < ND : k < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (k < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    if (NV > NM) __builtin_amdgcn_sched_group_barrier(0x020, NV > NM ? NV - NM : 1, 0);
+}
+
 // Tile (tm, tn) of the product p, computed by the calling workgroup.  QUANT: the
 // epilogue quantizes the bf16-rounded tile (p.qcodes, p.qscales, p.qbits)
 // instead of storing C.
@@ -463,8 +503,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint
     #pragma unroll
     for (int q = 0; q < T::NSQ; ++q) {
         const int j = wave + 4 * q;
-        const int row = 32 * j + (lane >> 1);
-        soff[q] = (int)((j < 2 * WM ? row : row - T::RA) * srow) + 16 * (lane & 1);
+        constexpr int LPR = T::SPITCH / 16;                            // lanes per row of a scale load
+        const int row = T::SROWS * j + lane / LPR;
+        soff[q] = (int)((row < T::RA ? row : row - T::RA) * srow) + 16 * (lane % LPR);
     }
 
     v16f acc[WM][WN];
@@ -491,10 +532,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint
         for (int par = 0; par < 2; ++par)
             roff[ks][par] = r32 * 128 + 16 * ((2 * ks + kc) ^ ((r32 ^ (r32 >> 3)) & 7) ^ (4 * par));
     const int rowA0 = wm * WM, rowB0 = T::RA / 32 + wn * WN;   // first 32-row blocks of this wave
-    const int scA = (wm * 32 * WM + r32) * 32, scB = (T::RA + wn * 32 * WN + r32) * 32;
+    const int scA = (wm * 32 * WM + r32) * T::SPITCH, scB = (T::RA + wn * 32 * WN + r32) * T::SPITCH;
 
-    // operand sets for K slices 0..3 of a stage (read two slices ahead of their MFMAs)
-    v4u32 a0[WM], b0[WN], a1[WM], b1[WN], a2[WM], b2[WN], a3[WM], b3[WN];
     v2u32 sa[WM], sb[WN], na[WM], nb[WN];   // scale words of this stage and the next
     const uint8_t* sbase = smem + 2 * T::CODE_BYTES;
 
@@ -503,47 +542,87 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint
     // stage 0 is in once only stage 1's loads remain (loads complete in order)
     __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(T::BATCH));
     barrier_only();
-    read_scales<WM, WN>(sbase, 0, scA, scB, kc, sa, sb);
-    read_ops<WM, WN, 0>(smem, 0, roff, rowA0, rowB0, a0, b0);
-    read_ops<WM, WN, 1>(smem, 0, roff, rowA0, rowB0, a1, b1);
-    for (int s = 0; s + 1 < steps; ++s) {
+    read_scales<WM, WN>(sbase, 0, scA, scB, sa, sb);
+    if constexpr (WM * WN >= 16) {
+        // 256 x 256 tiles: the accumulators fill the 256 accumulation registers,
+        // so operands are read one slice ahead of their MFMAs into two sets (a
+        // slice is 16 MFMAs per wave, 512 cycles, ample for the LDS reads); the
+        // barrier comes after the third slice's MFMAs.
+        v4u32 xa[WM], xb[WN], ya[WM], yb[WN];
+        read_ops<WM, WN, 0>(smem, 0, roff, rowA0, rowB0, xa, xb);
+        // stage s with scale words (ca, cb), reading stage s + 1's into (xa_, xb_): the two sets
+        // alternate between stages, so that no copy waits for a read
+        auto stage = [&](int s, v2u32 (&ca)[WM], v2u32 (&cb)[WN], v2u32 (&na_)[WM], v2u32 (&nb_)[WN]) {
+            read_ops<WM, WN, 1>(smem, s, roff, rowA0, rowB0, ya, yb);
+            mfmas<WM, WN, 0>(acc, xa, xb, ca, cb, kc);
+            read_ops<WM, WN, 2>(smem, s, roff, rowA0, rowB0, xa, xb);
+            mfmas<WM, WN, 1>(acc, ya, yb, ca, cb, kc);
+            read_ops<WM, WN, 3>(smem, s, roff, rowA0, rowB0, ya, yb);
+            mfmas<WM, WN, 2>(acc, xa, xb, ca, cb, kc);
+            interleave<3 * WM * WN, WM + WN, 0, WM * WN>();
+            // as below: stage s read and stage s + 1 in, for every wave after the barrier
+            __builtin_amdgcn_s_waitcnt(FP4Q_LGKMCNT0);
+            __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
+            barrier_only();
+            read_scales<WM, WN>(sbase, s + 1, scA, scB, na_, nb_);
+            read_ops<WM, WN, 0>(smem, s + 1, roff, rowA0, rowB0, xa, xb);
+            issue_stage<WM, WN, 1>(smem, bs, voff, soff, wave, s + 2, steps);
+            mfmas<WM, WN, 3>(acc, ya, yb, ca, cb, kc);
+            issue_stage<WM, WN, 2>(smem, bs, voff, soff, wave, s + 2, steps);
+            interleave<WM * WN, WM + WN + (WM + WN + 1) / 2, LdsTile<WM, WN>::BATCH>();
+        };
+        int s = 0;
+        for (; s + 2 < steps; s += 2) {
+            stage(s, sa, sb, na, nb);
+            stage(s + 1, na, nb, sa, sb);
+        }
+        stage(s, sa, sb, na, nb);   // s = steps - 2: stage steps - 1 has its scales in (na, nb)
+        s = steps - 1;
+        read_ops<WM, WN, 1>(smem, s, roff, rowA0, rowB0, ya, yb);
+        mfmas<WM, WN, 0>(acc, xa, xb, na, nb, kc);
+        read_ops<WM, WN, 2>(smem, s, roff, rowA0, rowB0, xa, xb);
+        mfmas<WM, WN, 1>(acc, ya, yb, na, nb, kc);
+        read_ops<WM, WN, 3>(smem, s, roff, rowA0, rowB0, ya, yb);
+        mfmas<WM, WN, 2>(acc, xa, xb, na, nb, kc);
+        mfmas<WM, WN, 3>(acc, ya, yb, na, nb, kc);
+    } else {
+        // operand sets for K slices 0..3 of a stage (read two slices ahead of their MFMAs)
+        v4u32 a0[WM], b0[WN], a1[WM], b1[WN], a2[WM], b2[WN], a3[WM], b3[WN];
+        read_ops<WM, WN, 0>(smem, 0, roff, rowA0, rowB0, a0, b0);
+        read_ops<WM, WN, 1>(smem, 0, roff, rowA0, rowB0, a1, b1);
+        auto stage = [&](int s, v2u32 (&ca)[WM], v2u32 (&cb)[WN], v2u32 (&na_)[WM], v2u32 (&nb_)[WN]) {
+            read_ops<WM, WN, 2>(smem, s, roff, rowA0, rowB0, a2, b2);
+            mfmas<WM, WN, 0>(acc, a0, b0, ca, cb, kc);
+            read_ops<WM, WN, 3>(smem, s, roff, rowA0, rowB0, a3, b3);
+            mfmas<WM, WN, 1>(acc, a1, b1, ca, cb, kc);
+            interleave<2 * WM * WN, 2 * (WM + WN), 0>();
+            // this wave's reads of stage s and its loads of stage s + 1 are done; after
+            // the barrier every wave's are, so stage s + 2 may load into stage s's buffers
+            __builtin_amdgcn_s_waitcnt(FP4Q_LGKMCNT0);
+            __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
+            barrier_only();
+            read_scales<WM, WN>(sbase, s + 1, scA, scB, na_, nb_);
+            read_ops<WM, WN, 0>(smem, s + 1, roff, rowA0, rowB0, a0, b0);
+            issue_stage<WM, WN, 1>(smem, bs, voff, soff, wave, s + 2, steps);
+            mfmas<WM, WN, 2>(acc, a2, b2, ca, cb, kc);
+            read_ops<WM, WN, 1>(smem, s + 1, roff, rowA0, rowB0, a1, b1);
+            issue_stage<WM, WN, 2>(smem, bs, voff, soff, wave, s + 2, steps);
+            mfmas<WM, WN, 3>(acc, a3, b3, ca, cb, kc);
+            interleave<2 * WM * WN, 2 * (WM + WN) + (WM + WN + 1) / 2, LdsTile<WM, WN>::BATCH>();
+        };
+        int s = 0;
+        for (; s + 2 < steps; s += 2) {
+            stage(s, sa, sb, na, nb);
+            stage(s + 1, na, nb, sa, sb);
+        }
+        stage(s, sa, sb, na, nb);   // s = steps - 2: stage steps - 1 has its scales in (na, nb)
+        s = steps - 1;
         read_ops<WM, WN, 2>(smem, s, roff, rowA0, rowB0, a2, b2);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas<WM, WN, 0>(acc, a0, b0, sa, sb);
-        __builtin_amdgcn_sched_barrier(0);
         read_ops<WM, WN, 3>(smem, s, roff, rowA0, rowB0, a3, b3);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas<WM, WN, 1>(acc, a1, b1, sa, sb);
-        __builtin_amdgcn_sched_barrier(0);
-        // this wave's reads of stage s and its loads of stage s + 1 are done; after
-        // the barrier every wave's are, so stage s + 2 may load into stage s's buffers
-        __builtin_amdgcn_s_waitcnt(FP4Q_LGKMCNT0);
-        __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
-        barrier_only();
-        read_scales<WM, WN>(sbase, s + 1, scA, scB, kc, na, nb);
-        read_ops<WM, WN, 0>(smem, s + 1, roff, rowA0, rowB0, a0, b0);
-        issue_stage<WM, WN, 1>(smem, bs, voff, soff, wave, s + 2, steps);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas<WM, WN, 2>(acc, a2, b2, sa, sb);
-        __builtin_amdgcn_sched_barrier(0);
-        read_ops<WM, WN, 1>(smem, s + 1, roff, rowA0, rowB0, a1, b1);
-        issue_stage<WM, WN, 2>(smem, bs, voff, soff, wave, s + 2, steps);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas<WM, WN, 3>(acc, a3, b3, sa, sb);
-        __builtin_amdgcn_sched_barrier(0);
-        #pragma unroll
-        for (int i = 0; i < WM; ++i) sa[i] = na[i];
-        #pragma unroll
-        for (int j = 0; j < WN; ++j) sb[j] = nb[j];
-    }
-    {
-        const int s = steps - 1;
-        read_ops<WM, WN, 2>(smem, s, roff, rowA0, rowB0, a2, b2);
-        read_ops<WM, WN, 3>(smem, s, roff, rowA0, rowB0, a3, b3);
-        mfmas<WM, WN, 0>(acc, a0, b0, sa, sb);
-        mfmas<WM, WN, 1>(acc, a1, b1, sa, sb);
-        mfmas<WM, WN, 2>(acc, a2, b2, sa, sb);
-        mfmas<WM, WN, 3>(acc, a3, b3, sa, sb);
+        mfmas<WM, WN, 0>(acc, a0, b0, na, nb, kc);
+        mfmas<WM, WN, 1>(acc, a1, b1, na, nb, kc);
+        mfmas<WM, WN, 2>(acc, a2, b2, na, nb, kc);
+        mfmas<WM, WN, 3>(acc, a3, b3, na, nb, kc);
     }
     // the loads issued past the last stage must land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
@@ -624,11 +703,30 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t remap) {
     return bid;
 }
 
+constexpr uint32_t kGroupM = 4;   // row tiles per group of the tile order
+
+// Tile (tm, tn) of the bid-th tile in the order that hands tiles out in groups
+// of kGroupM row tiles, column by column within a group: the 8 kGroupM
+// consecutive tiles an XCD runs at a time (4 x 8 of them for 256 x 192
+// tiles) then read 4 row blocks of A and 8 of B, where a row-major order would
+// read one or two of A and 32 of B, three times the bytes that reach its L2
+// from memory per stage.
+__device__ __forceinline__ void grouped_tile(uint32_t bid, uint32_t tiles_m, uint32_t tiles_n, uint32_t& tm,
+                                             uint32_t& tn) {
+    const uint32_t per = kGroupM * tiles_n;
+    const uint32_t grp = bid / per, first = grp * kGroupM;
+    const uint32_t rows = min(tiles_m - first, kGroupM);
+    const uint32_t r = bid - grp * per;
+    tm = first + r % rows;
+    tn = r / rows;
+}
+
 template <int WM, int WN, bool BF16, bool QUANT = false>
 __global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const uint32_t bid = xcd_tile(p.xcd_remap);
-    const uint32_t tm = bid / p.tiles_n, tn = bid - tm * p.tiles_n;
+    uint32_t tm, tn;
+    grouped_tile(bid, gridDim.x / p.tiles_n, p.tiles_n, tm, tn);
     gemm_tile<WM, WN, BF16, QUANT>(p, tm, tn, smem);
 }
 
@@ -710,15 +808,21 @@ hipError_t launch_gemm_mx_grouped(bool bf16_out, const GroupedGemmParams& gp, hi
 bool gemm_quant_supported(const GemmParams& p) { return main_path_ok(p); }
 
 hipError_t launch_gemm_mx_quant(const GemmParams& p, hipStream_t s) {
-    if (gemm_config(p.M, p.N) == 1) return launch_lds<4, 3>(true, p, s, true);
-    return launch_lds<2, 2>(true, p, s, true);
+    switch (gemm_config(p.M, p.N)) {
+        case 2: return launch_lds<4, 4>(true, p, s, true);
+        case 1: return launch_lds<4, 3>(true, p, s, true);
+        default: return launch_lds<2, 2>(true, p, s, true);
+    }
 }
 
 hipError_t launch_gemm_mx(bool bf16_out, const GemmParams& p, hipStream_t s) {
     // main path: K a multiple of 512 (whole stages and 16-byte aligned scale loads)
     if (main_path_ok(p)) {
-        if (gemm_config(p.M, p.N) == 1) return launch_lds<4, 3>(bf16_out, p, s);
-        return launch_lds<2, 2>(bf16_out, p, s);
+        switch (gemm_config(p.M, p.N)) {
+            case 2: return launch_lds<4, 4>(bf16_out, p, s);
+            case 1: return launch_lds<4, 3>(bf16_out, p, s);
+            default: return launch_lds<2, 2>(bf16_out, p, s);
+        }
     }
     const bool scale4 = p.K % 128 == 0 && ((uintptr_t)p.as & 3) == 0 && ((uintptr_t)p.bs & 3) == 0;
     GemmParams q = p;

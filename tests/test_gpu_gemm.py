@@ -186,6 +186,53 @@ def test_large_tiles_ragged_sampled(fq):
         check(got[:, cols], e_cols, m_cols, K, bf, f"large tiles cols {dtype}")
 
 
+@pytest.mark.parametrize("pad", [40, 3])
+def test_256x256_tiles_ragged_sampled(fq, pad):
+    # 4000 x 4000 makes 256 tiles of 256 x 256 (one round) against 336 of 256 x 192 (two), so the
+    # 256 x 256 configuration runs, with ragged last tiles in M and N.  Rows padded by 40 elements
+    # keep every row 16-byte aligned (whole tiles go through LDS); a padding of 3 does not (every
+    # tile stores element by element).  The padding holds a sentinel no store may touch.
+    M, N, K = 4000, 4000, 512
+    say(f"gemm 256x256 tiles M={M} N={N} K={K} pad={pad}")
+    a, asc = W.mx_operand(M, K, seed=61, stream=0)
+    b, bsc = W.mx_operand(N, K, seed=62, stream=0)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([rng.choice(M, 24, replace=False), np.arange(M - 8, M), np.arange(0, 4),
+                                     np.arange(3840, 3844)]))
+    cols = np.unique(np.concatenate([rng.choice(N, 24, replace=False), np.arange(N - 8, N), np.arange(0, 4),
+                                     np.arange(3840, 3844)]))
+    e_rows, m_rows = O.gemm_mx(a[rows], asc[rows], b, bsc, len(rows), N, K)
+    e_cols, m_cols = O.gemm_mx(a, asc, b[cols], bsc[cols], M, len(cols), K)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).ravel()).cuda()
+    for dtype in (torch.float32, torch.bfloat16):
+        buf = torch.full((M, N + pad), -7.0, dtype=dtype, device="cuda")
+        fq.fp4_gemm_mxfp4(dev(a), dev(asc), dev(b), dev(bsc), M, N, K, out=buf[:, :N])
+        torch.cuda.synchronize()
+        h = buf.float().cpu().numpy()
+        assert (h[:, N:] == -7.0).all(), "the product wrote past N in a padded row"
+        got = h[:, :N].astype(np.float64)
+        bf = dtype == torch.bfloat16
+        check(got[rows], e_rows, m_rows, K, bf, f"256x256 rows {dtype}")
+        check(got[:, cols], e_cols, m_cols, K, bf, f"256x256 cols {dtype}")
+
+
+def test_square_16384_sampled(fq):
+    # the square product bench.py times (256 x 256 tiles, 16 rounds): 8 sampled rows x all columns and
+    # all rows x 8 sampled columns, bf16 out
+    M = N = K = 16384
+    say(f"gemm square M={M} N={N} K={K}")
+    a, asc = W.mx_operand(M, K, seed=71, stream=0)
+    b, bsc = W.mx_operand(N, K, seed=72, stream=0)
+    rng = np.random.default_rng(13)
+    rows = np.sort(np.concatenate([rng.choice(M - 2, 6, replace=False), [M - 2, M - 1]]))
+    cols = np.sort(np.concatenate([rng.choice(N - 2, 6, replace=False), [N - 2, N - 1]]))
+    e_rows, m_rows = O.gemm_mx(a[rows], asc[rows], b, bsc, len(rows), N, K)
+    e_cols, m_cols = O.gemm_mx(a, asc, b[cols], bsc[cols], M, len(cols), K)
+    got = run(fq, a, asc, b, bsc, M, N, K, torch.bfloat16)
+    check(got[rows], e_rows, m_rows, K, True, "square rows")
+    check(got[:, cols], e_cols, m_cols, K, True, "square cols")
+
+
 def test_full_size_expert_gemm_sampled(fq):
     # the benchmark's product: activations [8192, 4096] x expert weight [1536, 4096]^T, bf16 and fp32 out;
     # 64 sampled rows x all columns and all rows x 48 sampled columns checked against the oracle

@@ -7,8 +7,9 @@ Oracle parity uses operands whose products and partial sums are exact in fp32
 (E8M0 scales 126..128: every product is a multiple of 2^-4 of magnitude at most
 144, so any sum of up to 4096 of them is exact), so the oracle alone fixes C, its
 bf16 rounding and its quantization, whatever order the matrix cores sum in.
-Shapes cover both tile configurations (128 x 128 and 256 x 192), partial tiles
-in M and N, and the full 8192 x 1536 x 4096 product (sampled rows).  On
+Shapes cover the three tile configurations (128 x 128, 256 x 192 and, for
+4000 x 4000, 256 x 256), partial tiles in M and N, and the full
+8192 x 1536 x 4096 product (sampled rows).  On
 Gaussian activations and weights quantized by the library, the fused kernel
 equals the plain product with bf16 output followed by fp4_quantize, bit for bit
 over whole tensors.  Outputs start as 0xA5 bytes.
@@ -45,7 +46,7 @@ def sample(M, k=24, seed=0):
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 192, 512), (300, 160, 1024), (1, 32, 512), (129, 992, 1536),
-                                   (8192, 1536, 4096)])
+                                   (8192, 1536, 4096), (4000, 4000, 512)])
 def test_fused_quantize_vs_oracle_on_exact_products(fq, M, N, K):
     a, asc = W.mx_operand(M, K, seed=M + 7, stream=0, scale_lo=126, scale_hi=128)
     b, bsc = W.mx_operand(N, K, seed=N + 9, stream=2, scale_lo=126, scale_hi=128)
@@ -69,7 +70,7 @@ def test_fused_quantize_vs_oracle_on_exact_products(fq, M, N, K):
         assert (gb[r] == wb).all(), ("bits", r)
 
 
-@pytest.mark.parametrize("M,N,K", [(8192, 1536, 4096), (1000, 608, 2048), (256, 192, 512)])
+@pytest.mark.parametrize("M,N,K", [(8192, 1536, 4096), (1000, 608, 2048), (256, 192, 512), (4000, 4000, 1024)])
 def test_fused_equals_product_then_quantize(fq, M, N, K):
     cfg = fq.Fp4Config(format=fq.MXFP4)
     xa = W.f32_to_bf16_rne(W.normal_outliers_f32(M, K, 1020, 16, 0.0, 1.0))
