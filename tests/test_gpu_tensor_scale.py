@@ -1,7 +1,10 @@
 """The one-launch tensor scale (fp4_tensor_scale_ws) equals the oracle's tensor
 scale and the three-launch fp4_tensor_scale bit for bit: small and large
 tensors (both launch shapes, one pass of up to 512 workgroups and the
-grid-stride form with 1024), ragged tails, padded rows, the RHT, both grids,
+grid-stride form with 1024), every grid size from 1 to 18 workgroups (the
+eight reduction slots with zero to three arrivals each) and others up to the
+1024 cap, with and without a one-group last workgroup, ragged tails, padded
+rows, the RHT, both grids,
 all-zero, empty and non-finite inputs.  One workspace serves every call in
 turn: each call leaves its maxima and arrival counters at 0.  A captured graph of calls
 replays equal to eager calls."""
@@ -66,6 +69,27 @@ def test_one_launch_tensor_scale_vs_oracle(fq, ws, rht, grid, shape, pad):
     want = np.float32(O.tensor_scale(oc, xh)).view(np.uint32)
     assert bits(got) == want
     assert bits(three) == want
+    assert counters_zero(ws)
+
+
+@pytest.mark.parametrize("k", list(range(1, 19)) + [63, 64, 65, 1023, 1024, 1100])
+@pytest.mark.parametrize("tail", [False, True])
+def test_one_launch_tensor_scale_grid_sizes(fq, ws, k, tail):
+    # a workgroup covers 1024 groups of 16 (16384 elements), so k rows of 16384 make k workgroups
+    # (at most 1024): slot b mod 8 of the reduction gets ceil((k - b) / 8) arrivals, and slots past
+    # k - 1 none.  With the tail the last row is one group long, so the last workgroup holds a
+    # single group.  The largest value sits in the last workgroup.
+    cols = 16384
+    xh = W.c1_x(k, cols, seed=k)
+    if tail:
+        xh = xh.copy()
+        xh[-1, 16:] = 0
+        xh[-1, 3] = W.f32_to_bf16_rne(np.array([[-977.0]], dtype=np.float32))[0, 0]
+    n = (k - 1) * cols + (16 if tail else cols)
+    flat = np.ascontiguousarray(xh).reshape(-1)[:n].reshape(1, n)
+    cfg = fq.Fp4Config()
+    got = fq.fp4_tensor_scale_ws(dev(flat), cfg, ws)
+    assert bits(got) == np.float32(O.tensor_scale(O.Cfg(), flat)).view(np.uint32)
     assert counters_zero(ws)
 
 
