@@ -534,6 +534,16 @@ def wl_c1(args, fq, torch, W, ceiling):
     ms, ok = graph_time(torch, lambda i: ts_rtn(i, False), gr, ts_rtn_check)
     r["tensor_scale_three_launches_plus_rtn_graph"] = dict(report(ms, 4.5625 * n, n, ceiling),
                                                            replays_match_eager=ok, launches=4)
+    # both in one launch (fp4_quantize_with_tensor_scale): each workgroup reduces the maximum of its
+    # own chunk, waits for s_t and quantizes the chunk it has just read; the same algorithmic bytes as
+    # the rows above, of which it reads x from HBM once
+    fq.fp4_quantize_with_tensor_scale(xs[0], cfg, ws, ts=tso[0], codes=oc[0], scales=os_[0])
+    fused_launches = fq.last_launches
+    ms, ok = graph_time(torch, lambda i: fq.fp4_quantize_with_tensor_scale(xs[i % P], cfg, ws, ts=tso[i % R],
+                                                                           codes=oc[i % R], scales=os_[i % R]),
+                        gr, ts_rtn_check)
+    r["tensor_scale_and_rtn_one_launch_graph"] = dict(report(ms, 4.5625 * n, n, ceiling), replays_match_eager=ok,
+                                                      launches=fused_launches)
     return r
 
 
@@ -679,7 +689,7 @@ def other_workloads(args, fq, torch, W, ceiling, names=("c1", "c3", "c4", "c5"))
 
 # the main kernel of each workload, whose roofline a single-workload run reports
 ROOFLINE_KERNEL = {
-    "c1": "tensor_scale_plus_rtn_graph",
+    "c1": "tensor_scale_and_rtn_one_launch_graph",
     "c3": "quantize_kv_grouped",
     "c4": "trainer_guided_grouped",
     "c5": "quantize_rht_sr_uniform",

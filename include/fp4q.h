@@ -140,6 +140,33 @@ fp4_status fp4_quantize(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, in
                         int64_t ld, const float* tensor_scale, void* codes, void* scales,
                         void* guide_bits_out, hipStream_t stream);
 
+/* NVFP4 tensor scale and block quantization of one tensor together
+ * [FQT-FP4 §3 E4M3 block scales under one fp32 tensor scale]: writes s_t to
+ * tensor_scale_out exactly as fp4_tensor_scale does, and codes, scales (and the
+ * guide bits when guide_bits_out is not NULL) exactly as fp4_quantize does with
+ * that s_t, RTN or SR.  Without the RHT, and when the device holds every
+ * workgroup of the launch at once (up to 2048 workgroups of 512 groups on an
+ * MI355X: about 16.7M elements), this is one launch: each workgroup reduces the
+ * maximum of its own chunk into `workspace`, waits for the last one to publish
+ * s_t, and quantizes the chunk it has just read.  Otherwise it is
+ * fp4_tensor_scale_ws followed by fp4_quantize (two launches).
+ *   cfg              NVFP4 (MXFP4: FP4_ERR_UNSUPPORTED), RTN or SR.
+ *   workspace        as for fp4_tensor_scale_ws: at least
+ *                    FP4_TENSOR_SCALE_WORKSPACE_BYTES, 256-byte aligned, zero-filled
+ *                    before first use; concurrent calls need their own.  Every call
+ *                    leaves its reduction words zeroed; the one-launch form also keeps
+ *                    the last scale it published and a phase bit there, for the next
+ *                    call (zero-filling the workspace again is always valid).
+ *   launches         NULL, or receives 1 or 2, the number of launches enqueued.
+ * The one-launch form needs all its workgroups running together: work that
+ * keeps compute units busy for more than about a second while it runs (another
+ * stream) makes the waiting workgroups give up, with NaN scales in their part of
+ * the output. */
+fp4_status fp4_quantize_with_tensor_scale(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
+                                          int64_t ld, float* tensor_scale_out, void* codes, void* scales,
+                                          void* guide_bits_out, void* workspace, size_t workspace_bytes,
+                                          int* launches, hipStream_t stream);
+
 /* Rollout-guided quantization [TRACE-JA "TRACEの仕組み"; TRACE-KO]: the
  * block scale (and NVFP4 tensor scale) come from the guide; each element is
  * rounded to the one of its two bracketing codewords whose LSB equals its

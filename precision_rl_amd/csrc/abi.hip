@@ -214,6 +214,44 @@ fp4_status fp4_quantize(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, in
                            guide_bits_out, nullptr, nullptr, stream);
 }
 
+fp4_status fp4_quantize_with_tensor_scale(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
+                                          int64_t ld, float* tensor_scale_out, void* codes, void* scales,
+                                          void* guide_bits_out, void* workspace, size_t workspace_bytes,
+                                          int* launches, hipStream_t stream) {
+    FP4Q_TRY(check_cfg(cfg));
+    if (cfg->format != FP4_NVFP4) return fail(FP4_ERR_UNSUPPORTED, "the tensor scale belongs to the NVFP4 format");
+    uint64_t ng = 0;
+    FP4Q_TRY(check_matrix(rows, cols, ld, 16, x_bf16, &ng));
+    FP4Q_TRY(need(tensor_scale_out, 4, "tensor_scale_out"));
+    FP4Q_TRY(need(workspace, 256, "workspace"));
+    if (workspace_bytes < fp4q::kTsWorkspaceBytes)
+        return fail(FP4_ERR_ARG, "workspace_bytes=%zu < %zu", workspace_bytes, fp4q::kTsWorkspaceBytes);
+    if (ng > 0) {
+        FP4Q_TRY(need(codes, 16, "codes"));
+        FP4Q_TRY(need(scales, 1, "scales"));
+        if (guide_bits_out) FP4Q_TRY(need(guide_bits_out, 16, "guide_bits_out"));
+    }
+    fp4q::QuantParams p{};
+    p.x = static_cast<const uint16_t*>(x_bf16);
+    p.ld = ld;
+    p.ngroups = (uint32_t)ng;
+    p.gpr = fp4q::make_fastdiv(cols > 0 ? (uint32_t)(cols / 16) : 1u);
+    p.codes = static_cast<uint8_t*>(codes);
+    p.scales = static_cast<uint8_t*>(scales);
+    p.bits_out = static_cast<uint8_t*>(guide_bits_out);
+    p.key0 = (uint32_t)cfg->sr_seed;
+    p.key1 = (uint32_t)(cfg->sr_seed >> 32);
+    p.sr_offset = cfg->sr_offset;
+    p.rht_seed = cfg->rht_seed;
+    const int mode = cfg->rounding == FP4_SR ? fp4q::MODE_SR : fp4q::MODE_RTN;
+    bool fused = false;
+    const hipError_t e = fp4q::launch_quantize_with_scale(cfg->grid, mode, cfg->rht16 != 0, guide_bits_out != nullptr,
+                                                          ld == cols, p, tensor_scale_out,
+                                                          static_cast<uint32_t*>(workspace), &fused, stream);
+    if (launches) *launches = fused ? 1 : (ng > 0 ? 2 : 1);
+    return hip_status(e, "fp4_quantize_with_tensor_scale launch");
+}
+
 fp4_status fp4_quantize_grouped(const fp4_cfg* cfg, int guided, int n, const fp4_tensor* tensors,
                                 hipStream_t stream) {
     FP4Q_TRY(check_cfg(cfg));

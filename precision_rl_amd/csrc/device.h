@@ -623,4 +623,45 @@ __device__ __forceinline__ uint32_t amax_bits16(const uint32_t w[8]) {
     return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
+// ---------------------------------------------------------------- cross-workgroup maximum
+// Maximum of m over a workgroup of WAVES waves, valid in thread 0.  red: WAVES
+// words of LDS.
+template <int WAVES = 4>
+__device__ __forceinline__ uint32_t wg_max_t0(uint32_t m, uint32_t* red) {
+    #pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        #pragma unroll
+        for (int i = 1; i < WAVES; ++i) m = max(m, red[i]);
+    }
+    return m;
+}
+
+// NVFP4 tensor scale from the bits of the largest finite |y|: amax / RN(Gmax * 448),
+// or 1 for an all-zero tensor.
+__device__ __forceinline__ float ts_from_amax(uint32_t amax_bits, float gmax448) {
+    const float a = __uint_as_float(amax_bits);
+    return a == 0.0f ? 1.0f : a / gmax448;
+}
+
+// Relaxed, agent-scope, returning atomics on the words of a reduction workspace
+// shared by the workgroups of one launch: each returns only once performed at
+// the L2, so a later atomic of the same thread cannot overtake it.
+__device__ __forceinline__ uint32_t fetch_max_agent(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t take_agent(uint32_t* p) {
+    return __hip_atomic_exchange(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Returns true for the arrival that completes the count n (the counter is then 0 again).
+__device__ __forceinline__ bool arrive(uint32_t* ctr, uint32_t n) {
+    return __builtin_amdgcn_atomic_inc32(ctr, n - 1u, __ATOMIC_RELAXED, "agent") == n - 1u;
+}
+// Makes the atomic that produced v complete (its value is in a register) before
+// any later memory operation is issued.
+__device__ __forceinline__ void completed(uint32_t v) { asm volatile("" ::"v"(v) : "memory"); }
+
+
 }  // namespace fp4q

@@ -110,7 +110,11 @@ struct AmaxParams {
 // Workspace of the one-launch tensor scale, in 32-bit words from a 256-byte
 // aligned base, each word on a 256-byte line of its own: the slot maxima and
 // slot arrival counters (kTsSlots of each), the top maximum and the top counter.
-// All must be 0 before the first call; every completed call leaves them 0.
+// All must be 0 before the first call; every completed call leaves them 0.  The
+// fused tensor scale and quantize adds two published-scale words and a phase
+// word: call k publishes s_t (its bits, never 0) in scale word phase and clears
+// the other one, which call k - 1 published, then flips the phase.  Zero is a
+// valid state of these three too, so a zero-filled workspace suits every call.
 constexpr uint32_t kTsSlots = 8;
 constexpr uint32_t kTsLine = 64;                        // words per 256-byte line
 constexpr uint32_t kTsMaxWorkgroups = 1024;
@@ -118,8 +122,11 @@ constexpr uint32_t kTsSlotMax = 0;
 constexpr uint32_t kTsSlotCtr = kTsSlots * kTsLine;
 constexpr uint32_t kTsTopMax = 2 * kTsSlots * kTsLine;
 constexpr uint32_t kTsTopCtr = kTsTopMax + kTsLine;
-constexpr uint32_t kTsWords = kTsTopCtr + kTsLine;
+constexpr uint32_t kTsScale = kTsTopCtr + kTsLine;     // two words, kTsLine apart
+constexpr uint32_t kTsPhase = kTsScale + 2 * kTsLine;
+constexpr uint32_t kTsWords = kTsPhase + kTsLine;
 constexpr size_t kTsWorkspaceBytes = 8192;
+constexpr int kMaxDevices = 64;                         // devices whose per-device state the library keeps
 static_assert(kTsWords * 4 <= kTsWorkspaceBytes, "tensor-scale workspace layout");
 
 struct EncodeParams {
@@ -165,6 +172,13 @@ hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams
 // One-launch tensor scale with its workspace (kTsWorkspaceBytes, 256-byte aligned, counters 0).
 hipError_t launch_tensor_scale_1(int grid, bool rht, bool contig, const AmaxParams& p, uint32_t* ws,
                                  hipStream_t s);
+// NVFP4 tensor scale and quantization (RTN or SR) of one tensor: one launch when
+// there is no RHT and the device can hold every workgroup of it at once, else
+// the one-launch tensor scale followed by the quantize launch.  p.ts is ignored
+// (the scale goes to ts_out); ws as for launch_tensor_scale_1.  *fused reports
+// which.
+hipError_t launch_quantize_with_scale(int grid, int mode, bool rht, bool emit, bool contig, const QuantParams& p,
+                                      float* ts_out, uint32_t* ws, bool* fused, hipStream_t s);
 // Device address of the library's static tensor-scale workspace (kTsWorkspaceBytes)
 // on the current device, looked up once per device; NULL with the error in *err
 // when the lookup fails.

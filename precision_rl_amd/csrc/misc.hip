@@ -91,29 +91,11 @@ __device__ __forceinline__ uint32_t amax_thread(const AmaxParams& p) {
     return m;
 }
 
-// Maximum of m over the workgroup, valid in thread 0.  red: kThreads/64 words of LDS.
-__device__ __forceinline__ uint32_t wg_max_t0(uint32_t m, uint32_t* red) {
-    #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        #pragma unroll
-        for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
-    }
-    return m;
-}
-
 template <bool RHT, bool CONTIG, int U>
 __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
     __shared__ uint32_t red[kThreads / 64];
-    const uint32_t m = wg_max_t0(amax_thread<RHT, CONTIG, U>(p), red);
+    const uint32_t m = wg_max_t0<kThreads / 64>(amax_thread<RHT, CONTIG, U>(p), red);
     if (threadIdx.x == 0 && m != 0) atomicMax(reinterpret_cast<unsigned int*>(p.acc), m);
-}
-
-__device__ __forceinline__ float ts_from_amax(uint32_t amax_bits, float gmax448) {
-    const float a = __uint_as_float(amax_bits);
-    return a == 0.0f ? 1.0f : a / gmax448;
 }
 
 // ---------------------------------------------------------------- one-launch tensor scale
@@ -131,25 +113,12 @@ __device__ __forceinline__ float ts_from_amax(uint32_t amax_bits, float gmax448)
 // agent-scope release/acquire fences (an L2 writeback and invalidate per
 // workgroup) cost more than the whole pass over a 16 MiB tensor, and so do
 // hundreds of atomics on one address, which is why there are eight slots.
-__device__ __forceinline__ uint32_t fetch_max_agent(uint32_t* p, uint32_t v) {
-    return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t take_agent(uint32_t* p) {
-    return __hip_atomic_exchange(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Returns true for the arrival that completes the count n (the counter is then 0 again).
-__device__ __forceinline__ bool arrive(uint32_t* ctr, uint32_t n) {
-    return __builtin_amdgcn_atomic_inc32(ctr, n - 1u, __ATOMIC_RELAXED, "agent") == n - 1u;
-}
-// Makes the atomic that produced v complete (its value is in a register) before
-// any later memory operation is issued.
-__device__ __forceinline__ void completed(uint32_t v) { asm volatile("" ::"v"(v) : "memory"); }
 
 template <bool RHT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_tensor_scale_1(const AmaxParams p, uint32_t* ws, float gmax448) {
     __shared__ uint32_t red[kThreads / 64];
     const uint32_t b = blockIdx.x, nwg = gridDim.x, slot = b % kTsSlots;
-    const uint32_t m = wg_max_t0(amax_thread<RHT, CONTIG, kAmaxU>(p), red);
+    const uint32_t m = wg_max_t0<kThreads / 64>(amax_thread<RHT, CONTIG, kAmaxU>(p), red);
     if (threadIdx.x != 0) return;
     uint32_t* smax = ws + kTsSlotMax + kTsLine * slot;
     completed(fetch_max_agent(smax, m));
@@ -451,7 +420,6 @@ hipError_t launch_tensor_scale_1(int grid, bool rht, bool contig, const AmaxPara
 static __device__ __align__(256) uint32_t scratch[kTsWorkspaceBytes / sizeof(uint32_t)];
 
 namespace {
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 uint32_t* g_scratch_ptr[kMaxDevices] = {};
 }  // namespace

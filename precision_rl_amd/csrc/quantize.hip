@@ -25,6 +25,8 @@
 //         inv = 2^-(code-127);
 //   guided: the code comes from the guide.
 // Per element: v = RN(y*inv), then the grid rounding of device.h.
+#include <mutex>
+
 #include "device.h"
 #include "internal.h"
 
@@ -559,6 +561,139 @@ hipError_t launch_grouped_m(int mode, bool rht, bool emit, const GroupedQuantPar
     }
 }
 
+
+// ---------------------------------------------------------------- tensor scale and quantize in one launch
+// NVFP4 (either grid), RTN or SR, no RHT.  Each workgroup first takes the
+// largest finite |x| of exactly the chunk it will quantize (plain loads, so the
+// bytes stay in the caches), folds it into the workspace's two-level reduction
+// as the one-launch tensor scale does, and waits until the workgroup that
+// completes the reduction has published s_t; then it quantizes its chunk, whose
+// bytes its compute unit has just read.  This needs every workgroup resident at
+// once: the host launches it only when the device holds the whole grid, and the
+// wait is bounded (kScaleWaitPolls polls, about a second) so that a workgroup
+// kept from seeing s_t gives up with a NaN scale instead of spinning forever.
+// Publication takes no counter that every workgroup must touch on its way out
+// (a thousand same-address atomics serialize into more than the whole launch):
+// the phase word, read by every workgroup before it arrives, names the scale
+// word of this call; the publisher writes s_t there, clears the other word
+// (the previous call's, long finished), and flips the phase for the next call.
+constexpr uint32_t kScaleWaitPolls = 1u << 20;
+
+template <int GRID, int MODE, bool EMIT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void k_quantize_with_scale(const QuantParams p, float* ts_out, uint32_t* ws,
+                                                                  float gmax448) {
+    constexpr int kH = 4;
+    constexpr uint32_t kChunkGroups = kThreads * (kH / 2);
+    __shared__ float tab[128];
+    __shared__ uint32_t red[kThreads / 64];
+    __shared__ float ts_sh;
+    const uint32_t b = blockIdx.x, nwg = gridDim.x, slot = b % kTsSlots;
+    const uint32_t lane = threadIdx.x & 63u;
+    // the half-groups quantize_chunk reads for chunk b; past the end, the last one again
+    const uint32_t hg0 = b * (2u * kChunkGroups) + (threadIdx.x >> 6) * (64u * kH) + lane;
+    const uint32_t nhg = 2u * p.ngroups;
+    uint32_t m = 0;
+    #pragma unroll
+    for (int s = 0; s < kH; ++s) {
+        const uint32_t hg = min(hg0 + 64u * s, nhg - 1u);
+        const v4u32 a = *reinterpret_cast<const v4u32*>(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld));
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+            m = lo < 0x7F80u ? max(m, lo << 16) : m;
+            m = hi < 0x7F80u ? max(m, hi << 16) : m;
+        }
+    }
+    m = wg_max_t0<kThreads / 64>(m, red);
+    if (threadIdx.x == 0) {
+        // read before arriving: the phase flips only after every workgroup has arrived
+        const uint32_t phase_word = __hip_atomic_load(ws + kTsPhase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        completed(phase_word);   // performed before this workgroup's arrival below
+        const uint32_t phase = phase_word & 1u;
+        uint32_t* mine = ws + kTsScale + kTsLine * phase;
+        uint32_t* smax = ws + kTsSlotMax + kTsLine * slot;
+        completed(fetch_max_agent(smax, m));
+        if (arrive(ws + kTsSlotCtr + kTsLine * slot, (nwg - slot + kTsSlots - 1) / kTsSlots)) {
+            completed(fetch_max_agent(ws + kTsTopMax, take_agent(smax)));
+            if (arrive(ws + kTsTopCtr, min(nwg, kTsSlots))) {
+                const float ts = ts_from_amax(take_agent(ws + kTsTopMax), gmax448);   // > 0: bits never 0
+                *ts_out = ts;
+                completed(take_agent(ws + kTsScale + kTsLine * (phase ^ 1u)));
+                completed(__hip_atomic_exchange(mine, __float_as_uint(ts), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                completed(__hip_atomic_exchange(ws + kTsPhase, phase ^ 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            }
+        }
+        uint32_t v = 0;
+        for (uint32_t n = 0; n < kScaleWaitPolls; ++n) {
+            v = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (v) break;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        ts_sh = v ? __uint_as_float(v) : __builtin_nanf("");
+    }
+    __syncthreads();
+    QuantParams q = p;
+    q.ts = &ts_sh;
+    quantize_chunk<0, GRID, MODE, false, EMIT, CONTIG, 0, kH>(q, b, tab);
+}
+
+template <int GRID, int MODE, bool EMIT, bool CONTIG>
+hipError_t launch_with_scale_t(const QuantParams& p, float* ts_out, uint32_t* ws, bool* fused, hipStream_t s) {
+    constexpr uint32_t kChunkGroups = kThreads * 2;
+    const uint32_t blocks = (p.ngroups + kChunkGroups - 1) / kChunkGroups;
+    // workgroups the device holds at once, per device (the same on every call)
+    static std::mutex mu;
+    static int resident[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int cap = 0;
+    if (dev >= 0 && dev < kMaxDevices) {
+        std::lock_guard<std::mutex> lock(mu);
+        if (resident[dev] == 0) {
+            int per_cu = 0, cus = 0;
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(&k_quantize_with_scale<GRID, MODE, EMIT, CONTIG>), kThreads, 0);
+            if (e != hipSuccess) return e;
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess) return e;
+            resident[dev] = per_cu * cus > 0 ? per_cu * cus : -1;
+        }
+        cap = resident[dev];
+    }
+    const float g448 = GRID == 0 ? 2688.0f : 3136.0f;
+    if (blocks > 0 && (int64_t)blocks <= cap) {
+        *fused = true;
+        hipLaunchKernelGGL((k_quantize_with_scale<GRID, MODE, EMIT, CONTIG>), dim3(blocks), dim3(kThreads), 0, s, p,
+                           ts_out, ws, g448);
+        return hipGetLastError();
+    }
+    *fused = false;
+    return hipErrorNotSupported;   // the caller takes the two-launch path
+}
+
+template <int GRID, int MODE, bool EMIT>
+hipError_t launch_with_scale_c(bool contig, const QuantParams& p, float* ts_out, uint32_t* ws, bool* fused,
+                               hipStream_t s) {
+    return contig ? launch_with_scale_t<GRID, MODE, EMIT, true>(p, ts_out, ws, fused, s)
+                  : launch_with_scale_t<GRID, MODE, EMIT, false>(p, ts_out, ws, fused, s);
+}
+
+template <int GRID, int MODE>
+hipError_t launch_with_scale_e(bool emit, bool contig, const QuantParams& p, float* ts_out, uint32_t* ws,
+                               bool* fused, hipStream_t s) {
+    return emit ? launch_with_scale_c<GRID, MODE, true>(contig, p, ts_out, ws, fused, s)
+                : launch_with_scale_c<GRID, MODE, false>(contig, p, ts_out, ws, fused, s);
+}
+
+template <int GRID>
+hipError_t launch_with_scale_m(int mode, bool emit, bool contig, const QuantParams& p, float* ts_out, uint32_t* ws,
+                               bool* fused, hipStream_t s) {
+    return mode == MODE_SR ? launch_with_scale_e<GRID, MODE_SR>(emit, contig, p, ts_out, ws, fused, s)
+                           : launch_with_scale_e<GRID, MODE_RTN>(emit, contig, p, ts_out, ws, fused, s);
+}
+
 }  // namespace
 
 uint32_t quantize_chunks(int format, int mode, bool rht, uint32_t ngroups) {
@@ -604,6 +739,29 @@ hipError_t launch_quantize(int format, int grid, int mode, bool rht, bool emit, 
     }
     return grid == 0 ? launch_m<1, 0>(mode, rht, emit, contig, p, s)
                      : launch_m<1, 1>(mode, rht, emit, contig, p, s);
+}
+
+hipError_t launch_quantize_with_scale(int grid, int mode, bool rht, bool emit, bool contig, const QuantParams& p,
+                                      float* ts_out, uint32_t* ws, bool* fused, hipStream_t s) {
+    *fused = false;
+    if (p.ngroups > 0 && !rht) {
+        const hipError_t e = grid == 0 ? launch_with_scale_m<0>(mode, emit, contig, p, ts_out, ws, fused, s)
+                                       : launch_with_scale_m<1>(mode, emit, contig, p, ts_out, ws, fused, s);
+        if (*fused || e != hipErrorNotSupported) return e;
+    }
+    // with the RHT, too large to hold at once, or empty: the one-launch tensor scale, then quantize
+    AmaxParams a{};
+    a.x = p.x;
+    a.ld = p.ld;
+    a.ngroups = p.ngroups;
+    a.gpr = p.gpr;
+    a.rht_seed = p.rht_seed;
+    a.acc = ts_out;
+    hipError_t e = launch_tensor_scale_1(grid, rht, contig, a, ws, s);
+    if (e != hipSuccess || p.ngroups == 0) return e;
+    QuantParams q = p;
+    q.ts = ts_out;
+    return launch_quantize(0, grid, mode, rht, emit, contig, q, s);
 }
 
 }  // namespace fp4q

@@ -70,6 +70,7 @@ MAX_GROUP = 16
 
 _lib = None
 EXPORTS = ("fp4_tensor_scale", "fp4_tensor_scale_ws", "fp4_tensor_scale_workspace_bytes",
+           "fp4_quantize_with_tensor_scale",
            "fp4_tensor_scale_noalloc", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
            "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_pack_grouped",
            "guide_unpack",
@@ -105,6 +106,7 @@ def lib():
         "fp4_tensor_scale_ws": [CP, P, I64, I64, I64, P, P, C.c_size_t, P],
         "fp4_tensor_scale_noalloc": [CP, P, I64, I64, I64, P, P],
         "fp4_quantize": [CP, P, I64, I64, I64, P, P, P, P, P],
+        "fp4_quantize_with_tensor_scale": [CP, P, I64, I64, I64, P, P, P, P, P, C.c_size_t, P, P],
         "fp4_quantize_guided": [CP, P, I64, I64, I64, P, P, P, P, P, P],
         "fp4_quantize_grouped": [CP, I, I, C.POINTER(_CTensor), P],
         "fp4_fake_quantize": [CP, I, P, I64, I64, I64, P, P, P, P, I64, P],
@@ -236,6 +238,34 @@ def fp4_quantize(x: torch.Tensor, cfg: Fp4Config, tensor_scale: torch.Tensor | N
     _check(lib().fp4_quantize(C.byref(c), _ptr(x), rows, cols, ld, _ptr(tensor_scale), _ptr(codes),
                               _ptr(scales), _ptr(bits) if emit else None, _stream(x)), "fp4_quantize")
     return (codes, scales, bits) if emit else (codes, scales)
+
+
+def fp4_quantize_with_tensor_scale(x: torch.Tensor, cfg: Fp4Config, workspace: torch.Tensor, emit: bool = False,
+                                   ts=None, codes=None, scales=None, bits=None):
+    """NVFP4 tensor scale and quantization together (one launch where the device holds the whole
+    grid, else two), with a workspace from tensor_scale_workspace().  Returns (ts, codes, scales)
+    or (ts, codes, scales, guide_bits) when ``emit``; the number of launches enqueued is kept in
+    ``last_launches``."""
+    global last_launches
+    _on_gpu(x, workspace, ts, codes, scales, bits)
+    rows, cols, ld = _matrix(x)
+    n = rows * cols
+    ts = _alloc(1, torch.float32, x.device) if ts is None else ts
+    codes = _u8(n // 2, x) if codes is None else codes
+    scales = _u8(n // cfg.block, x) if scales is None else scales
+    if emit and bits is None:
+        bits = _u8(n // 8, x)
+    c = cfg.c()
+    nl = C.c_int(0)
+    _check(lib().fp4_quantize_with_tensor_scale(C.byref(c), _ptr(x), rows, cols, ld, _ptr(ts), _ptr(codes),
+                                                _ptr(scales), _ptr(bits) if emit else None, _ptr(workspace),
+                                                workspace.numel() * workspace.element_size(), C.byref(nl),
+                                                _stream(x)), "fp4_quantize_with_tensor_scale")
+    last_launches = nl.value
+    return (ts, codes, scales, bits) if emit else (ts, codes, scales)
+
+
+last_launches = 0
 
 
 def fp4_quantize_guided(x: torch.Tensor, cfg: Fp4Config, guide_bits: torch.Tensor,

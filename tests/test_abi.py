@@ -31,6 +31,7 @@ def test_header_declares_the_expected_calls():
     names = _declared()
     for n in ["fp4_quantize", "fp4_quantize_guided", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_guide_mismatch",
               "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "guide_pack_grouped", "fp4_rht16", "fp4_tensor_scale", "fp4_encode_values", "fp4_codes_bytes",
+              "fp4_quantize_with_tensor_scale",
               "fp4_scales_bytes", "fp4_guide_bytes", "fp4_status_str", "fp4_last_error"]:
         assert n in names, n
 
@@ -197,6 +198,31 @@ def test_tensor_scale_workspace_errors(fq):
     assert "workspace" in L.fp4_last_error().decode()
     assert f(C.byref(c), p, 4, 24, 24, p, p, n, None) == 2                  # cols % 16
     assert f(C.byref(c), p, 4, 32, 32, None, p, n, None) == 1               # no output
+
+
+def test_quantize_with_tensor_scale_host_side_errors(fq):
+    L = fq.lib()
+    A = 1 << 20
+    p = C.c_void_p(A)
+    n = L.fp4_tensor_scale_workspace_bytes()
+    f = L.fp4_quantize_with_tensor_scale
+    nl = C.c_int(-1)
+
+    def call(cfg, cols=32, ts=p, ws=p, wsb=n, codes=p, scales=p):
+        c = cfg.c()
+        return f(C.byref(c), p, 4, cols, cols, ts, codes, scales, None, ws, wsb, C.byref(nl), None)
+
+    ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED = 1, 2, 3, 4
+    assert call(fq.Fp4Config(format=fq.MXFP4)) == ERR_UNSUPPORTED      # MXFP4 has no tensor scale
+    assert "NVFP4" in L.fp4_last_error().decode()
+    assert call(fq.Fp4Config(), ws=None) == ERR_ARG
+    assert call(fq.Fp4Config(), ws=C.c_void_p(A + 64)) == ERR_ALIGN
+    assert call(fq.Fp4Config(), wsb=n - 1) == ERR_ARG
+    assert call(fq.Fp4Config(), cols=24) == ERR_SHAPE
+    assert call(fq.Fp4Config(), ts=None) == ERR_ARG
+    assert call(fq.Fp4Config(), codes=None) == ERR_ARG
+    assert call(fq.Fp4Config(), codes=C.c_void_p(A + 8)) == ERR_ALIGN
+    assert nl.value == -1                                                 # nothing was launched
 
 
 def test_gemm_quantize_host_side_errors(fq):
