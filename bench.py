@@ -331,9 +331,11 @@ def headline(args, fq, torch, W, ceiling):
             timer.run(name, fn)
     torch.cuda.synchronize()
     kernels = {}
+    # in-step figures are medians: a launch timed between two events also times any host stall
+    # between the first event and the launch (one 34 ms stall once made a 10 us kernel's mean 352 us)
     for name, (ms, cnt, pct) in timer.summary().items():
-        kernels[name] = dict(report(ms, bytes_per[name] * n, n, ceiling), launches=cnt,
-                             us_p10_median_p90=[round(q * 1e3, 2) for q in pct])
+        kernels[name] = dict(report(pct[1], bytes_per[name] * n, n, ceiling), launches=cnt,
+                             us_mean=round(ms * 1e3, 2), us_p10_median_p90=[round(q * 1e3, 2) for q in pct])
     # back-to-back launches of each kernel alone: the roofline figure.  Inputs and outputs rotate over Q
     # sets (the codes and guides the step produced, copied), so that no set comes round again within more
     # than 1 GiB of traffic: neither reads nor writes can be served by the 256 MB Infinity Cache.
@@ -511,8 +513,9 @@ def wl_c1(args, fq, torch, W, ceiling):
                         lambda: same(*zip((oc[Lo], os_[Lo]), fq.fp4_quantize_guided(xs[L], cfg, guides[L][2],
                                                                                      guides[L][1], tss[L]))))
     r["quantize_guided_graph"] = dict(report(ms, 2.75 * n, n, ceiling), replays_match_eager=ok)
-    # the tensor scale in one launch (workspace), alone and followed by the RTN quantize that uses it:
-    # end to end, both passes over x (2 + 2.5625 bytes per element)
+    # the tensor scale in one launch (workspace), alone and followed by the RTN quantize that uses it.
+    # End to end the task's algorithmic bytes are those of one pass: x read once and the codes and
+    # scales written (2.5625 bytes per element); the two- and four-launch forms read x twice
     ws = fq.tensor_scale_workspace()
     ms, ok = graph_time(torch, lambda i: fq.fp4_tensor_scale_ws(xs[i % P], cfg, ws, out=tso[i % R]), gr,
                         lambda: same((tso[Lo], fq.fp4_tensor_scale(xs[L], cfg))))
@@ -529,20 +532,19 @@ def wl_c1(args, fq, torch, W, ceiling):
         t = fq.fp4_tensor_scale(xs[L], cfg)
         return same((tso[Lo], t), *zip((oc[Lo], os_[Lo]), fq.fp4_quantize(xs[L], cfg, t)))
     ms, ok = graph_time(torch, lambda i: ts_rtn(i, True), gr, ts_rtn_check)
-    r["tensor_scale_plus_rtn_graph"] = dict(report(ms, 4.5625 * n, n, ceiling), replays_match_eager=ok,
+    r["tensor_scale_plus_rtn_graph"] = dict(report(ms, 2.5625 * n, n, ceiling), replays_match_eager=ok,
                                             launches=2)
     ms, ok = graph_time(torch, lambda i: ts_rtn(i, False), gr, ts_rtn_check)
-    r["tensor_scale_three_launches_plus_rtn_graph"] = dict(report(ms, 4.5625 * n, n, ceiling),
+    r["tensor_scale_three_launches_plus_rtn_graph"] = dict(report(ms, 2.5625 * n, n, ceiling),
                                                            replays_match_eager=ok, launches=4)
     # both in one launch (fp4_quantize_with_tensor_scale): each workgroup reduces the maximum of its
-    # own chunk, waits for s_t and quantizes the chunk it has just read; the same algorithmic bytes as
-    # the rows above, of which it reads x from HBM once
+    # own chunk, waits for s_t and quantizes the chunk it has just read, so x comes from HBM once
     fq.fp4_quantize_with_tensor_scale(xs[0], cfg, ws, ts=tso[0], codes=oc[0], scales=os_[0])
     fused_launches = fq.last_launches
     ms, ok = graph_time(torch, lambda i: fq.fp4_quantize_with_tensor_scale(xs[i % P], cfg, ws, ts=tso[i % R],
                                                                            codes=oc[i % R], scales=os_[i % R]),
                         gr, ts_rtn_check)
-    r["tensor_scale_and_rtn_one_launch_graph"] = dict(report(ms, 4.5625 * n, n, ceiling), replays_match_eager=ok,
+    r["tensor_scale_and_rtn_one_launch_graph"] = dict(report(ms, 2.5625 * n, n, ceiling), replays_match_eager=ok,
                                                       launches=fused_launches)
     return r
 
@@ -882,7 +884,7 @@ def main():
                      "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                      "traffic": read_traffic(f"{dom}@c2", sha),
                      "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": dk["us_back_to_back"],
-                     "avg_launch_us_in_step": dk["us"]},
+                     "median_launch_us_in_step": dk["us"]},
         "roofline_c5": workload_roofline("c5", workloads.get(WORKLOADS["c5"][0]), sha),
         "cpu_baseline": cpu,
         "cpu_baseline_all_threads": cpu_all,
