@@ -94,16 +94,17 @@ typedef struct {
 fp4_status fp4_tensor_scale(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
                             int64_t ld, float* tensor_scale_out, hipStream_t stream);
 
-/* The same tensor scale in one launch [FQT-FP4 §3]: every workgroup publishes its
- * partial maximum in `workspace`, and the last one to finish reduces them and
- * writes s_t, bit for bit equal to fp4_tensor_scale.
+/* The same tensor scale in one launch [FQT-FP4 §3]: every workgroup stores its
+ * partial maximum in a word of `workspace` tagged with the call's epoch, and
+ * workgroup 0 waits until all are tagged, reduces them and writes s_t, bit for
+ * bit equal to fp4_tensor_scale.
  *   workspace        device memory of at least fp4_tensor_scale_workspace_bytes()
  *                    (FP4_TENSOR_SCALE_WORKSPACE_BYTES), 256-byte aligned, owned by the
  *                    caller and zero-filled before its first use; every call leaves it
- *                    ready for the next one (its arrival counters return to 0).  Calls
- *                    that may run at the same time need workspaces of their own.
+ *                    ready for the next one (it advances the epoch count kept there).
+ *                    Calls that may run at the same time need workspaces of their own.
  *   workspace_bytes  its size; FP4_ERR_ARG when too small. */
-#define FP4_TENSOR_SCALE_WORKSPACE_BYTES 8192
+#define FP4_TENSOR_SCALE_WORKSPACE_BYTES 24576
 fp4_status fp4_tensor_scale_ws(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
                                int64_t ld, float* tensor_scale_out, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
@@ -112,11 +113,11 @@ size_t fp4_tensor_scale_workspace_bytes(void);
 /* fp4_tensor_scale_ws without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  The workspace is a static array of
- * FP4_TENSOR_SCALE_WORKSPACE_BYTES that the library holds on each GPU it runs on
- * until the process ends; this call allocates nothing.  That size serves every
+ * 16 KiB that the library holds on each GPU it runs on until the process ends;
+ * this call allocates nothing.  That size serves every
  * input the other entry points accept (the launch has at most 1024 workgroups);
  * larger inputs fail with FP4_ERR_SHAPE as everywhere.  Calls on one GPU share
- * its array: every completed call leaves it zeroed for the next, and calls that
+ * its array: every completed call leaves it ready for the next, and calls that
  * overlap in time on one GPU (several streams, several host threads) race, with
  * undefined results for them and for later calls.  Same result as
  * fp4_tensor_scale, bit for bit. */
@@ -146,17 +147,19 @@ fp4_status fp4_quantize(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, in
  * guide bits when guide_bits_out is not NULL) exactly as fp4_quantize does with
  * that s_t, RTN or SR.  Without the RHT, and when the device holds every
  * workgroup of the launch at once (up to 2048 workgroups of 512 groups on an
- * MI355X: about 16.7M elements), this is one launch: each workgroup reduces the
- * maximum of its own chunk into `workspace`, waits for the last one to publish
- * s_t, and quantizes the chunk it has just read.  Otherwise it is
- * fp4_tensor_scale_ws followed by fp4_quantize (two launches).
+ * MI355X: about 16.7M elements), this is one launch: each workgroup stores the
+ * maximum of its own chunk in a word of `workspace`, workgroup 0 reduces those
+ * words and publishes s_t, and each workgroup quantizes the chunk it holds in
+ * registers.  Otherwise it is fp4_tensor_scale_ws followed by fp4_quantize (two
+ * launches).
  *   cfg              NVFP4 (MXFP4: FP4_ERR_UNSUPPORTED), RTN or SR.
  *   workspace        as for fp4_tensor_scale_ws: at least
  *                    FP4_TENSOR_SCALE_WORKSPACE_BYTES, 256-byte aligned, zero-filled
  *                    before first use; concurrent calls need their own.  Every call
- *                    leaves its reduction words zeroed; the one-launch form also keeps
- *                    the last scale it published and a phase bit there, for the next
- *                    call (zero-filling the workspace again is always valid).
+ *                    leaves the reduction words of fp4_tensor_scale_ws zeroed; the
+ *                    one-launch form keeps an epoch count there and words tagged with
+ *                    it, for the next call (zero-filling the workspace again is always
+ *                    valid).
  *   launches         NULL, or receives 1 or 2, the number of launches enqueued.
  * The one-launch form needs all its workgroups running together: work that
  * keeps compute units busy for more than about a second while it runs (another

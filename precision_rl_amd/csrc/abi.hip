@@ -122,6 +122,7 @@ fp4_status fp4_tensor_scale(const fp4_cfg* cfg, const void* x_bf16, int64_t rows
                       "fp4_tensor_scale launch");
 }
 
+static_assert(FP4_TENSOR_SCALE_WORKSPACE_BYTES == fp4q::kTsWorkspaceBytes, "workspace size in the header");
 size_t fp4_tensor_scale_workspace_bytes(void) { return fp4q::kTsWorkspaceBytes; }
 
 fp4_status fp4_tensor_scale_ws(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
@@ -152,9 +153,8 @@ fp4_status fp4_tensor_scale_noalloc(const fp4_cfg* cfg, const void* x_bf16, int6
     uint64_t ng = 0;
     FP4Q_TRY(check_matrix(rows, cols, ld, 16, x_bf16, &ng));
     FP4Q_TRY(need(tensor_scale_out, 4, "tensor_scale_out"));
-    // the launch never exceeds kTsMaxWorkgroups workgroups, whose shared words fit
-    // the static workspace whatever the input size
-    static_assert(fp4q::kTsWords * 4 <= fp4q::kTsWorkspaceBytes, "static workspace too small");
+    // the launch never exceeds kTsMaxWorkgroups workgroups, whose words the static
+    // workspace holds, whatever the input size
     hipError_t e = hipSuccess;
     uint32_t* ws = fp4q::static_ts_workspace(&e);
     if (!ws) return hip_status(e, "fp4_tensor_scale_noalloc: static workspace lookup");

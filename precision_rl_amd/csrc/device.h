@@ -646,22 +646,56 @@ __device__ __forceinline__ float ts_from_amax(uint32_t amax_bits, float gmax448)
     return a == 0.0f ? 1.0f : a / gmax448;
 }
 
-// Relaxed, agent-scope, returning atomics on the words of a reduction workspace
-// shared by the workgroups of one launch: each returns only once performed at
-// the L2, so a later atomic of the same thread cannot overtake it.
-__device__ __forceinline__ uint32_t fetch_max_agent(uint32_t* p, uint32_t v) {
-    return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Cross-workgroup reduction without atomics.  Workgroup b of a launch stores
+// tag << 32 | m in word b of a workspace; one workgroup reads every word until
+// all carry the call's tag.  The stores and loads are relaxed and agent-scope:
+// performed at the device's point of coherence, not held in one XCD's L2.  The
+// tag is the workspace's epoch + 1, and only the gathering workgroup advances
+// the epoch, after it has seen every word tagged, when every workgroup has read
+// the epoch already; so a word from an earlier call never passes for one of
+// this call (until the 32-bit epoch wraps), and all-zero words are a valid start.
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t take_agent(uint32_t* p) {
-    return __hip_atomic_exchange(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t load_agent(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Returns true for the arrival that completes the count n (the counter is then 0 again).
-__device__ __forceinline__ bool arrive(uint32_t* ctr, uint32_t n) {
-    return __builtin_amdgcn_atomic_inc32(ctr, n - 1u, __ATOMIC_RELAXED, "agent") == n - 1u;
+__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Makes the atomic that produced v complete (its value is in a register) before
-// any later memory operation is issued.
-__device__ __forceinline__ void completed(uint32_t v) { asm volatile("" ::"v"(v) : "memory"); }
+__device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) { return (uint64_t)tag << 32 | v; }
 
+// Polls before a wait gives up: at least 2^20 loads, about a second.
+constexpr uint32_t kGatherPolls = 1u << 20;
+
+// This thread's share of the gather: the largest low half of words i = threadIdx.x
+// + THREADS k < n (at most MAXN words), once all of them carry `tag`; each round
+// loads them all at once.  Returns 0xFFFFFFFF if they are not all tagged within
+// kGatherPolls rounds (the maxima are finite float bits, never that value).
+template <uint32_t MAXN, uint32_t THREADS>
+__device__ __forceinline__ uint32_t gather_max(const uint64_t* words, uint32_t n, uint32_t tag) {
+    constexpr uint32_t kPer = (MAXN + THREADS - 1) / THREADS;
+    for (uint32_t r = 0; r < kGatherPolls; ++r) {
+        uint64_t v[kPer];
+        #pragma unroll
+        for (uint32_t k = 0; k < kPer; ++k) {
+            const uint32_t i = threadIdx.x + THREADS * k;
+            v[k] = i < n ? load_agent(words + i) : tagged(tag, 0u);
+        }
+        bool all = true;
+        uint32_t g = 0;
+        #pragma unroll
+        for (uint32_t k = 0; k < kPer; ++k) {
+            all = all && (uint32_t)(v[k] >> 32) == tag;
+            g = max(g, (uint32_t)v[k]);
+        }
+        if (all) return g;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return 0xFFFFFFFFu;
+}
 
 }  // namespace fp4q

@@ -107,27 +107,26 @@ struct AmaxParams {
     float* acc;                 // receives max finite |y| (as bits, atomic max)
 };
 
-// Workspace of the one-launch tensor scale, in 32-bit words from a 256-byte
-// aligned base, each word on a 256-byte line of its own: the slot maxima and
-// slot arrival counters (kTsSlots of each), the top maximum and the top counter.
-// All must be 0 before the first call; every completed call leaves them 0.  The
-// fused tensor scale and quantize adds two published-scale words and a phase
-// word: call k publishes s_t (its bits, never 0) in scale word phase and clears
-// the other one, which call k - 1 published, then flips the phase.  Zero is a
-// valid state of these three too, so a zero-filled workspace suits every call.
-constexpr uint32_t kTsSlots = 8;
+// Workspace of the one-launch tensor scale and of the fused tensor scale and
+// quantize, in 32-bit words from a 256-byte aligned base: the epoch word (the
+// tag of the last call whose reduction completed), kTsPubCopies copies of the
+// fused launch's 64-bit published word (tag << 32 | bits of s_t), each on a
+// 256-byte line of its own, and from word kTsGather on one 64-bit word per
+// workgroup (tag << 32 | bits of its maximum).  A word counts only when its tag
+// is the call's own, so zero is a valid state of all of them: a zero-filled
+// workspace suits every call, and every call leaves it ready for the next.
 constexpr uint32_t kTsLine = 64;                        // words per 256-byte line
-constexpr uint32_t kTsMaxWorkgroups = 1024;
-constexpr uint32_t kTsSlotMax = 0;
-constexpr uint32_t kTsSlotCtr = kTsSlots * kTsLine;
-constexpr uint32_t kTsTopMax = 2 * kTsSlots * kTsLine;
-constexpr uint32_t kTsTopCtr = kTsTopMax + kTsLine;
-constexpr uint32_t kTsScale = kTsTopCtr + kTsLine;     // two words, kTsLine apart
-constexpr uint32_t kTsPhase = kTsScale + 2 * kTsLine;
-constexpr uint32_t kTsWords = kTsPhase + kTsLine;
-constexpr size_t kTsWorkspaceBytes = 8192;
+constexpr uint32_t kTsMaxWorkgroups = 1024;             // one-launch tensor scale
+constexpr uint32_t kTsEpoch = 0;
+constexpr uint32_t kTsPub = kTsLine;                    // 64-bit copies, kTsLine words apart
+constexpr uint32_t kTsPubCopies = 16;
+constexpr uint32_t kTsGather = 2048;                    // 64-bit words from here on, one per workgroup
+constexpr uint32_t kTsGatherMax = 2048;                 // workgroups of the fused launch
+constexpr size_t kTsWorkspaceBytes = 4 * kTsGather + 8 * kTsGatherMax;
+constexpr uint32_t kTsStaticWords = kTsGather + 2 * kTsMaxWorkgroups;   // what the one-launch tensor scale uses
+static_assert(kTsPub + kTsLine * kTsPubCopies <= kTsGather && kTsMaxWorkgroups <= kTsGatherMax,
+              "tensor-scale workspace layout");
 constexpr int kMaxDevices = 64;                         // devices whose per-device state the library keeps
-static_assert(kTsWords * 4 <= kTsWorkspaceBytes, "tensor-scale workspace layout");
 
 struct EncodeParams {
     const float* v;

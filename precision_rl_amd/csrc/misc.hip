@@ -99,33 +99,36 @@ __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
 }
 
 // ---------------------------------------------------------------- one-launch tensor scale
-// Each workgroup folds its maximum into the maximum of its slot (b % 8) and then
-// counts itself in at that slot.  The last arrival of a slot takes the slot
-// maximum (leaving 0 behind), folds it into the top maximum and counts itself in
-// at the top; the last arrival there takes the top maximum and writes s_t.  The
-// counters wrap to 0 with their last arrival (atomic inc), so each call leaves
-// the workspace as it found it.
-// Every shared word is touched only by atomics that return their old value, and
-// each one's value is used before the next is issued, so it has been performed
-// where its address is held; atomics on one address are performed there one at a
-// time, so the arrival that completes a count comes after every maximum folded
-// in by the workgroups it counts.  No cache writeback or invalidate is involved:
-// agent-scope release/acquire fences (an L2 writeback and invalidate per
-// workgroup) cost more than the whole pass over a 16 MiB tensor, and so do
-// hundreds of atomics on one address, which is why there are eight slots.
+// Each workgroup stores its maximum, tagged with this call's epoch, in a
+// workspace word of its own (device.h, cross-workgroup reduction) and ends;
+// workgroup 0 then waits until every word carries the tag, takes their maximum,
+// writes s_t and advances the epoch.  Only workgroup 0 waits, on workgroups that
+// never wait themselves, so the grid need not be resident all at once.  Distinct
+// words take no atomics: through shared counters, a hundred and more same-
+// address atomics per word serialize at about 13 ns each, and agent-scope
+// release/acquire fences (an L2 writeback and invalidate per workgroup) cost
+// more than the whole pass over a 16 MiB tensor.
 
 template <bool RHT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_tensor_scale_1(const AmaxParams p, uint32_t* ws, float gmax448) {
     __shared__ uint32_t red[kThreads / 64];
-    const uint32_t b = blockIdx.x, nwg = gridDim.x, slot = b % kTsSlots;
+    __shared__ uint32_t tag_sh;
+    const uint32_t b = blockIdx.x, nwg = gridDim.x;
+    const uint32_t epoch = threadIdx.x == 0 ? load_agent(ws + kTsEpoch) : 0u;
     const uint32_t m = wg_max_t0<kThreads / 64>(amax_thread<RHT, CONTIG, kAmaxU>(p), red);
-    if (threadIdx.x != 0) return;
-    uint32_t* smax = ws + kTsSlotMax + kTsLine * slot;
-    completed(fetch_max_agent(smax, m));
-    if (!arrive(ws + kTsSlotCtr + kTsLine * slot, (nwg - slot + kTsSlots - 1) / kTsSlots)) return;
-    completed(fetch_max_agent(ws + kTsTopMax, take_agent(smax)));
-    if (!arrive(ws + kTsTopCtr, min(nwg, kTsSlots))) return;
-    *p.acc = ts_from_amax(take_agent(ws + kTsTopMax), gmax448);
+    uint64_t* const words = reinterpret_cast<uint64_t*>(ws + kTsGather);
+    if (threadIdx.x == 0) {
+        store_agent(words + b, tagged(epoch + 1u, m));
+        tag_sh = epoch + 1u;
+    }
+    if (b != 0) return;
+    __syncthreads();   // tag_sh; also orders the first use of red before the second
+    const uint32_t tag = tag_sh;
+    const uint32_t g = wg_max_t0<kThreads / 64>(gather_max<kTsMaxWorkgroups, kThreads>(words, nwg, tag), red);
+    if (threadIdx.x == 0) {
+        *p.acc = g == 0xFFFFFFFFu ? __builtin_nanf("") : ts_from_amax(g, gmax448);
+        store_agent(ws + kTsEpoch, tag);
+    }
 }
 
 __global__ void k_ts_finalize(float* acc, float gmax448) {
@@ -397,9 +400,8 @@ hipError_t launch_tensor_scale(int grid, bool rht, bool contig, const AmaxParams
 }
 
 // One launch of at most kTsMaxWorkgroups workgroups of kAmaxU groups per lane
-// (a 16 MiB tensor gets 512: measured faster than 256 once no address takes more
-// than a sixty-fourth of the atomics); an empty tensor still gets one workgroup,
-// which writes s_t = 1.
+// (a 16 MiB tensor gets 512); an empty tensor still gets one workgroup, which
+// writes s_t = 1.
 hipError_t launch_tensor_scale_1(int grid, bool rht, bool contig, const AmaxParams& p, uint32_t* ws, hipStream_t s) {
     const float g448 = grid == 0 ? 2688.0f : 3136.0f;
     const uint32_t per_wg = kThreads * kAmaxU;
@@ -414,10 +416,14 @@ hipError_t launch_tensor_scale_1(int grid, bool rht, bool contig, const AmaxPara
 
 // Workspace of fp4_tensor_scale_noalloc, for callers that cannot allocate: one
 // array per device, zero when the code object is loaded and left zero by every
-// completed call.  Host code reaches it only through the device address that
-// hipGetSymbolAddress returns for the current device (the array's name is a
-// host-side stand-in, not a device address).
-static __device__ __align__(256) uint32_t scratch[kTsWorkspaceBytes / sizeof(uint32_t)];
+// completed call.  It holds the words the one-launch tensor scale uses (the
+// epoch and kTsMaxWorkgroups gather words), not those only the fused quantize
+// needs.  Host code reaches it
+// only through the device address that hipGetSymbolAddress returns for the
+// current device (the array's name is a host-side stand-in, not a device
+// address).
+static __device__ __align__(256) uint32_t scratch[kTsStaticWords];
+static_assert(sizeof(scratch) == 16384, "the header states the static workspace size");
 
 namespace {
 std::mutex g_scratch_mu;

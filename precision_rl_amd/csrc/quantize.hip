@@ -79,11 +79,12 @@ __device__ __forceinline__ v4u32* rht_transpose_lds() {
 // takes the guide bits from the rollout's full codes and counts, instead of
 // storing anything, how often the guided result differs from those codes.
 // tab: LDS space for the NVFP4 reciprocal table, which the chunk builds once its
-// loads are in flight (OUT = 2: the caller has built it).
+// loads are in flight (OUT = 2: the caller has built it).  PRE: the caller has
+// loaded the lane's half-groups (the same ones, in slot order) into pre.
 template <int FMT, int GRID, int MODE, bool RHT, bool EMIT, bool CONTIG, int OUT = 0,
-          int KH = halves_per_lane<FMT, MODE, RHT>()>
+          int KH = halves_per_lane<FMT, MODE, RHT>(), bool PRE = false>
 __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg, float* tab,
-                                               uint32_t* acc = nullptr) {
+                                               uint32_t* acc = nullptr, const uint32_t (*pre)[4] = nullptr) {
     constexpr float kGmax = GRID == 0 ? 6.0f : 7.0f;
     constexpr int kH = KH;
     constexpr int kG = kH / 2;                                      // whole groups per lane
@@ -107,8 +108,13 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     uint32_t w[kH][4];
     #pragma unroll
     for (int s = 0; s < kH; ++s) {
-        const uint32_t hg = min(hg0 + 64u * s, nhg - 1u);
-        load16_nt(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld), w[s]);
+        if constexpr (PRE) {
+            #pragma unroll
+            for (int j = 0; j < 4; ++j) w[s][j] = pre[s][j];
+        } else {
+            const uint32_t hg = min(hg0 + 64u * s, nhg - 1u);
+            load16_nt(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld), w[s]);
+        }
     }
     uint32_t gb[kG], gs[kG];
     v2u32 rc[kG];
@@ -563,22 +569,16 @@ hipError_t launch_grouped_m(int mode, bool rht, bool emit, const GroupedQuantPar
 
 
 // ---------------------------------------------------------------- tensor scale and quantize in one launch
-// NVFP4 (either grid), RTN or SR, no RHT.  Each workgroup first takes the
-// largest finite |x| of exactly the chunk it will quantize (plain loads, so the
-// bytes stay in the caches), folds it into the workspace's two-level reduction
-// as the one-launch tensor scale does, and waits until the workgroup that
-// completes the reduction has published s_t; then it quantizes its chunk, whose
-// bytes its compute unit has just read.  This needs every workgroup resident at
-// once: the host launches it only when the device holds the whole grid, and the
-// wait is bounded (kScaleWaitPolls polls, about a second) so that a workgroup
-// kept from seeing s_t gives up with a NaN scale instead of spinning forever.
-// Publication takes no counter that every workgroup must touch on its way out
-// (a thousand same-address atomics serialize into more than the whole launch):
-// the phase word, read by every workgroup before it arrives, names the scale
-// word of this call; the publisher writes s_t there, clears the other word
-// (the previous call's, long finished), and flips the phase for the next call.
-constexpr uint32_t kScaleWaitPolls = 1u << 20;
-
+// NVFP4 (either grid), RTN or SR, no RHT.  Each workgroup loads exactly the
+// chunk it will quantize, keeps it in registers, and stores the chunk's largest
+// finite |x|, tagged with this call's epoch, in a workspace word of its own;
+// workgroup 0 gathers those words as the one-launch tensor scale does and
+// publishes s_t in tagged words (copies on several lines, so that the waiting
+// workgroups' loads spread), which the others wait for; then each quantizes its
+// chunk from its registers.  This needs every workgroup resident at once: the
+// host launches it only when the device holds the whole grid, and each wait is
+// bounded (kGatherPolls polls, about a second) so that a workgroup kept from
+// seeing s_t gives up with a NaN scale instead of spinning forever.
 template <int GRID, int MODE, bool EMIT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_quantize_with_scale(const QuantParams p, float* ts_out, uint32_t* ws,
                                                                   float gmax448) {
@@ -586,56 +586,67 @@ __global__ __launch_bounds__(kThreads) void k_quantize_with_scale(const QuantPar
     constexpr uint32_t kChunkGroups = kThreads * (kH / 2);
     __shared__ float tab[128];
     __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint32_t tag_sh;
     __shared__ float ts_sh;
-    const uint32_t b = blockIdx.x, nwg = gridDim.x, slot = b % kTsSlots;
+    const uint32_t b = blockIdx.x, nwg = gridDim.x;
     const uint32_t lane = threadIdx.x & 63u;
-    // the half-groups quantize_chunk reads for chunk b; past the end, the last one again
+    // the epoch word, read while the chunk loads (any time before this
+    // workgroup's own word is stored will do)
+    const uint32_t epoch = threadIdx.x == 0 ? load_agent(ws + kTsEpoch) : 0u;
+    // the half-groups quantize_chunk would read for chunk b (past the end, the
+    // last one again), kept in registers for it
     const uint32_t hg0 = b * (2u * kChunkGroups) + (threadIdx.x >> 6) * (64u * kH) + lane;
     const uint32_t nhg = 2u * p.ngroups;
-    uint32_t m = 0;
+    uint32_t w[kH][4];
     #pragma unroll
     for (int s = 0; s < kH; ++s) {
         const uint32_t hg = min(hg0 + 64u * s, nhg - 1u);
-        const v4u32 a = *reinterpret_cast<const v4u32*>(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld));
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        load16_nt(p.x + half_offset<CONTIG>(hg, p.gpr, p.ld), w[s]);
+    }
+    uint32_t m = 0;
+    #pragma unroll
+    for (int s = 0; s < kH; ++s) {
         #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+            const uint32_t lo = w[s][j] & 0x7FFFu, hi = (w[s][j] >> 16) & 0x7FFFu;
             m = lo < 0x7F80u ? max(m, lo << 16) : m;
             m = hi < 0x7F80u ? max(m, hi << 16) : m;
         }
     }
     m = wg_max_t0<kThreads / 64>(m, red);
+    uint64_t* const words = reinterpret_cast<uint64_t*>(ws + kTsGather);
     if (threadIdx.x == 0) {
-        // read before arriving: the phase flips only after every workgroup has arrived
-        const uint32_t phase_word = __hip_atomic_load(ws + kTsPhase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        completed(phase_word);   // performed before this workgroup's arrival below
-        const uint32_t phase = phase_word & 1u;
-        uint32_t* mine = ws + kTsScale + kTsLine * phase;
-        uint32_t* smax = ws + kTsSlotMax + kTsLine * slot;
-        completed(fetch_max_agent(smax, m));
-        if (arrive(ws + kTsSlotCtr + kTsLine * slot, (nwg - slot + kTsSlots - 1) / kTsSlots)) {
-            completed(fetch_max_agent(ws + kTsTopMax, take_agent(smax)));
-            if (arrive(ws + kTsTopCtr, min(nwg, kTsSlots))) {
-                const float ts = ts_from_amax(take_agent(ws + kTsTopMax), gmax448);   // > 0: bits never 0
-                *ts_out = ts;
-                completed(take_agent(ws + kTsScale + kTsLine * (phase ^ 1u)));
-                completed(__hip_atomic_exchange(mine, __float_as_uint(ts), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                completed(__hip_atomic_exchange(ws + kTsPhase, phase ^ 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            }
+        store_agent(words + b, tagged(epoch + 1u, m));
+        tag_sh = epoch + 1u;
+    }
+    if (b == 0) {
+        __syncthreads();   // tag_sh; also orders the first use of red before the second
+        const uint32_t tag = tag_sh;
+        const uint32_t g = wg_max_t0<kThreads / 64>(gather_max<kTsGatherMax, kThreads>(words, nwg, tag), red);
+        if (threadIdx.x == 0) {
+            const float ts = g == 0xFFFFFFFFu ? __builtin_nanf("") : ts_from_amax(g, gmax448);
+            *ts_out = ts;
+            #pragma unroll
+            for (uint32_t c = 0; c < kTsPubCopies; ++c)
+                store_agent(reinterpret_cast<uint64_t*>(ws + kTsPub + kTsLine * c), tagged(tag, __float_as_uint(ts)));
+            store_agent(ws + kTsEpoch, tag);
+            ts_sh = ts;
         }
-        uint32_t v = 0;
-        for (uint32_t n = 0; n < kScaleWaitPolls; ++n) {
-            v = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (v) break;
-            __builtin_amdgcn_s_sleep(8);
+    } else if (threadIdx.x == 0) {
+        const uint64_t* pub = reinterpret_cast<const uint64_t*>(ws + kTsPub + kTsLine * (b % kTsPubCopies));
+        const uint32_t tag = tag_sh;
+        uint64_t v = 0;
+        for (uint32_t n = 0; n < kGatherPolls; ++n) {
+            v = load_agent(pub);
+            if ((uint32_t)(v >> 32) == tag) break;
+            __builtin_amdgcn_s_sleep(4);
         }
-        ts_sh = v ? __uint_as_float(v) : __builtin_nanf("");
+        ts_sh = (uint32_t)(v >> 32) == tag ? __uint_as_float((uint32_t)v) : __builtin_nanf("");
     }
     __syncthreads();
     QuantParams q = p;
     q.ts = &ts_sh;
-    quantize_chunk<0, GRID, MODE, false, EMIT, CONTIG, 0, kH>(q, b, tab);
+    quantize_chunk<0, GRID, MODE, false, EMIT, CONTIG, 0, kH, true>(q, b, tab, nullptr, w);
 }
 
 template <int GRID, int MODE, bool EMIT, bool CONTIG>
@@ -663,7 +674,7 @@ hipError_t launch_with_scale_t(const QuantParams& p, float* ts_out, uint32_t* ws
         cap = resident[dev];
     }
     const float g448 = GRID == 0 ? 2688.0f : 3136.0f;
-    if (blocks > 0 && (int64_t)blocks <= cap) {
+    if (blocks > 0 && (int64_t)blocks <= cap && blocks <= kTsGatherMax) {
         *fused = true;
         hipLaunchKernelGGL((k_quantize_with_scale<GRID, MODE, EMIT, CONTIG>), dim3(blocks), dim3(kThreads), 0, s, p,
                            ts_out, ws, g448);

@@ -2,8 +2,10 @@
 quantization of one tensor together.  Where the launch is one kernel (no RHT,
 grid within what the device holds at once) and where it is two (RHT, or a grid
 too large), s_t must equal the oracle's tensor scale bit for bit and the codes,
-scales and guide bits the oracle's quantization with that s_t; every reduction
-word of the workspace must be 0 again after each call.  Covered: every grid size from
+scales and guide bits the oracle's quantization with that s_t.  After each call
+the workspace's epoch has advanced by one, every workgroup's word carries it
+(in the one-launch form, with exactly its own chunk's largest finite |x|) and
+so do the published copies of s_t.  Covered: every grid size from
 1 to 9 workgroups (a workgroup quantizes 512 groups of 16) and others up to the
 one-launch limit and past it, ragged tails, padded rows, both grids, RTN with and
 without emission and SR, all-zero, empty and non-finite inputs, replays of a
@@ -16,13 +18,10 @@ import torch
 
 import oracle as O
 from precision_rl_amd import workloads as W
+from ts_workspace import chunk_max_bits, check_after, epoch, fused_grid, ts_grid
 
 pytestmark = pytest.mark.gpu
 
-# the workspace's reduction words, each on its own 256-byte line: 8 slot maxima, 8 slot
-# counters, top maximum, top counter (the two published-scale words and the phase word
-# that follow carry over from call to call)
-SHARED_WORDS = [64 * k for k in range(18)]
 CHUNK = 512 * 16          # elements one workgroup of the one-launch form quantizes
 
 
@@ -59,14 +58,10 @@ def bits32(x):
     return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
 
 
-def words_zero(ws):
-    w = ws.view(torch.int32).cpu().numpy()
-    return all(int(w[i]) == 0 for i in SHARED_WORDS)
-
-
 def check(fq, ws, xh, cfg, emit, pad=0, launches=None):
     oc = O.Cfg(grid=cfg.grid, rht16=cfg.rht16, rht_seed=cfg.rht_seed, sr_seed=cfg.sr_seed, sr_offset=cfg.sr_offset)
     mode = O.SR if cfg.rounding == 1 else O.RTN
+    e0 = epoch(ws)
     out = fq.fp4_quantize_with_tensor_scale(dev(xh, pad), cfg, ws, emit=emit)
     got_launches = fq.last_launches
     ts = O.tensor_scale(oc, xh)
@@ -76,9 +71,13 @@ def check(fq, ws, xh, cfg, emit, pad=0, launches=None):
     assert (host(out[1]) == want[0]).all(), "codes"
     if emit:
         assert (host(out[3]) == want[2]).all(), "guide bits"
-    assert words_zero(ws), "workspace not left at zero"
     if launches is not None:
         assert got_launches == launches
+    ng = xh.size // 16
+    if got_launches == 1:
+        check_after(ws, e0, fused_grid(ng), ts_bits=bits32([ts])[0], wg_max_bits=chunk_max_bits(xh, CHUNK))
+    else:
+        check_after(ws, e0, ts_grid(ng), amax_bits=None if cfg.rht16 else int(chunk_max_bits(xh, xh.size).max()))
     return got_launches
 
 
@@ -127,10 +126,11 @@ def test_special_inputs(fq, ws):
     cfg = fq.Fp4Config()
     z = np.zeros((64, 256), dtype=np.uint16)
     check(fq, ws, z, cfg, emit=True, launches=1)
+    e0 = epoch(ws)
     ts, codes, scales = fq.fp4_quantize_with_tensor_scale(torch.empty((0, 64), dtype=torch.bfloat16,
                                                                       device="cuda"), cfg, ws)
     assert bits32(host(ts))[0] == bits32([1.0])[0] and codes.numel() == 0
-    assert words_zero(ws)
+    check_after(ws, e0, 1, amax_bits=0)            # the one-launch tensor scale with one workgroup
     # non-finite values are left out of s_t; their blocks get the NaN scale code
     xf = np.random.default_rng(3).standard_normal((300, 512)).astype(np.float32)
     xf[7, 9], xf[100, 0], xf[299, 511] = np.inf, -np.inf, np.nan
@@ -138,7 +138,8 @@ def test_special_inputs(fq, ws):
 
 
 def test_zero_filled_workspace_between_calls(fq, ws):
-    # zero-filling resets the phase; the next calls must still publish and read the right word
+    # zero-filling resets the epoch (and every word); the next calls must still tag, publish and read
+    # the right words
     cfg = fq.Fp4Config()
     for k in range(5):
         if k in (1, 3):
@@ -170,7 +171,6 @@ def test_graph_replays(fq, ws):
         for o, w in zip(outs, want):
             for t, wt in zip(o, w):
                 assert (host(t) == wt).all(), rep
-        assert words_zero(ws)
         # eager work between the replays
         fq.fp4_quantize_with_tensor_scale(xs[rep], cfg, ws, emit=True)
         torch.cuda.synchronize()

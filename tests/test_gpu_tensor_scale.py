@@ -2,24 +2,22 @@
 scale and the three-launch fp4_tensor_scale bit for bit: small and large
 tensors (both launch shapes, one pass of up to 512 workgroups and the
 grid-stride form with 1024), every grid size from 1 to 18 workgroups (the
-eight reduction slots with zero to three arrivals each) and others up to the
-1024 cap, with and without a one-group last workgroup, ragged tails, padded
-rows, the RHT, both grids,
-all-zero, empty and non-finite inputs.  One workspace serves every call in
-turn: each call leaves its maxima and arrival counters at 0.  A captured graph of calls
-replays equal to eager calls."""
+workgroup words gathered in one or several loads per thread) and others up
+to the 1024 cap, with and without a one-group last workgroup, ragged tails,
+padded rows, the RHT, both grids, all-zero, empty and non-finite inputs.  One
+workspace serves every call in turn: each call advances its epoch by one and
+tags every workgroup's word with it (and without the RHT, the largest word is
+the tensor's largest finite |x|).  A captured graph of calls replays equal to
+eager calls."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 from precision_rl_amd import workloads as W
+from ts_workspace import chunk_max_bits, check_after, epoch, ts_grid
 
 pytestmark = pytest.mark.gpu
-
-# word offsets of the shared words in the workspace: 8 slot maxima, 8 slot counters, top maximum, top counter
-SHARED_WORDS = [64 * k for k in range(18)]
-
 
 @pytest.fixture(scope="module")
 def fq():
@@ -50,11 +48,6 @@ def bits(t):
     return np.float32(t.cpu().numpy()[0]).view(np.uint32)
 
 
-def counters_zero(ws):
-    w = ws.view(torch.int32).cpu().numpy()
-    return all(int(w[i]) == 0 for i in SHARED_WORDS)
-
-
 @pytest.mark.parametrize("rht,grid", [(False, 0), (True, 1), (True, 0)])
 @pytest.mark.parametrize("shape,pad", [((3, 16), 0), ((5, 48), 8), ((129, 96), 0), ((1, 16 * 1027), 0),
                                        ((4096, 2048), 0), ((1000, 2080), 16), ((4096, 8192), 0)])
@@ -64,12 +57,14 @@ def test_one_launch_tensor_scale_vs_oracle(fq, ws, rht, grid, shape, pad):
     cfg = fq.Fp4Config(grid=grid, rht16=rht, rht_seed=7)
     oc = O.Cfg(grid=grid, rht16=rht, rht_seed=7)
     x = dev(xh, pad)
+    e0 = epoch(ws)
     got = fq.fp4_tensor_scale_ws(x, cfg, ws)
-    three = fq.fp4_tensor_scale(x, cfg)
     want = np.float32(O.tensor_scale(oc, xh)).view(np.uint32)
     assert bits(got) == want
+    check_after(ws, e0, ts_grid(rows * cols // 16),
+                amax_bits=None if rht else int(chunk_max_bits(xh, rows * cols).max()))
+    three = fq.fp4_tensor_scale(x, cfg)
     assert bits(three) == want
-    assert counters_zero(ws)
 
 
 @pytest.mark.parametrize("k", list(range(1, 19)) + [63, 64, 65, 1023, 1024, 1100])
@@ -88,9 +83,12 @@ def test_one_launch_tensor_scale_grid_sizes(fq, ws, k, tail):
     n = (k - 1) * cols + (16 if tail else cols)
     flat = np.ascontiguousarray(xh).reshape(-1)[:n].reshape(1, n)
     cfg = fq.Fp4Config()
+    e0 = epoch(ws)
     got = fq.fp4_tensor_scale_ws(dev(flat), cfg, ws)
     assert bits(got) == np.float32(O.tensor_scale(O.Cfg(), flat)).view(np.uint32)
-    assert counters_zero(ws)
+    # up to 1024 workgroups, workgroup b takes row b (1024 groups)
+    check_after(ws, e0, ts_grid(n // 16), wg_max_bits=chunk_max_bits(flat, cols) if k <= 1024 else None,
+                amax_bits=int(chunk_max_bits(flat, n).max()))
 
 
 def test_one_launch_tensor_scale_special_inputs(fq, ws):
@@ -104,9 +102,15 @@ def test_one_launch_tensor_scale_special_inputs(fq, ws):
     xf = np.random.default_rng(3).standard_normal((300, 512)).astype(np.float32)
     xf[7, 9], xf[100, 0], xf[299, 511] = np.inf, -np.inf, np.nan
     xh = W.f32_to_bf16_rne(xf)
+    e0 = epoch(ws)
     got = fq.fp4_tensor_scale_ws(dev(xh), cfg, ws)
     assert bits(got) == np.float32(O.tensor_scale(oc, xh)).view(np.uint32)
-    assert counters_zero(ws)
+    check_after(ws, e0, ts_grid(300 * 512 // 16), amax_bits=int(chunk_max_bits(xh, xh.size).max()))
+    # a workspace zero-filled again is a valid start
+    ws.zero_()
+    got = fq.fp4_tensor_scale_ws(dev(xh), cfg, ws)
+    assert bits(got) == np.float32(O.tensor_scale(oc, xh)).view(np.uint32)
+    check_after(ws, 0, ts_grid(300 * 512 // 16))
 
 
 def test_one_launch_tensor_scale_in_a_graph(fq, ws):
@@ -131,6 +135,7 @@ def test_one_launch_tensor_scale_in_a_graph(fq, ws):
         torch.cuda.synchronize()
         assert [bits(o) for o in outs] == want, rep
         # eager work between the replays
+        e0 = epoch(ws)
         fq.fp4_tensor_scale_ws(xs[rep], cfg, ws, out=outs[rep])
         assert bits(outs[rep]) == want[rep]
-    assert counters_zero(ws)
+        check_after(ws, e0, ts_grid(2048 * 2048 // 16))
