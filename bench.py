@@ -770,7 +770,30 @@ def gemm_workload(args, fq, torch, W):
         "speedup_vs_two_launches": round(ms_2 / ms_f, 3),
         "equals_product_then_quantize": bool(same),
         "bytes_written": M * N // 2 + M * N // 32 + M * N // 8, "bytes_of_bf16_c_not_written": 2 * M * N}
-    del qc, qs, qb, cb, ref, outs, ws, prods, arr
+    # the same with the result stored as NVFP4 under a given tensor scale (a KV-cache write), against the
+    # plain product followed by fp4_quantize (NVFP4, RTN, emission) with that scale
+    nv = fq.Fp4Config()
+    ts = fq.fp4_tensor_scale(cb, nv)
+    ns_ = torch.empty(M * N // 16, dtype=torch.uint8, device="cuda")
+    fq.fp4_gemm_mxfp4_quantize_nvfp4(a, asc, b, bsc, M, N, K, ts, codes=qc, scales=ns_, bits=qb)
+    ref = fq.fp4_quantize(cb, nv, ts, emit=True)
+    same_nv = all(torch.equal(x, y) for x, y in zip((qc, ns_, qb), ref))
+    ms_fn = back_to_back(torch, lambda i: fq.fp4_gemm_mxfp4_quantize_nvfp4(a, asc, b, bsc, M, N, K, ts, codes=qc,
+                                                                          scales=ns_, bits=qb), reps, warm=5)
+    sp_fn = take_spread()
+
+    def two_step_nv(i):
+        fq.fp4_gemm_mxfp4(a, asc, b, bsc, M, N, K, out=cb)
+        fq.fp4_quantize(cb, nv, ts, emit=True, codes=qc, scales=ns_, bits=qb)
+    ms_2n = back_to_back(torch, two_step_nv, reps, warm=5)
+    res["fused_quantize_epilogue_nvfp4"] = {
+        "us": round(ms_fn * 1e3, 2), "TFLOPs": round(flops / (ms_fn * 1e-3) / 1e12, 1),
+        "us_p10_median_p90_single_launch": sp_fn,
+        "us_product_bf16_then_quantize_emit": round(ms_2n * 1e3, 2),
+        "speedup_vs_two_launches": round(ms_2n / ms_fn, 3),
+        "equals_product_then_quantize": bool(same_nv),
+        "bytes_written": M * N // 2 + M * N // 16 + M * N // 8, "bytes_of_bf16_c_not_written": 2 * M * N}
+    del qc, qs, qb, cb, ref, outs, ws, prods, arr, ns_, ts
     # a square product, 16384^3 with bf16 out (256 x 256 tiles, 16 rounds): random E2M1 codes and
     # E8M0 scales 120..130, drawn on the device
     S = 16384

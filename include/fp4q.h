@@ -320,6 +320,27 @@ fp4_status fp4_gemm_mxfp4_quantize(const void* a_codes, const void* a_scales, co
                                    const void* b_scales, int64_t M, int64_t N, int64_t K, void* c_codes,
                                    void* c_scales, void* c_guide_bits, hipStream_t stream);
 
+/* The same product with its result quantized to NVFP4 instead [TRACE-JA
+ * "実験結果": FP4 KV cache; "量子化情報キャッシュ": the rollout's codewords;
+ * FQT-FP4 section 3: E4M3 block scales under one fp32 tensor scale], for a
+ * producer whose output is stored as NVFP4, such as the K and V projections
+ * writing the KV cache: C = A * B^T exactly as fp4_gemm_mxfp4 computes it,
+ * rounded to bf16, then quantized along its rows as fp4_quantize does with
+ * format NVFP4, the E2M1 grid and round to nearest under the given tensor
+ * scale: codes [M, N/2], E4M3 scales [M, N/16] and, when c_guide_bits is not
+ * NULL, the guide bitplane [M, N/8].  Bit for bit equal to fp4_gemm_mxfp4 with
+ * bf16 output followed by fp4_quantize (NVFP4, RTN, emission, tensor_scale).
+ *   tensor_scale   device pointer to s_t (positive and finite), for example
+ *                  the previous step's, or a calibrated value: the product's
+ *                  own amax is not known until every tile is done.
+ *   N % 32 == 0 (FP4_ERR_SHAPE); K and the scale pointers as for
+ *   fp4_gemm_mxfp4_quantize; c_codes and c_guide_bits 16-byte aligned,
+ *   c_scales 2-byte aligned. */
+fp4_status fp4_gemm_mxfp4_quantize_nvfp4(const void* a_codes, const void* a_scales, const void* b_codes,
+                                         const void* b_scales, int64_t M, int64_t N, int64_t K,
+                                         const float* tensor_scale, void* c_codes, void* c_scales,
+                                         void* c_guide_bits, hipStream_t stream);
+
 /* One product of a grouped call (fields as in fp4_gemm_mxfp4). */
 typedef struct {
     const void* a_codes;

@@ -523,9 +523,9 @@ fp4_status fp4_gemm_mxfp4(const void* a_codes, const void* a_scales, const void*
     return hip_status(fp4q::launch_gemm_mx(dtype == FP4_OUT_BF16, p, stream), "gemm launch");
 }
 
-fp4_status fp4_gemm_mxfp4_quantize(const void* a_codes, const void* a_scales, const void* b_codes,
-                                   const void* b_scales, int64_t M, int64_t N, int64_t K, void* c_codes,
-                                   void* c_scales, void* c_guide_bits, hipStream_t stream) {
+static fp4_status gemm_quantize(const void* a_codes, const void* a_scales, const void* b_codes,
+                                const void* b_scales, int64_t M, int64_t N, int64_t K, const float* tensor_scale,
+                                void* c_codes, void* c_scales, void* c_guide_bits, hipStream_t stream) {
     fp4q::GemmParams p{};
     bool empty = false;
     FP4Q_TRY(gemm_params(a_codes, a_scales, b_codes, b_scales, M, N, K, nullptr, 0, FP4_OUT_BF16, &p, &empty, false));
@@ -536,7 +536,7 @@ fp4_status fp4_gemm_mxfp4_quantize(const void* a_codes, const void* a_scales, co
     if ((uint64_t)M * (uint64_t)N / 16 >= (1ull << 31))
         return fail(FP4_ERR_SHAPE, "result too large to quantize (%lld x %lld)", (long long)M, (long long)N);
     FP4Q_TRY(need(c_codes, 16, "c_codes"));
-    FP4Q_TRY(need(c_scales, 1, "c_scales"));
+    FP4Q_TRY(need(c_scales, tensor_scale ? 2 : 1, "c_scales"));   // NVFP4: two scale bytes per store
     if (c_guide_bits) FP4Q_TRY(need(c_guide_bits, 16, "c_guide_bits"));
     if (!fp4q::gemm_quant_supported(p))
         return fail(FP4_ERR_UNSUPPORTED, "the quantizing product needs K a positive multiple of 512 (K=%lld) and "
@@ -544,7 +544,24 @@ fp4_status fp4_gemm_mxfp4_quantize(const void* a_codes, const void* a_scales, co
     p.qcodes = static_cast<uint8_t*>(c_codes);
     p.qscales = static_cast<uint8_t*>(c_scales);
     p.qbits = static_cast<uint8_t*>(c_guide_bits);
+    p.qts = tensor_scale;
     return hip_status(fp4q::launch_gemm_mx_quant(p, stream), "quantizing gemm launch");
+}
+
+fp4_status fp4_gemm_mxfp4_quantize(const void* a_codes, const void* a_scales, const void* b_codes,
+                                   const void* b_scales, int64_t M, int64_t N, int64_t K, void* c_codes,
+                                   void* c_scales, void* c_guide_bits, hipStream_t stream) {
+    return gemm_quantize(a_codes, a_scales, b_codes, b_scales, M, N, K, nullptr, c_codes, c_scales, c_guide_bits,
+                         stream);
+}
+
+fp4_status fp4_gemm_mxfp4_quantize_nvfp4(const void* a_codes, const void* a_scales, const void* b_codes,
+                                         const void* b_scales, int64_t M, int64_t N, int64_t K,
+                                         const float* tensor_scale, void* c_codes, void* c_scales,
+                                         void* c_guide_bits, hipStream_t stream) {
+    FP4Q_TRY(need(tensor_scale, 4, "tensor_scale"));
+    return gemm_quantize(a_codes, a_scales, b_codes, b_scales, M, N, K, tensor_scale, c_codes, c_scales,
+                         c_guide_bits, stream);
 }
 
 fp4_status fp4_gemm_mxfp4_grouped(int n, const fp4_gemm_desc* products, fp4_dtype dtype, hipStream_t stream) {

@@ -31,8 +31,9 @@
 // edge tiles store element by element through a buffer range that drops what
 // lies outside C.
 // The same K loop can instead end in the MXFP4 quantization of the
-// bf16-rounded product (the producer-side epilogue): C is then not written,
-// only its codes, scales and guide bits.
+// bf16-rounded product, or its NVFP4 quantization under a given tensor scale
+// (the producer-side epilogue): C is then not written, only its codes, scales
+// and guide bits.
 //
 // Other K (multiples of 32), k_gemm_mx_any: 128 x 128 tiles, K advancing 128
 // values per stage through registers into LDS rows padded to 80 bytes.
@@ -400,12 +401,69 @@ __device__ __forceinline__ uint32_t quantize_block32_bf16(const uint32_t w[16], 
     return sc;
 }
 
+// The NVFP4 tensor scale's per-launch terms: the block divisor RN(6 s_t), its
+// reciprocal, and whether that reciprocal is a normal number.
+struct NvScale {
+    float ts, denom, rden;
+    bool rden_ok;
+};
+
+__device__ __forceinline__ NvScale nv_scale(float ts) {
+    NvScale n;
+    n.ts = ts;
+    n.denom = 6.0f * ts;
+    n.rden = 1.0f / n.denom;
+    n.rden_ok = n.denom >= 0x1p-125f && n.denom <= 0x1p125f;
+    return n;
+}
+
+// NVFP4 round-to-nearest quantization of two 16-element groups of bf16 values
+// (w[0..7] the first, w[8..15] the second, element 2j in the low half of a
+// dword), as the NVFP4 quantizer does it without the RHT: per group the scale
+// code is the E4M3 RNE of amax / RN(6 s_t), saturating at 448 (the quotient taken
+// as a product with the reciprocal wherever that gives the same code, else
+// divided), the elements are multiplied by RN(1 / RN(dec(code) s_t)) and rounded
+// to E2M1 ties to even; a group holding a non-finite value gets scale 0x7F and
+// zero codes.  Returns the two scale codes, the first in the low byte; c
+// receives the 16 bytes of codes.
+__device__ __forceinline__ uint32_t quantize_2x16_nvfp4_bf16(const uint32_t w[16], const NvScale& ns,
+                                                             uint32_t c[4]) {
+    uint32_t scs = 0;
+    #pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const uint32_t* gw = w + 8 * g;
+        const uint32_t key = amax_bits16(gw) << 16;
+        float t = __uint_as_float(key) * ns.rden;
+        const uint32_t tb = __float_as_uint(t);
+        // the product gives the quotient's E4M3 code unless it lies within 4 fp32
+        // steps of a code midpoint, or below 2^-6 + 4 steps (and is not 0)
+        if (!ns.rden_ok || tb - 1u < 0x3C800003u || (tb & 0xFFFFFu) - 0x7FFFCu <= 8u)
+            t = __uint_as_float(key) / ns.denom;
+        uint32_t sc = e4m3_encode_rne(clamp448(t));
+        const float inv = nvfp4_inv(sc, ns.ts);
+        float y[16];
+        widen16<false>(gw, 0u, y);
+        #pragma unroll
+        for (int j = 0; j < 16; ++j) y[j] = y[j] * inv;
+        uint32_t c0 = encode8<0, MODE_RTN>(y, 0u, 0u, 0u), c1 = encode8<0, MODE_RTN>(y + 8, 0u, 0u, 0u);
+        if (key >= 0x7F800000u) {
+            sc = 0x7Fu;
+            c0 = c1 = 0u;
+        }
+        c[2 * g] = c0;
+        c[2 * g + 1] = c1;
+        scs |= sc << (8 * g);
+    }
+    return scs;
+}
+
 // Producer-side epilogue: the wave's quarter of C, rounded to bf16, goes through
 // LDS half its rows at a time (as the staged store does); then each lane takes
-// one 32-element block of a row, quantizes it to MXFP4 with round to nearest and
-// writes its 16 bytes of codes, its scale byte and, when asked for, its 32 guide
-// bits.  N % 32 == 0, so a block lies wholly inside or outside C.
-template <int WM, int WN>
+// 32 consecutive elements of a row (one MXFP4 block, or two NVFP4 groups under
+// the tensor scale *p.qts when NV), quantizes them with round to nearest and
+// writes their 16 bytes of codes, their scale byte(s) and, when asked for, their
+// 32 guide bits.  N % 32 == 0, so the 32 elements lie wholly inside or outside C.
+template <int WM, int WN, bool NV>
 __device__ __forceinline__ void quantize_epilogue(const GemmParams& p, const v16f (&acc)[WM][WN], uint8_t* smem,
                                                   int wave, int lane, int kc, int r32, int64_t row0, int64_t col0) {
     constexpr int HR = 16 * WM;              // rows per half
@@ -413,7 +471,9 @@ __device__ __forceinline__ void quantize_epilogue(const GemmParams& p, const v16
     constexpr int NB = HR * WN;              // 32-element blocks per half
     static_assert(NB % 64 == 0, "whole wave instructions per half");
     uint8_t* st = smem + wave * HR * PITCH;
-    const int64_t cb = p.N / 2, sb = p.N / 32, bb = p.N / 8;   // bytes per row of codes, scales, bits
+    const int64_t cb = p.N / 2, sb = p.N / (NV ? 16 : 32), bb = p.N / 8;   // bytes per row of codes, scales, bits
+    NvScale ns{};
+    if constexpr (NV) ns = nv_scale(*p.qts);
     barrier_only();   // every wave is done with the K loop's LDS
     #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -438,11 +498,12 @@ __device__ __forceinline__ void quantize_epilogue(const GemmParams& p, const v16
                 w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
             }
             uint32_t codes[4];
-            const uint32_t sc = quantize_block32_bf16(w, codes);
+            const uint32_t sc = NV ? quantize_2x16_nvfp4_bf16(w, ns, codes) : quantize_block32_bf16(w, codes);
             const int64_t row = row0 + h * HR + r, col = col0 + 32 * blk;
             if (row < p.M && col < p.N) {
                 *reinterpret_cast<v4u32*>(p.qcodes + row * cb + col / 2) = (v4u32){codes[0], codes[1], codes[2], codes[3]};
-                p.qscales[row * sb + col / 32] = (uint8_t)sc;
+                if constexpr (NV) *reinterpret_cast<uint16_t*>(p.qscales + row * sb + col / 16) = (uint16_t)sc;
+                else p.qscales[row * sb + col / 32] = (uint8_t)sc;
                 if (p.qbits) {
                     const uint32_t bits = gather_nibble_lsbs(codes[0]) | (gather_nibble_lsbs(codes[1]) << 8) |
                                           (gather_nibble_lsbs(codes[2]) << 16) | (gather_nibble_lsbs(codes[3]) << 24);
@@ -469,10 +530,11 @@ __device__ __forceinline__ void interleave() {
     if (NV > NM) __builtin_amdgcn_sched_group_barrier(0x020, NV > NM ? NV - NM : 1, 0);
 }
 
-// Tile (tm, tn) of the product p, computed by the calling workgroup.  QUANT: the
-// epilogue quantizes the bf16-rounded tile (p.qcodes, p.qscales, p.qbits)
+// Tile (tm, tn) of the product p, computed by the calling workgroup.  QUANT 1
+// (MXFP4) or 2 (NVFP4): the epilogue quantizes the bf16-rounded tile (p.qcodes,
+// p.qscales, p.qbits)
 // instead of storing C.
-template <int WM, int WN, bool BF16, bool QUANT = false>
+template <int WM, int WN, bool BF16, int QUANT = 0>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint32_t tn, uint8_t* smem) {
     using T = LdsTile<WM, WN>;
     const int t = threadIdx.x, lane = t & 63;
@@ -626,8 +688,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint
     }
     // the loads issued past the last stage must land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
-    if constexpr (QUANT) {
-        quantize_epilogue<WM, WN>(p, acc, smem, wave, lane, kc, r32, m0 + wm * 32 * WM, n0 + wn * 32 * WN);
+    if constexpr (QUANT != 0) {
+        quantize_epilogue<WM, WN, QUANT == 2>(p, acc, smem, wave, lane, kc, r32, m0 + wm * 32 * WM,
+                                              n0 + wn * 32 * WN);
         return;
     }
 
@@ -721,7 +784,7 @@ __device__ __forceinline__ void grouped_tile(uint32_t bid, uint32_t tiles_m, uin
     tn = r / rows;
 }
 
-template <int WM, int WN, bool BF16, bool QUANT = false>
+template <int WM, int WN, bool BF16, int QUANT = 0>
 __global__ __launch_bounds__(256) void k_gemm_mx_lds(const GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const uint32_t bid = xcd_tile(p.xcd_remap);
@@ -745,7 +808,7 @@ __global__ __launch_bounds__(256) void k_gemm_mx_lds_grouped(const GroupedGemmPa
 }
 
 template <int WM, int WN>
-static hipError_t launch_lds(bool bf16_out, GemmParams p, hipStream_t s, bool quant = false) {
+static hipError_t launch_lds(bool bf16_out, GemmParams p, hipStream_t s, int quant = 0) {
     using T = LdsTile<WM, WN>;
     const uint32_t tiles_m = (uint32_t)((p.M + T::RA - 1) / T::RA);
     p.tiles_n = (uint32_t)((p.N + T::RB - 1) / T::RB);
@@ -753,7 +816,8 @@ static hipError_t launch_lds(bool bf16_out, GemmParams p, hipStream_t s, bool qu
     p.xcd_remap = g % 8 == 0 ? 1u : 0u;
     const int esz = bf16_out ? 2 : 4;
     p.staged = ((uintptr_t)p.c & 15) == 0 && (p.ldc * esz) % 16 == 0 ? 1u : 0u;
-    if (quant) hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, true, true>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
+    if (quant == 2) hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, true, 2>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
+    else if (quant) hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, true, 1>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
     else if (bf16_out) hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, true>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
     else hipLaunchKernelGGL((k_gemm_mx_lds<WM, WN, false>), dim3(g), dim3(256), T::LDS_BYTES, s, p);
     return hipGetLastError();
@@ -808,10 +872,11 @@ hipError_t launch_gemm_mx_grouped(bool bf16_out, const GroupedGemmParams& gp, hi
 bool gemm_quant_supported(const GemmParams& p) { return main_path_ok(p); }
 
 hipError_t launch_gemm_mx_quant(const GemmParams& p, hipStream_t s) {
+    const int q = p.qts ? 2 : 1;
     switch (gemm_config(p.M, p.N)) {
-        case 2: return launch_lds<4, 4>(true, p, s, true);
-        case 1: return launch_lds<4, 3>(true, p, s, true);
-        default: return launch_lds<2, 2>(true, p, s, true);
+        case 2: return launch_lds<4, 4>(true, p, s, q);
+        case 1: return launch_lds<4, 3>(true, p, s, q);
+        default: return launch_lds<2, 2>(true, p, s, q);
     }
 }
 

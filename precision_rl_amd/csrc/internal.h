@@ -148,9 +148,10 @@ struct GemmParams {
     uint32_t tiles_n;           // column tiles of C
     uint32_t xcd_remap;         // 1: hand out tiles XCD by XCD (grid size a multiple of 8)
     uint32_t staged;            // 1: C and its rows 16-byte aligned (whole tiles stored through LDS)
-    uint8_t* qcodes;            // quantize epilogue: MXFP4 codes of the bf16-rounded C, [M, N/2]
-    uint8_t* qscales;           // ... E8M0 scales [M, N/32]
+    uint8_t* qcodes;            // quantize epilogue: codes of the bf16-rounded C, [M, N/2]
+    uint8_t* qscales;           // ... E8M0 scales [M, N/32], or E4M3 scales [M, N/16] (NVFP4)
     uint8_t* qbits;             // ... guide bits [M, N/8], or null
+    const float* qts;           // ... NVFP4: the tensor scale s_t; null: MXFP4
 };
 
 // Launchers (return hipGetLastError() of the launch).
@@ -199,7 +200,8 @@ hipError_t launch_encode_values(int grid, int mode, const EncodeParams& p, hipSt
 hipError_t launch_encode_scales(const float* t, uint8_t* out, uint32_t n4, hipStream_t s);
 hipError_t launch_gemm_mx(bool bf16_out, const GemmParams& p, hipStream_t s);
 // The same product ending in the MXFP4 RTN quantization of its bf16-rounded
-// result (p.qcodes, p.qscales, p.qbits); only where gemm_quant_supported(p).
+// result (p.qcodes, p.qscales, p.qbits; NVFP4 under *p.qts when p.qts is not
+// null, else MXFP4); only where gemm_quant_supported(p).
 bool gemm_quant_supported(const GemmParams& p);
 hipError_t launch_gemm_mx_quant(const GemmParams& p, hipStream_t s);
 

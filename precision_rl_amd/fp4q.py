@@ -56,8 +56,18 @@ class Fp4Config:
         return 32 if self.format == MXFP4 else 16
 
     def c(self) -> _CCfg:
-        return _CCfg(self.format, self.grid, self.rounding, int(bool(self.rht16)), self.sr_seed,
-                     self.sr_offset, self.rht_seed)
+        """The C struct of these fields (shared by calls with equal fields; the library only reads it)."""
+        key = (self.format, self.grid, self.rounding, int(bool(self.rht16)), self.sr_seed, self.sr_offset,
+               self.rht_seed)
+        cc = _CFG_CACHE.get(key)
+        if cc is None:
+            if len(_CFG_CACHE) >= 4096:      # e.g. an SR offset that advances every step
+                _CFG_CACHE.clear()
+            cc = _CFG_CACHE[key] = _CCfg(*key)
+        return cc
+
+
+_CFG_CACHE: dict = {}
 
 
 class _CTensor(C.Structure):
@@ -74,7 +84,8 @@ EXPORTS = ("fp4_tensor_scale", "fp4_tensor_scale_ws", "fp4_tensor_scale_workspac
            "fp4_tensor_scale_noalloc", "fp4_quantize", "fp4_quantize_guided", "fp4_quantize_grouped",
            "fp4_fake_quantize", "fp4_guide_mismatch", "fp4_dequantize", "guide_pack", "guide_pack_grouped",
            "guide_unpack",
-           "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_gemm_mxfp4_quantize", "fp4_rht16",
+           "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_gemm_mxfp4_quantize", "fp4_gemm_mxfp4_quantize_nvfp4",
+           "fp4_rht16",
            "fp4_encode_values", "fp4_encode_scales", "fp4_stream_copy", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
            "fp4_status_str", "fp4_last_error")
 
@@ -118,6 +129,7 @@ def lib():
         "fp4_gemm_mxfp4": [P, P, P, P, I64, I64, I64, P, I64, I, P],
         "fp4_gemm_mxfp4_grouped": [I, C.POINTER(_CGemm), I, P],
         "fp4_gemm_mxfp4_quantize": [P, P, P, P, I64, I64, I64, P, P, P, P],
+        "fp4_gemm_mxfp4_quantize_nvfp4": [P, P, P, P, I64, I64, I64, P, P, P, P, P],
         "fp4_rht16": [P, I64, I64, I64, C.c_uint64, I, P, I, P],
         "fp4_encode_values": [I, I, P, P, I64, P, P],
         "fp4_encode_scales": [P, I64, P, P],
@@ -148,12 +160,18 @@ def _check(status: int, where: str):
         raise Fp4Error(status, where, lib().fp4_last_error().decode())
 
 
-def _stream(t: torch.Tensor):
-    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(t: torch.Tensor) -> int:
+    """The current HIP stream of t's device, as an address (ctypes passes ints as void*)."""
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _ptr(t):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _on_gpu(*ts):
@@ -402,6 +420,25 @@ def fp4_gemm_mxfp4_quantize(a_codes: torch.Tensor, a_scales: torch.Tensor, b_cod
     _check(lib().fp4_gemm_mxfp4_quantize(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
                                          _ptr(codes), _ptr(scales), _ptr(bits) if emit else None,
                                          _stream(a_codes)), "fp4_gemm_mxfp4_quantize")
+    return (codes, scales, bits) if emit else (codes, scales)
+
+
+def fp4_gemm_mxfp4_quantize_nvfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor,
+                                  b_scales: torch.Tensor, M: int, N: int, K: int, tensor_scale: torch.Tensor,
+                                  emit: bool = True, codes=None, scales=None, bits=None):
+    """NVFP4 codes, E4M3 scales (and guide bits) of the bf16-rounded C = A * B^T under the tensor scale
+    ``tensor_scale`` (f32[1] on the device), quantized in the product's epilogue.  Returns
+    (codes, scales[, bits])."""
+    _on_gpu(a_codes, a_scales, b_codes, b_scales, tensor_scale, codes, scales, bits)
+    n = M * N
+    codes = _u8(n // 2, a_codes) if codes is None else codes
+    scales = _u8(n // 16, a_codes) if scales is None else scales
+    if emit and bits is None:
+        bits = _u8(n // 8, a_codes)
+    _check(lib().fp4_gemm_mxfp4_quantize_nvfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N,
+                                               K, _ptr(tensor_scale), _ptr(codes), _ptr(scales),
+                                               _ptr(bits) if emit else None, _stream(a_codes)),
+           "fp4_gemm_mxfp4_quantize_nvfp4")
     return (codes, scales, bits) if emit else (codes, scales)
 
 

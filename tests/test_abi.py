@@ -31,7 +31,7 @@ def test_header_declares_the_expected_calls():
     names = _declared()
     for n in ["fp4_quantize", "fp4_quantize_guided", "fp4_dequantize", "guide_pack", "guide_unpack", "fp4_guide_mismatch",
               "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "guide_pack_grouped", "fp4_rht16", "fp4_tensor_scale", "fp4_encode_values", "fp4_codes_bytes",
-              "fp4_quantize_with_tensor_scale",
+              "fp4_quantize_with_tensor_scale", "fp4_gemm_mxfp4_quantize", "fp4_gemm_mxfp4_quantize_nvfp4",
               "fp4_scales_bytes", "fp4_guide_bytes", "fp4_status_str", "fp4_last_error"]:
         assert n in names, n
 
@@ -237,3 +237,16 @@ def test_gemm_quantize_host_side_errors(fq):
     assert g(p, p, p, p, 64, 64, 512, p, p, C.c_void_p(A + 4), None) == 3   # misaligned bits
     assert g(p, p, p, p, 0, 64, 512, None, None, None, None) == 0    # empty: no-op
     assert g(p, p, C.c_void_p(A + 1), p, 64, 64, 512, p, p, p, None) == 3   # misaligned B codes
+
+
+def test_gemm_quantize_nvfp4_host_side_errors(fq):
+    g = fq.lib().fp4_gemm_mxfp4_quantize_nvfp4
+    A = 1 << 20
+    p = C.c_void_p(A)
+    assert g(p, p, p, p, 64, 64, 512, None, p, p, p, None) == 1               # no tensor scale
+    assert g(p, p, p, p, 64, 64, 512, C.c_void_p(A + 2), p, p, p, None) == 3  # misaligned tensor scale
+    assert g(p, p, p, p, 64, 48, 512, p, p, p, p, None) == 2                  # N % 32
+    assert g(p, p, p, p, 64, 64, 544, p, p, p, p, None) == 4                  # K not a multiple of 512
+    assert g(p, p, p, p, 64, 64, 512, p, p, C.c_void_p(A + 1), p, None) == 3  # scales: two bytes per store
+    assert g(p, p, p, p, 64, 64, 512, p, None, p, p, None) == 1               # no codes
+    assert g(p, p, p, p, 0, 64, 512, p, None, None, None, None) == 0          # empty: no-op

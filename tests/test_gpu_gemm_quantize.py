@@ -12,7 +12,11 @@ Shapes cover the three tile configurations (128 x 128, 256 x 192 and, for
 8192 x 1536 x 4096 product (sampled rows).  On
 Gaussian activations and weights quantized by the library, the fused kernel
 equals the plain product with bf16 output followed by fp4_quantize, bit for bit
-over whole tensors.  Outputs start as 0xA5 bytes.
+over whole tensors.  The NVFP4 form (fp4_gemm_mxfp4_quantize_nvfp4: E4M3 scales
+of 16-element groups under a given tensor scale) is checked the same two ways,
+with tensor scales that reach both the product and the divided form of the
+scale quotient, saturated scales and all-zero groups.  Outputs start as 0xA5
+bytes.
 """
 import numpy as np
 import pytest
@@ -86,3 +90,59 @@ def test_fused_equals_product_then_quantize(fq, M, N, K):
     for f, t in zip(fused, two_step):
         assert torch.equal(f, t)
     assert torch.equal(no_bits[0], fused[0]) and torch.equal(no_bits[1], fused[1])
+
+
+def nv_oracle_check(gc, gs, gb, xb, rows, ts, N):
+    oc = O.Cfg()
+    for i, r in enumerate(rows):
+        wc, ws, wb = O.quantize(oc, O.RTN, xb[i:i + 1], ts, row0=r, emit=True)
+        assert (gs[r] == ws).all(), ("scales", r)
+        assert (gc[r] == wc).all(), ("codes", r)
+        assert (gb[r] == wb).all(), ("bits", r)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 192, 512), (300, 160, 1024), (1, 32, 512), (129, 992, 1536),
+                                   (8192, 1536, 4096), (4000, 4000, 512)])
+def test_fused_nvfp4_vs_oracle_on_exact_products(fq, M, N, K):
+    a, asc = W.mx_operand(M, K, seed=M + 11, stream=0, scale_lo=126, scale_hi=128)
+    b, bsc = W.mx_operand(N, K, seed=N + 13, stream=2, scale_lo=126, scale_hi=128)
+    A, As, B, Bs = dev(a), dev(asc), dev(b), dev(bsc)
+    rows = sample(M, seed=K + 1)
+    exact, _ = O.gemm_mx(a.reshape(M, -1)[rows], asc.reshape(M, -1)[rows], b, bsc, len(rows), N, K)
+    xb = W.f32_to_bf16_rne(exact.astype(np.float32))
+    # the tensor scale of the sampled rows (the product form of the scale quotient), one so small
+    # that every scale saturates at 448 and the quotient is divided (6 s_t below 2^-125), and one so
+    # large that 6 s_t exceeds 2^125 (divided, most scales and codes 0)
+    for ts in (O.tensor_scale(O.Cfg(), xb), 1e-39, 1e37):
+        t = torch.tensor([ts], dtype=torch.float32, device="cuda")
+        codes, scales, bits = fq.fp4_gemm_mxfp4_quantize_nvfp4(A, As, B, Bs, M, N, K, t)
+        torch.cuda.synchronize()
+        nv_oracle_check(codes.cpu().numpy().reshape(M, N // 2), scales.cpu().numpy().reshape(M, N // 16),
+                        bits.cpu().numpy().reshape(M, N // 8), xb, rows, float(t.cpu()[0]), N)
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 1024, 4096), (1000, 608, 2048), (256, 192, 512), (4000, 4000, 1024)])
+def test_fused_nvfp4_equals_product_then_quantize(fq, M, N, K):
+    # the K and V projections of a KV cache: activations times a weight, the product stored as NVFP4
+    cfg = fq.Fp4Config(format=fq.MXFP4)
+    nv = fq.Fp4Config()
+    xa = W.f32_to_bf16_rne(W.normal_outliers_f32(M, K, 1030, 16, 0.0, 1.0))
+    xw = W.f32_to_bf16_rne(W.normal_outliers_f32(N, K, 1030, 0, 0.0, 1.0, sigma=0.02))
+    tod = lambda h: torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).cuda()
+    a, asc = fq.fp4_quantize(tod(xa), cfg)
+    b, bsc = fq.fp4_quantize(tod(xw), cfg)
+    c = fq.fp4_gemm_mxfp4(a, asc, b, bsc, M, N, K, dtype=torch.bfloat16)
+    ts = fq.fp4_tensor_scale(c, nv)
+    fused = fq.fp4_gemm_mxfp4_quantize_nvfp4(a, asc, b, bsc, M, N, K, ts)
+    two_step = fq.fp4_quantize(c, nv, ts, emit=True)
+    no_bits = fq.fp4_gemm_mxfp4_quantize_nvfp4(a, asc, b, bsc, M, N, K, ts, emit=False)
+    torch.cuda.synchronize()
+    for f, t in zip(fused, two_step):
+        assert torch.equal(f, t)
+    assert torch.equal(no_bits[0], fused[0]) and torch.equal(no_bits[1], fused[1])
+    # a zero weight: every group of C is zero (scale 0, codes 0)
+    z = torch.zeros_like(b)
+    zs = torch.full_like(bsc, 127)
+    zc, zsc, zb = fq.fp4_gemm_mxfp4_quantize_nvfp4(a, asc, z, zs, M, N, K, ts)
+    torch.cuda.synchronize()
+    assert int(zc.count_nonzero()) == 0 and int(zsc.count_nonzero()) == 0 and int(zb.count_nonzero()) == 0
