@@ -133,6 +133,11 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             gs[k] = p.gscales[FMT == 0 ? g : (g >> 1)];
         }
     }
+    // Every load of the chunk is issued before any of its data is used: left to
+    // itself the compiler issues the second group's guide loads after the wait
+    // for the first x loads, and their whole latency then ends the wave's life
+    // (C2 guided quantize, guides from HBM: 32.6 against 30.2 us without them).
+    if constexpr (MODE == MODE_GUIDED) __builtin_amdgcn_sched_barrier(0);
     uint32_t n_skip = 0, n_nonadj = 0, n_mism = 0;   // OUT == 2
 
     const uint32_t signs = RHT ? rht_sign_mask(p.rht_seed) : 0u;   // uniform: scalar unit
