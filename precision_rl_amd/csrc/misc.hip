@@ -209,41 +209,34 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) 
 #endif
 constexpr int kGuideSlots = FP4Q_GUIDE_SLOTS;
 
-// Workgroup wg of guide_pack over one tensor.
+// Workgroup wg of guide_pack over one tensor.  Every load of the workgroup is
+// issued before any of its data is used: lanes past the last whole unit read
+// that unit again (in bounds, no branch) and store nothing.  (Loads under a
+// branch per slot made the compiler wait for the codes before it issued the
+// scale loads, two memory round trips per wave.)  An odd NVFP4 group count
+// leaves a last unit of one group (8 bytes of codes), which the lane that owns
+// it handles on its own.
 template <int FMT>
 __device__ __forceinline__ void guide_pack_wg(const GuideParams& p, uint32_t wg) {
-    // an odd NVFP4 group count leaves a last unit of one group (8 bytes of codes)
-    const uint32_t nunits = (p.ngroups + 1u) >> 1;
-    const uint32_t half_unit = (p.ngroups & 1u) ? nunits - 1u : 0xFFFFFFFFu;
+    const uint32_t nfull = p.ngroups >> 1;              // units of two groups
     const uint32_t u0 = wg * (kThreads * kGuideSlots) + (threadIdx.x >> 6) * (64u * kGuideSlots) +
                         (threadIdx.x & 63u);
-    v4u32 c[kGuideSlots];
-    uint32_t sc[kGuideSlots];
-    #pragma unroll
-    for (int s = 0; s < kGuideSlots; ++s) {
-        const uint32_t u = u0 + 64u * s;
-        c[s] = (v4u32){0u, 0u, 0u, 0u};
-        sc[s] = 0u;
-        if (u < nunits) {
-            if (u != half_unit) {
-                c[s] = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p.in) + u);
-                if constexpr (FMT == 0) sc[s] = p.scales_in[2 * u] | ((uint32_t)p.scales_in[2 * u + 1] << 8);
-                else sc[s] = p.scales_in[u];
-            } else {
-                const v2u32 h = reinterpret_cast<const v2u32*>(p.in)[2 * u];
-                c[s].x = h.x;
-                c[s].y = h.y;
-                sc[s] = p.scales_in[2 * u];
-            }
+    if (nfull > 0) {
+        v4u32 c[kGuideSlots];
+        uint32_t sc[kGuideSlots];
+        #pragma unroll
+        for (int s = 0; s < kGuideSlots; ++s) {
+            const uint32_t u = min(u0 + 64u * s, nfull - 1u);
+            c[s] = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p.in) + u);
+            if constexpr (FMT == 0) sc[s] = p.scales_in[2 * u] | ((uint32_t)p.scales_in[2 * u + 1] << 8);
+            else sc[s] = p.scales_in[u];
         }
-    }
-    #pragma unroll
-    for (int s = 0; s < kGuideSlots; ++s) {
-        const uint32_t u = u0 + 64u * s;
-        if (u >= nunits) continue;
-        const uint32_t bits = gather_nibble_lsbs(c[s].x) | (gather_nibble_lsbs(c[s].y) << 8) |
-                              (gather_nibble_lsbs(c[s].z) << 16) | (gather_nibble_lsbs(c[s].w) << 24);
-        if (u != half_unit) {
+        #pragma unroll
+        for (int s = 0; s < kGuideSlots; ++s) {
+            const uint32_t u = u0 + 64u * s;
+            if (u >= nfull) continue;
+            const uint32_t bits = gather_nibble_lsbs(c[s].x) | (gather_nibble_lsbs(c[s].y) << 8) |
+                                  (gather_nibble_lsbs(c[s].z) << 16) | (gather_nibble_lsbs(c[s].w) << 24);
             st_out(reinterpret_cast<uint32_t*>(p.out) + u, bits);
             if constexpr (FMT == 0) {
                 st_out(p.scales_out + 2 * u, (uint8_t)sc[s]);
@@ -251,9 +244,16 @@ __device__ __forceinline__ void guide_pack_wg(const GuideParams& p, uint32_t wg)
             } else {
                 st_out(p.scales_out + u, (uint8_t)sc[s]);
             }
-        } else {
-            st_out(reinterpret_cast<uint16_t*>(p.out) + 2 * u, (uint16_t)bits);
-            st_out(p.scales_out + 2 * u, (uint8_t)sc[s]);
+        }
+    }
+    if (p.ngroups & 1u) {   // NVFP4 only: the last unit is group 2 nfull alone
+        #pragma unroll
+        for (int s = 0; s < kGuideSlots; ++s) {
+            if (u0 + 64u * s != nfull) continue;
+            const v2u32 h = reinterpret_cast<const v2u32*>(p.in)[2 * nfull];
+            const uint32_t bits = gather_nibble_lsbs(h.x) | (gather_nibble_lsbs(h.y) << 8);
+            st_out(reinterpret_cast<uint16_t*>(p.out) + 2 * nfull, (uint16_t)bits);
+            st_out(p.scales_out + 2 * nfull, p.scales_in[2 * nfull]);
         }
     }
 }
@@ -280,15 +280,15 @@ template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_guide_unpack(const GuideParams p) {
     const uint32_t u0 = blockIdx.x * (kThreads * kGuideSlots) + (threadIdx.x >> 6) * (64u * kGuideSlots) +
                         (threadIdx.x & 63u);
+    if (p.ngroups == 0) return;
+    // every load issued before any is used: lanes past the end read the last
+    // group again (in bounds, no branch) and store nothing
     uint32_t b[kGuideSlots], sc[kGuideSlots];
     #pragma unroll
     for (int s = 0; s < kGuideSlots; ++s) {
-        const uint32_t g = u0 + 64u * s;
-        b[s] = sc[s] = 0u;
-        if (g < p.ngroups) {
-            b[s] = reinterpret_cast<const uint16_t*>(p.in)[g];
-            if (FMT == 0 || (g & 1u) == 0) sc[s] = p.scales_in[FMT == 0 ? g : (g >> 1)];
-        }
+        const uint32_t g = min(u0 + 64u * s, p.ngroups - 1u);
+        b[s] = reinterpret_cast<const uint16_t*>(p.in)[g];
+        sc[s] = p.scales_in[FMT == 0 ? g : (g >> 1)];
     }
     #pragma unroll
     for (int s = 0; s < kGuideSlots; ++s) {
