@@ -43,11 +43,14 @@ constexpr int halves_per_lane() { return FMT == 1 && MODE == MODE_SR && !RHT ? 2
 // Groups per workgroup.
 template <int FMT, int MODE, bool RHT>
 constexpr uint32_t chunk_groups() { return kThreads * (halves_per_lane<FMT, MODE, RHT>() / 2); }
-// A single-tensor launch that would have fewer workgroups than this (8 per
-// compute unit) uses two slots instead of four: twice the workgroups, so more
-// loads in flight across the chip (measured on 4096 x 2048 NVFP4: RTN 5.35
-// against 5.78 us, guided 5.82 against 6.56 us; four slots stay faster on
-// large tensors and in the grouped launches).
+// Single-tensor launches without the RHT take two slots instead of four for RTN
+// and guided rounding (twice the workgroups, so more loads in flight across the
+// chip: 16384 x 4096 MXFP4 RTN 29.5 against 30.0 us, guided 31.0 against 31.6,
+// NVFP4 RTN 29.7 against 30.1, guided 32.2 against 32.5; on 4096 x 2048 NVFP4
+// RTN 5.35 against 5.78 us, guided 5.82 against 6.56), and for SR when they
+// would have fewer workgroups than this (8 per compute unit); NVFP4 SR on large
+// tensors and the grouped launches stay faster with four (C4's grouped rollout
+// RTN: 36.3 against 38.1 us).
 constexpr uint32_t kSmallLaunchBlocks = 2048;
 
 // Number of nonzero nibbles of w.
@@ -504,7 +507,7 @@ hipError_t launch_t(const QuantParams& p, hipStream_t s) {
     constexpr uint32_t kChunkGroups = chunk_groups<FMT, MODE, RHT>();
     const uint32_t blocks = (p.ngroups + kChunkGroups - 1) / kChunkGroups;
     if constexpr (kH == 4 && !RHT) {   // the RHT kernels' LDS transpose is written for four slots
-        if (blocks < kSmallLaunchBlocks) {
+        if (MODE != MODE_SR || blocks < kSmallLaunchBlocks) {
             const uint32_t b2 = (p.ngroups + kThreads - 1) / kThreads;
             hipLaunchKernelGGL((k_quantize<FMT, GRID, MODE, RHT, EMIT, CONTIG, 2>), dim3(b2), dim3(kThreads),
                                0, s, p);

@@ -205,11 +205,11 @@ def test_c5_uniform_rht16_sr_65536x8192(fq):
 @pytest.mark.parametrize("grid", [0, 1])
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_both_slot_counts_at_the_small_launch_threshold(fq, fmt, grid, rows, pad):
-    # A single-tensor launch below 2048 workgroups of four slots takes two slots
-    # per lane: 8191 x 2048 (NVFP4: 2047 workgroups of four) launches two, 8192 x 2048
-    # launches four, and 8193 x 2048 with padded rows launches four with a ragged
-    # last chunk.  All equal the oracle in every mode and on both grids, on the
-    # whole tensor.
+    # A single-tensor SR launch below 2048 workgroups of four slots takes two slots
+    # per lane (RTN and guided always take two): 8191 x 2048 (NVFP4: 2047 workgroups
+    # of four) launches two, 8192 x 2048 launches four, and 8193 x 2048 with padded
+    # rows launches four with a ragged last chunk.  All equal the oracle in every
+    # mode and on both grids, on the whole tensor.
     cols = 2048
     say("slot threshold", fmt, grid, rows, cols, pad)
     xh = W.c1_x(rows, cols, seed=21)
