@@ -623,6 +623,20 @@ __device__ __forceinline__ uint32_t amax_bits16(const uint32_t w[8]) {
     return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
+// ---------------------------------------------------------------- grouped launches
+// The part t of a grouped launch that workgroup b belongs to: start[t] <= b <
+// start[t + 1], for n parts (n <= N) with non-decreasing starts.  Counting the
+// starts at or below b over all N entries at once lets them come in with wide
+// scalar loads; a scan that stops at the first start past b made one dependent
+// load per part before the workgroup could load anything else.
+template <int N>
+__device__ __forceinline__ uint32_t group_of(const uint32_t (&start)[N + 1], uint32_t n, uint32_t b) {
+    uint32_t t = 0;
+    #pragma unroll
+    for (int i = 1; i < N; ++i) t += ((uint32_t)i < n && b >= start[i]) ? 1u : 0u;
+    return t;
+}
+
 // ---------------------------------------------------------------- cross-workgroup maximum
 // Maximum of m over a workgroup of WAVES waves, valid in thread 0.  red: WAVES
 // words of LDS.

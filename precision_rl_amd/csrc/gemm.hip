@@ -799,8 +799,7 @@ template <int WM, int WN, bool BF16>
 __global__ __launch_bounds__(256) void k_gemm_mx_lds_grouped(const GroupedGemmParams gp) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const uint32_t bid = xcd_tile(gp.xcd_remap);
-    uint32_t i = 0;
-    while (i + 1 < gp.n && bid >= gp.tile_start[i + 1]) ++i;
+    const uint32_t i = group_of<kMaxGemmGroup>(gp.tile_start, gp.n, bid);
     const GemmParams& p = gp.g[i];
     const uint32_t local = bid - gp.tile_start[i];
     const uint32_t tm = local / p.tiles_n, tn = local - tm * p.tiles_n;

@@ -267,8 +267,7 @@ __global__ __launch_bounds__(kThreads) void k_guide_pack(const GuideParams p) {
 // wg_start[t] .. wg_start[t + 1] - 1.
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_guide_pack_grouped(const GroupedGuideParams gp) {
-    uint32_t t = 0;
-    while (t + 1 < gp.n && blockIdx.x >= gp.wg_start[t + 1]) ++t;
+    const uint32_t t = group_of<kMaxGroup>(gp.wg_start, gp.n, blockIdx.x);
     guide_pack_wg<FMT>(gp.t[t], blockIdx.x - gp.wg_start[t]);
 }
 

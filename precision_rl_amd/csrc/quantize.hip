@@ -394,13 +394,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const QuantParams p) {
 }
 
 // Several tensors with one configuration in one launch: workgroup b belongs to
-// the tensor t with wg_start[t] <= b < wg_start[t+1] (a uniform scan of at most
-// kMaxGroup entries), and processes that tensor's chunk b - wg_start[t].
+// the tensor t with wg_start[t] <= b < wg_start[t+1] (group_of), and processes
+// that tensor's chunk b - wg_start[t].
 template <int FMT, int GRID, int MODE, bool RHT, bool EMIT>
 __global__ __launch_bounds__(kThreads) void k_quantize_grouped(const GroupedQuantParams gp) {
     const uint32_t b = blockIdx.x;
-    uint32_t t = 0;
-    while (t + 1 < gp.n && b >= gp.wg_start[t + 1]) ++t;
+    const uint32_t t = group_of<kMaxGroup>(gp.wg_start, gp.n, b);
     const uint32_t wg = b - gp.wg_start[t];
     __shared__ float tab[128];
     if ((gp.contig_mask >> t) & 1u)
