@@ -250,7 +250,9 @@ def headline(args, fq, torch, W, ceiling):
     log(f"generating C2 {rows}x{cols} Student-t(4) ...")
     x_h, xr_h = W.c2_pair(rows, cols, seed=1)
     cfg_rtn = fq.Fp4Config(format=fq.MXFP4)
-    cfg_sr = fq.Fp4Config(format=fq.MXFP4, rounding=fq.SR, sr_seed=W.C2_SR_SEED)
+    # SR quantizes the gradient for a later product: no kernel of the step reads its output, which
+    # therefore streams past the caches (stream_out); the others' outputs are read by the next kernel
+    cfg_sr = fq.Fp4Config(format=fq.MXFP4, rounding=fq.SR, sr_seed=W.C2_SR_SEED, stream_out=True)
     P = 3  # rotating input sets: 3 x 256 MiB
     x0, xr0 = to_dev(x_h), to_dev(xr_h)
     xs = [x0] + [torch.roll(x0, shifts=(s * 977), dims=0) for s in range(1, P)]
@@ -660,7 +662,10 @@ def wl_c5(args, fq, torch, W, ceiling):
     n = rows * cols
     log("uniform + RHT16 + SR 65536x8192 (generating 1 GiB) ...")
     x = to_dev(W.c5_x(rows, cols))
-    cfg5 = fq.Fp4Config(grid=fq.UNIFORM, rounding=fq.SR, rht16=True, rht_seed=W.C5_RHT_SEED, sr_seed=W.C5_SR_SEED)
+    # the quantized operand (288 MB, more than the 256 MB Infinity Cache holds) waits for its product:
+    # its stores stream past the caches (stream_out)
+    cfg5 = fq.Fp4Config(grid=fq.UNIFORM, rounding=fq.SR, rht16=True, rht_seed=W.C5_RHT_SEED, sr_seed=W.C5_SR_SEED,
+                        stream_out=True)
     ts = fq.fp4_tensor_scale(x, cfg5)
     outs5 = [(u8(n // 2), u8(n // 16)) for _ in range(2)]   # 2 x 288 MB: the writes cannot stay in the cache
     tso = torch.empty(1, dtype=torch.float32, device="cuda")

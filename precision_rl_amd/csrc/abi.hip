@@ -43,6 +43,8 @@ fp4_status check_cfg(const fp4_cfg* cfg) {
         return fail(FP4_ERR_ARG, "unknown grid %d", cfg->grid);
     if (cfg->rounding != FP4_RTN && cfg->rounding != FP4_SR)
         return fail(FP4_ERR_ARG, "unknown rounding %d", cfg->rounding);
+    if (cfg->stream_out != 0 && cfg->stream_out != 1)
+        return fail(FP4_ERR_ARG, "stream_out=%d is neither 0 nor 1", cfg->stream_out);
     return FP4_OK;
 }
 
@@ -123,6 +125,7 @@ fp4_status fp4_tensor_scale(const fp4_cfg* cfg, const void* x_bf16, int64_t rows
 }
 
 static_assert(FP4_TENSOR_SCALE_WORKSPACE_BYTES == fp4q::kTsWorkspaceBytes, "workspace size in the header");
+static_assert(sizeof(fp4_cfg) == 48, "fp4_cfg layout in the header");
 size_t fp4_tensor_scale_workspace_bytes(void) { return fp4q::kTsWorkspaceBytes; }
 
 fp4_status fp4_tensor_scale_ws(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
@@ -200,6 +203,7 @@ static fp4_status quantize_common(const fp4_cfg* cfg, int mode, const void* x_bf
     p.key1 = (uint32_t)(cfg->sr_seed >> 32);
     p.sr_offset = cfg->sr_offset;
     p.rht_seed = cfg->rht_seed;
+    p.stream_out = (uint32_t)cfg->stream_out;
     return hip_status(fp4q::launch_quantize(cfg->format, cfg->grid, mode, cfg->rht16 != 0,
                                             bits_out != nullptr, ld == cols, p, stream),
                       "quantize launch");
@@ -243,6 +247,7 @@ fp4_status fp4_quantize_with_tensor_scale(const fp4_cfg* cfg, const void* x_bf16
     p.key1 = (uint32_t)(cfg->sr_seed >> 32);
     p.sr_offset = cfg->sr_offset;
     p.rht_seed = cfg->rht_seed;
+    p.stream_out = (uint32_t)cfg->stream_out;
     const int mode = cfg->rounding == FP4_SR ? fp4q::MODE_SR : fp4q::MODE_RTN;
     bool fused = false;
     const hipError_t e = fp4q::launch_quantize_with_scale(cfg->grid, mode, cfg->rht16 != 0, guide_bits_out != nullptr,
@@ -298,6 +303,7 @@ fp4_status fp4_quantize_grouped(const fp4_cfg* cfg, int guided, int n, const fp4
         p.key1 = (uint32_t)(cfg->sr_seed >> 32);
         p.sr_offset = cfg->sr_offset;
         p.rht_seed = cfg->rht_seed;
+        p.stream_out = (uint32_t)cfg->stream_out;
         if (d.ld == d.cols) gp.contig_mask |= 1u << t;
         wg += fp4q::quantize_chunks(cfg->format, mode, cfg->rht16 != 0, (uint32_t)ng);
         if (wg >= (1ull << 31)) return fail(FP4_ERR_SHAPE, "grouped call too large");
@@ -344,6 +350,7 @@ fp4_status fp4_fake_quantize(const fp4_cfg* cfg, int guided, const void* x_bf16,
     p.key1 = (uint32_t)(cfg->sr_seed >> 32);
     p.sr_offset = cfg->sr_offset;
     p.rht_seed = cfg->rht_seed;
+    p.stream_out = (uint32_t)cfg->stream_out;
     p.fq_out = static_cast<uint16_t*>(out_bf16);
     p.ld_out = ld_out;
     const int mode = guided ? fp4q::MODE_GUIDED : (cfg->rounding == FP4_SR ? fp4q::MODE_SR : fp4q::MODE_RTN);

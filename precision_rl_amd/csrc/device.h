@@ -27,8 +27,9 @@ typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Streaming memory access.  Inputs are read once: non-temporal loads keep them
-// from displacing reusable lines.  Outputs use non-temporal stores when
-// FP4Q_NT_STORES is set (default off: measured slower for the write-heavy kernels).
+// from displacing reusable lines.  Quantize outputs take non-temporal stores when
+// the caller says they are not read again soon (fp4_cfg.stream_out); the other
+// outputs when FP4Q_NT_STORES is set (default off).
 #ifndef FP4Q_NT_STORES
 #define FP4Q_NT_STORES 0
 #endif
@@ -43,20 +44,22 @@ __device__ __forceinline__ void load16_nt(const uint16_t* p, uint32_t w[4]) {
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
 }
 
+// nt: a non-temporal store (the caller's output is not read again soon).
 template <typename T>
-__device__ __forceinline__ void st_out(T* p, T v) {
-    if (FP4Q_NT_STORES) __builtin_nontemporal_store(v, p);
+__device__ __forceinline__ void st_out(T* p, T v, bool nt = FP4Q_NT_STORES) {
+    if (nt) __builtin_nontemporal_store(v, p);
     else *p = v;
 }
 
-__device__ __forceinline__ void st_out2(void* base, uint32_t idx, uint32_t a, uint32_t b) {
+__device__ __forceinline__ void st_out2(void* base, uint32_t idx, uint32_t a, uint32_t b, bool nt = FP4Q_NT_STORES) {
     v2u32 v = {a, b};
-    st_out(reinterpret_cast<v2u32*>(base) + idx, v);
+    st_out(reinterpret_cast<v2u32*>(base) + idx, v, nt);
 }
 
-__device__ __forceinline__ void st_out4(void* base, int64_t idx, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+__device__ __forceinline__ void st_out4(void* base, int64_t idx, uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                        bool nt = FP4Q_NT_STORES) {
     v4u32 v = {a, b, c, d};
-    st_out(reinterpret_cast<v4u32*>(base) + idx, v);
+    st_out(reinterpret_cast<v4u32*>(base) + idx, v, nt);
 }
 
 // Non-temporal 16-byte store, for an output several times larger than its

@@ -59,6 +59,7 @@ struct QuantParams {
     int64_t ld_out;             // its row stride in elements
     const uint8_t* rcodes;      // guide diagnostic: the rollout's full codes (guide bits are their LSBs)
     unsigned long long* counts; // guide diagnostic: elements, non-adjacent, mismatched (zeroed first)
+    uint32_t stream_out;        // 1: codes, scales, guide bits and fake-quantized values by non-temporal stores
 };
 
 // Up to kMaxGroup tensors sharing one configuration, quantized by one launch.

@@ -142,6 +142,7 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     // (C2 guided quantize, guides from HBM: 32.6 against 30.2 us without them).
     if constexpr (MODE == MODE_GUIDED) __builtin_amdgcn_sched_barrier(0);
     uint32_t n_skip = 0, n_nonadj = 0, n_mism = 0;   // OUT == 2
+    const bool nt = p.stream_out != 0;               // uniform: a scalar branch per store
 
     const uint32_t signs = RHT ? rht_sign_mask(p.rht_seed) : 0u;   // uniform: scalar unit
     float ts = 1.0f, denom = 1.0f, rden = 0.0f;
@@ -353,8 +354,9 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             to_bf16x16(dv, ok, o);
             if constexpr (RHT) {   // this lane's own group, as loaded
                 if (g < p.ngroups) {
-                    st_out4(p.fq_out + half_offset<false>(2u * g, p.gpr, p.ld_out), 0, o[0], o[1], o[2], o[3]);
-                    st_out4(p.fq_out + half_offset<false>(2u * g + 1u, p.gpr, p.ld_out), 0, o[4], o[5], o[6], o[7]);
+                    st_out4(p.fq_out + half_offset<false>(2u * g, p.gpr, p.ld_out), 0, o[0], o[1], o[2], o[3], nt);
+                    st_out4(p.fq_out + half_offset<false>(2u * g + 1u, p.gpr, p.ld_out), 0, o[4], o[5], o[6], o[7],
+                            nt);
                 }
             } else {
                 // back to half-groups (the same exchange, inverted): slot 2k takes this
@@ -363,19 +365,21 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
                 uint32_t oa[4], ob[4];
                 pair_exchange(o, o + 4, q, oa, ob);
                 const uint32_t ha = hg0 + 128u * k, hb = ha + 64u;
-                if (ha < nhg) st_out4(p.fq_out + half_offset<false>(ha, p.gpr, p.ld_out), 0, oa[0], oa[1], oa[2], oa[3]);
-                if (hb < nhg) st_out4(p.fq_out + half_offset<false>(hb, p.gpr, p.ld_out), 0, ob[0], ob[1], ob[2], ob[3]);
+                if (ha < nhg)
+                    st_out4(p.fq_out + half_offset<false>(ha, p.gpr, p.ld_out), 0, oa[0], oa[1], oa[2], oa[3], nt);
+                if (hb < nhg)
+                    st_out4(p.fq_out + half_offset<false>(hb, p.gpr, p.ld_out), 0, ob[0], ob[1], ob[2], ob[3], nt);
             }
         } else if (g < p.ngroups) {
-            st_out2(p.codes, g, c0, c1);
+            st_out2(p.codes, g, c0, c1, nt);
             if constexpr (FMT == 0) {
-                st_out(p.scales + g, (uint8_t)sc);
+                st_out(p.scales + g, (uint8_t)sc, nt);
             } else {
-                if ((g & 1u) == 0) st_out(p.scales + (g >> 1), (uint8_t)sc);
+                if ((g & 1u) == 0) st_out(p.scales + (g >> 1), (uint8_t)sc, nt);
             }
             if constexpr (EMIT) {
                 st_out(reinterpret_cast<uint16_t*>(p.bits_out) + g,
-                       (uint16_t)(gather_nibble_lsbs(c0) | (gather_nibble_lsbs(c1) << 8)));
+                       (uint16_t)(gather_nibble_lsbs(c0) | (gather_nibble_lsbs(c1) << 8)), nt);
             }
         }
     }

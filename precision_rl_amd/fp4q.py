@@ -37,7 +37,7 @@ class Fp4Error(RuntimeError):
 class _CCfg(C.Structure):
     _fields_ = [("format", C.c_int32), ("grid", C.c_int32), ("rounding", C.c_int32),
                 ("rht16", C.c_int32), ("sr_seed", C.c_uint64), ("sr_offset", C.c_uint64),
-                ("rht_seed", C.c_uint64)]
+                ("rht_seed", C.c_uint64), ("stream_out", C.c_int32)]
 
 
 @dataclass
@@ -50,6 +50,7 @@ class Fp4Config:
     sr_seed: int = 0
     sr_offset: int = 0
     rht_seed: int = 0
+    stream_out: bool = False    # outputs not read again soon: non-temporal stores
 
     @property
     def block(self) -> int:
@@ -58,7 +59,7 @@ class Fp4Config:
     def c(self) -> _CCfg:
         """The C struct of these fields (shared by calls with equal fields; the library only reads it)."""
         key = (self.format, self.grid, self.rounding, int(bool(self.rht16)), self.sr_seed, self.sr_offset,
-               self.rht_seed)
+               self.rht_seed, int(bool(self.stream_out)))
         cc = _CFG_CACHE.get(key)
         if cc is None:
             if len(_CFG_CACHE) >= 4096:      # e.g. an SR offset that advances every step

@@ -250,3 +250,17 @@ def test_gemm_quantize_nvfp4_host_side_errors(fq):
     assert g(p, p, p, p, 64, 64, 512, p, p, C.c_void_p(A + 1), p, None) == 3  # scales: two bytes per store
     assert g(p, p, p, p, 64, 64, 512, p, None, p, p, None) == 1               # no codes
     assert g(p, p, p, p, 0, 64, 512, p, None, None, None, None) == 0          # empty: no-op
+
+
+def test_cfg_layout_and_stream_out_values(fq):
+    # the binding's struct matches the header's 48-byte fp4_cfg, and stream_out takes 0 or 1 only
+    assert C.sizeof(fq._CCfg) == 48
+    assert fq._CCfg.stream_out.offset == 40
+    L = fq.lib()
+    A = 1 << 20
+    p = C.c_void_p(A)
+    for v, want in ((0, 0), (1, 0), (2, 1), (-1, 1)):
+        c = fq.Fp4Config(format=fq.MXFP4).c()
+        c2 = fq._CCfg(c.format, c.grid, c.rounding, c.rht16, c.sr_seed, c.sr_offset, c.rht_seed, v)
+        st = L.fp4_quantize(C.byref(c2), p, 0, 32, 32, None, p, p, None, None)   # empty: checks only
+        assert st == want, (v, st)
