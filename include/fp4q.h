@@ -172,12 +172,26 @@ fp4_status fp4_quantize(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, in
  *   launches         NULL, or receives 1 or 2, the number of launches enqueued.
  * The one-launch form needs all its workgroups running together: work that
  * keeps compute units busy for more than about a second while it runs (another
- * stream) makes the waiting workgroups give up, with NaN scales in their part of
- * the output. */
+ * stream) makes the waiting workgroups give up (fp4_set_wait_limit): s_t is then
+ * NaN, and the codes and scales of the blocks those workgroups quantize under
+ * it mean nothing. */
 fp4_status fp4_quantize_with_tensor_scale(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
                                           int64_t ld, float* tensor_scale_out, void* codes, void* scales,
                                           void* guide_bits_out, void* workspace, size_t workspace_bytes,
                                           int* launches, hipStream_t stream);
+
+/* The number of polls a workgroup that waits on the others of its launch (the
+ * gather of fp4_tensor_scale_ws and fp4_tensor_scale_noalloc, and both waits of
+ * the one-launch fp4_quantize_with_tensor_scale) makes before it gives up:
+ * FP4_WAIT_LIMIT_DEFAULT (2^20 polls, about a second) unless changed.  A wait
+ * that gives up writes s_t = NaN instead of hanging (and, in the one-launch
+ * quantize, the workgroup goes on with that s_t) and marks the launch in the
+ * workspace, so that its workgroups that start later store nothing; the
+ * workspace stays valid for the next call.  For tests of that path (0: every wait gives up at once) and
+ * for callers that bound their latency.  Applies to launches enqueued after the
+ * call, process-wide; returns the previous limit. */
+#define FP4_WAIT_LIMIT_DEFAULT 1048576u
+uint32_t fp4_set_wait_limit(uint32_t polls);
 
 /* Rollout-guided quantization [TRACE-JA "TRACEの仕組み"; TRACE-KO]: the
  * block scale (and NVFP4 tensor scale) come from the guide; each element is

@@ -128,6 +128,9 @@ static_assert(FP4_TENSOR_SCALE_WORKSPACE_BYTES == fp4q::kTsWorkspaceBytes, "work
 static_assert(sizeof(fp4_cfg) == 48, "fp4_cfg layout in the header");
 size_t fp4_tensor_scale_workspace_bytes(void) { return fp4q::kTsWorkspaceBytes; }
 
+static_assert(FP4_WAIT_LIMIT_DEFAULT == fp4q::kGatherPolls, "default wait limit in the header");
+uint32_t fp4_set_wait_limit(uint32_t polls) { return fp4q::set_wait_limit(polls); }
+
 fp4_status fp4_tensor_scale_ws(const fp4_cfg* cfg, const void* x_bf16, int64_t rows, int64_t cols,
                                int64_t ld, float* tensor_scale_out, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {

@@ -685,17 +685,52 @@ __device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
 }
 __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) { return (uint64_t)tag << 32 | v; }
 
-// Polls before a wait gives up: at least 2^20 loads, about a second.
+// The workspace's 64-bit state word: the epoch in its low half and, in its high
+// half, the mark of the last launch whose wait gave up (0 after a launch that
+// did not).  A launch's mark comes from the address of its dispatch packet,
+// which differs between queues and between launches on a queue until its ring
+// of packets wraps, graph replays included (never 0).
+__device__ __forceinline__ uint32_t launch_mark() {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(__builtin_amdgcn_dispatch_ptr());
+    return ((uint32_t)(a >> 6) & 0x7FFFFFFFu) + 1u;   // packets are 64 bytes
+}
+
+// A call as its workgroup sees it at the start: its tag (the epoch + 1) and
+// whether its own launch has already given up.  When a wait gives up, the
+// gathering workgroup advances the epoch without knowing that every workgroup
+// of the launch has read it; one that starts later would read the new epoch
+// and tag its word with the next call's tag, which that call's gather could
+// take for its own.  The mark in the same word tells such a workgroup that its
+// launch is over: it stores nothing.  (A later launch whose packet lands in the
+// marked slot before any call has succeeded on this workspace since is taken
+// for that launch: it gives s_t = NaN, never a wrong one, and the call after it
+// proceeds.)
+struct CallState {
+    uint32_t epoch, tag;
+    bool late;
+};
+__device__ __forceinline__ CallState call_state(const uint32_t* state) {
+    const uint64_t w = load_agent(reinterpret_cast<const uint64_t*>(state));
+    return CallState{(uint32_t)w, (uint32_t)w + 1u, (uint32_t)(w >> 32) == launch_mark()};
+}
+// The gathering workgroup's last store: the next epoch, and this launch's mark
+// if its wait gave up.
+__device__ __forceinline__ void end_call(uint32_t* state, uint32_t epoch, bool gave_up) {
+    store_agent(reinterpret_cast<uint64_t*>(state), (uint64_t)(gave_up ? launch_mark() : 0u) << 32 | (epoch + 1u));
+}
+
+// Polls before a wait gives up, by default: 2^20 loads, about a second.  The
+// launches take the limit as an argument (fp4_set_wait_limit).
 constexpr uint32_t kGatherPolls = 1u << 20;
 
 // This thread's share of the gather: the largest low half of words i = threadIdx.x
 // + THREADS k < n (at most MAXN words), once all of them carry `tag`; each round
 // loads them all at once.  Returns 0xFFFFFFFF if they are not all tagged within
-// kGatherPolls rounds (the maxima are finite float bits, never that value).
+// `polls` rounds (the maxima are finite float bits, never that value).
 template <uint32_t MAXN, uint32_t THREADS>
-__device__ __forceinline__ uint32_t gather_max(const uint64_t* words, uint32_t n, uint32_t tag) {
+__device__ __forceinline__ uint32_t gather_max(const uint64_t* words, uint32_t n, uint32_t tag, uint32_t polls) {
     constexpr uint32_t kPer = (MAXN + THREADS - 1) / THREADS;
-    for (uint32_t r = 0; r < kGatherPolls; ++r) {
+    for (uint32_t r = 0; r < polls; ++r) {
         uint64_t v[kPer];
         #pragma unroll
         for (uint32_t k = 0; k < kPer; ++k) {

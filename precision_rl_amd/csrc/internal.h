@@ -129,6 +129,10 @@ static_assert(kTsPub + kTsLine * kTsPubCopies <= kTsGather && kTsMaxWorkgroups <
               "tensor-scale workspace layout");
 constexpr int kMaxDevices = 64;                         // devices whose per-device state the library keeps
 
+// Polls a workgroup waiting on others makes before it gives up (fp4_set_wait_limit).
+uint32_t wait_limit();
+uint32_t set_wait_limit(uint32_t polls);   // returns the previous limit
+
 struct EncodeParams {
     const float* v;
     const uint8_t* aux;

@@ -1,5 +1,6 @@
 // misc.hip -- tensor scale, dequantization, guide pack/unpack, standalone RHT16
 // and the element-encode entry, for gfx950.
+#include <atomic>
 #include <mutex>
 
 #include "device.h"
@@ -102,7 +103,8 @@ __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
 // Each workgroup stores its maximum, tagged with this call's epoch, in a
 // workspace word of its own (device.h, cross-workgroup reduction) and ends;
 // workgroup 0 then waits until every word carries the tag, takes their maximum,
-// writes s_t and advances the epoch.  Only workgroup 0 waits, on workgroups that
+// writes s_t and advances the epoch (call_state, end_call: a wait that gives up
+// marks the launch, s_t is NaN).  Only workgroup 0 waits, on workgroups that
 // never wait themselves, so the grid need not be resident all at once.  Distinct
 // words take no atomics: through shared counters, a hundred and more same-
 // address atomics per word serialize at about 13 ns each, and agent-scope
@@ -110,24 +112,29 @@ __global__ __launch_bounds__(kThreads) void k_amax(const AmaxParams p) {
 // more than the whole pass over a 16 MiB tensor.
 
 template <bool RHT, bool CONTIG>
-__global__ __launch_bounds__(kThreads) void k_tensor_scale_1(const AmaxParams p, uint32_t* ws, float gmax448) {
+__global__ __launch_bounds__(kThreads) void k_tensor_scale_1(const AmaxParams p, uint32_t* ws, float gmax448,
+                                                             uint32_t polls) {
     __shared__ uint32_t red[kThreads / 64];
-    __shared__ uint32_t tag_sh;
+    __shared__ CallState cs_sh;
     const uint32_t b = blockIdx.x, nwg = gridDim.x;
-    const uint32_t epoch = threadIdx.x == 0 ? load_agent(ws + kTsEpoch) : 0u;
+    const CallState cs = threadIdx.x == 0 ? call_state(ws + kTsEpoch) : CallState{};
     const uint32_t m = wg_max_t0<kThreads / 64>(amax_thread<RHT, CONTIG, kAmaxU>(p), red);
     uint64_t* const words = reinterpret_cast<uint64_t*>(ws + kTsGather);
     if (threadIdx.x == 0) {
-        store_agent(words + b, tagged(epoch + 1u, m));
-        tag_sh = epoch + 1u;
+        if (!cs.late) store_agent(words + b, tagged(cs.tag, m));
+        cs_sh = cs;
     }
     if (b != 0) return;
-    __syncthreads();   // tag_sh; also orders the first use of red before the second
-    const uint32_t tag = tag_sh;
-    const uint32_t g = wg_max_t0<kThreads / 64>(gather_max<kTsMaxWorkgroups, kThreads>(words, nwg, tag), red);
+    __syncthreads();   // cs_sh; also orders the first use of red before the second
+    const CallState c = cs_sh;
+    if (c.late) {      // this launch gave up before: s_t is NaN, the state stays
+        if (threadIdx.x == 0) *p.acc = __builtin_nanf("");
+        return;
+    }
+    const uint32_t g = wg_max_t0<kThreads / 64>(gather_max<kTsMaxWorkgroups, kThreads>(words, nwg, c.tag, polls), red);
     if (threadIdx.x == 0) {
         *p.acc = g == 0xFFFFFFFFu ? __builtin_nanf("") : ts_from_amax(g, gmax448);
-        store_agent(ws + kTsEpoch, tag);
+        end_call(ws + kTsEpoch, c.epoch, g == 0xFFFFFFFFu);
     }
 }
 
@@ -406,12 +413,21 @@ hipError_t launch_tensor_scale_1(int grid, bool rht, bool contig, const AmaxPara
     const uint32_t per_wg = kThreads * kAmaxU;
     uint32_t blocks = (p.ngroups + per_wg - 1) / per_wg;
     blocks = blocks < 1u ? 1u : (blocks > kTsMaxWorkgroups ? kTsMaxWorkgroups : blocks);
-#define FP4Q_TS1(R, C) hipLaunchKernelGGL((k_tensor_scale_1<R, C>), dim3(blocks), dim3(kThreads), 0, s, p, ws, g448)
+    const uint32_t polls = wait_limit();
+#define FP4Q_TS1(R, C) \
+    hipLaunchKernelGGL((k_tensor_scale_1<R, C>), dim3(blocks), dim3(kThreads), 0, s, p, ws, g448, polls)
     if (rht) { if (contig) FP4Q_TS1(true, true); else FP4Q_TS1(true, false); }
     else { if (contig) FP4Q_TS1(false, true); else FP4Q_TS1(false, false); }
 #undef FP4Q_TS1
     return hipGetLastError();
 }
+
+namespace {
+std::atomic<uint32_t> g_wait_limit{kGatherPolls};
+}  // namespace
+
+uint32_t wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+uint32_t set_wait_limit(uint32_t polls) { return g_wait_limit.exchange(polls, std::memory_order_relaxed); }
 
 // Workspace of fp4_tensor_scale_noalloc, for callers that cannot allocate: one
 // array per device, zero when the code object is loaded and left zero by every

@@ -588,22 +588,22 @@ hipError_t launch_grouped_m(int mode, bool rht, bool emit, const GroupedQuantPar
 // workgroups' loads spread), which the others wait for; then each quantizes its
 // chunk from its registers.  This needs every workgroup resident at once: the
 // host launches it only when the device holds the whole grid, and each wait is
-// bounded (kGatherPolls polls, about a second) so that a workgroup kept from
+// bounded (wait_limit() polls, by default about a second) so that a workgroup kept from
 // seeing s_t gives up with a NaN scale instead of spinning forever.
 template <int GRID, int MODE, bool EMIT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_quantize_with_scale(const QuantParams p, float* ts_out, uint32_t* ws,
-                                                                  float gmax448) {
+                                                                  float gmax448, uint32_t polls) {
     constexpr int kH = 4;
     constexpr uint32_t kChunkGroups = kThreads * (kH / 2);
     __shared__ float tab[128];
     __shared__ uint32_t red[kThreads / 64];
-    __shared__ uint32_t tag_sh;
+    __shared__ CallState cs_sh;
     __shared__ float ts_sh;
     const uint32_t b = blockIdx.x, nwg = gridDim.x;
     const uint32_t lane = threadIdx.x & 63u;
-    // the epoch word, read while the chunk loads (any time before this
-    // workgroup's own word is stored will do)
-    const uint32_t epoch = threadIdx.x == 0 ? load_agent(ws + kTsEpoch) : 0u;
+    // the workspace's state word, read while the chunk loads (any time before
+    // this workgroup's own word is stored will do)
+    const CallState cs = threadIdx.x == 0 ? call_state(ws + kTsEpoch) : CallState{};
     // the half-groups quantize_chunk would read for chunk b (past the end, the
     // last one again), kept in registers for it
     const uint32_t hg0 = b * (2u * kChunkGroups) + (threadIdx.x >> 6) * (64u * kH) + lane;
@@ -627,32 +627,37 @@ __global__ __launch_bounds__(kThreads) void k_quantize_with_scale(const QuantPar
     m = wg_max_t0<kThreads / 64>(m, red);
     uint64_t* const words = reinterpret_cast<uint64_t*>(ws + kTsGather);
     if (threadIdx.x == 0) {
-        store_agent(words + b, tagged(epoch + 1u, m));
-        tag_sh = epoch + 1u;
+        if (!cs.late) store_agent(words + b, tagged(cs.tag, m));
+        cs_sh = cs;
     }
     if (b == 0) {
-        __syncthreads();   // tag_sh; also orders the first use of red before the second
-        const uint32_t tag = tag_sh;
-        const uint32_t g = wg_max_t0<kThreads / 64>(gather_max<kTsGatherMax, kThreads>(words, nwg, tag), red);
-        if (threadIdx.x == 0) {
-            const float ts = g == 0xFFFFFFFFu ? __builtin_nanf("") : ts_from_amax(g, gmax448);
-            *ts_out = ts;
-            #pragma unroll
-            for (uint32_t c = 0; c < kTsPubCopies; ++c)
-                store_agent(reinterpret_cast<uint64_t*>(ws + kTsPub + kTsLine * c), tagged(tag, __float_as_uint(ts)));
-            store_agent(ws + kTsEpoch, tag);
-            ts_sh = ts;
+        __syncthreads();   // cs_sh; also orders the first use of red before the second
+        const CallState c = cs_sh;
+        if (c.late) {      // this launch gave up before: s_t is NaN, the state stays
+            if (threadIdx.x == 0) *ts_out = ts_sh = __builtin_nanf("");
+        } else {
+            const uint32_t g =
+                wg_max_t0<kThreads / 64>(gather_max<kTsGatherMax, kThreads>(words, nwg, c.tag, polls), red);
+            if (threadIdx.x == 0) {
+                const float ts = g == 0xFFFFFFFFu ? __builtin_nanf("") : ts_from_amax(g, gmax448);
+                *ts_out = ts;
+                #pragma unroll
+                for (uint32_t k = 0; k < kTsPubCopies; ++k)
+                    store_agent(reinterpret_cast<uint64_t*>(ws + kTsPub + kTsLine * k),
+                                tagged(c.tag, __float_as_uint(ts)));
+                end_call(ws + kTsEpoch, c.epoch, g == 0xFFFFFFFFu);
+                ts_sh = ts;
+            }
         }
     } else if (threadIdx.x == 0) {
         const uint64_t* pub = reinterpret_cast<const uint64_t*>(ws + kTsPub + kTsLine * (b % kTsPubCopies));
-        const uint32_t tag = tag_sh;
         uint64_t v = 0;
-        for (uint32_t n = 0; n < kGatherPolls; ++n) {
+        for (uint32_t n = 0; !cs.late && n < polls; ++n) {
             v = load_agent(pub);
-            if ((uint32_t)(v >> 32) == tag) break;
+            if ((uint32_t)(v >> 32) == cs.tag) break;
             __builtin_amdgcn_s_sleep(4);
         }
-        ts_sh = (uint32_t)(v >> 32) == tag ? __uint_as_float((uint32_t)v) : __builtin_nanf("");
+        ts_sh = !cs.late && (uint32_t)(v >> 32) == cs.tag ? __uint_as_float((uint32_t)v) : __builtin_nanf("");
     }
     __syncthreads();
     QuantParams q = p;
@@ -688,7 +693,7 @@ hipError_t launch_with_scale_t(const QuantParams& p, float* ts_out, uint32_t* ws
     if (blocks > 0 && (int64_t)blocks <= cap && blocks <= kTsGatherMax) {
         *fused = true;
         hipLaunchKernelGGL((k_quantize_with_scale<GRID, MODE, EMIT, CONTIG>), dim3(blocks), dim3(kThreads), 0, s, p,
-                           ts_out, ws, g448);
+                           ts_out, ws, g448, wait_limit());
         return hipGetLastError();
     }
     *fused = false;

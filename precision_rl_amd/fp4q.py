@@ -88,7 +88,7 @@ EXPORTS = ("fp4_tensor_scale", "fp4_tensor_scale_ws", "fp4_tensor_scale_workspac
            "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_grouped", "fp4_gemm_mxfp4_quantize", "fp4_gemm_mxfp4_quantize_nvfp4",
            "fp4_rht16",
            "fp4_encode_values", "fp4_encode_scales", "fp4_stream_copy", "fp4_codes_bytes", "fp4_scales_bytes", "fp4_guide_bytes",
-           "fp4_status_str", "fp4_last_error")
+           "fp4_set_wait_limit", "fp4_status_str", "fp4_last_error")
 
 
 class _CGuide(C.Structure):
@@ -140,6 +140,8 @@ def lib():
         f = getattr(L, name)
         f.argtypes = args
         f.restype = C.c_int
+    L.fp4_set_wait_limit.argtypes = [C.c_uint32]
+    L.fp4_set_wait_limit.restype = C.c_uint32
     L.fp4_tensor_scale_workspace_bytes.argtypes = []
     L.fp4_tensor_scale_workspace_bytes.restype = C.c_size_t
     for name in ("fp4_codes_bytes",):

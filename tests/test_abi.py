@@ -264,3 +264,13 @@ def test_cfg_layout_and_stream_out_values(fq):
         c2 = fq._CCfg(c.format, c.grid, c.rounding, c.rht16, c.sr_seed, c.sr_offset, c.rht_seed, v)
         st = L.fp4_quantize(C.byref(c2), p, 0, 32, 32, None, p, p, None, None)   # empty: checks only
         assert st == want, (v, st)
+
+
+def test_wait_limit_setter(fq):
+    L = fq.lib()
+    prev = L.fp4_set_wait_limit(7)
+    try:
+        assert prev == 1 << 20
+        assert L.fp4_set_wait_limit(0) == 7
+    finally:
+        assert L.fp4_set_wait_limit(prev) == 0

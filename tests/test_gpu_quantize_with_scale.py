@@ -18,7 +18,7 @@ import torch
 
 import oracle as O
 from precision_rl_amd import workloads as W
-from ts_workspace import chunk_max_bits, check_after, epoch, fused_grid, ts_grid
+from ts_workspace import chunk_max_bits, check_after, epoch, fused_grid, mark, ts_grid
 
 pytestmark = pytest.mark.gpu
 
@@ -174,3 +174,24 @@ def test_graph_replays(fq, ws):
         # eager work between the replays
         fq.fp4_quantize_with_tensor_scale(xs[rep], cfg, ws, emit=True)
         torch.cuda.synchronize()
+
+
+def test_waits_give_up_with_nan_and_workspace_recovers(fq, ws):
+    # a wait limit of 0: workgroup 0 publishes s_t = NaN at once and every other workgroup stops
+    # waiting at once, so the launch ends with s_t NaN; the next call with the default limit is exact
+    L = fq.lib()
+    cfg = fq.Fp4Config()
+    # 256 workgroups, one launch; every chunk maximum of this tensor is far above any value of the
+    # next one, so a word left over from this launch and taken by the next call's gather would show
+    xf = np.random.default_rng(78).standard_normal((256, CHUNK)).astype(np.float32) * 4096.0
+    e0 = epoch(ws)
+    prev = L.fp4_set_wait_limit(0)
+    try:
+        out = fq.fp4_quantize_with_tensor_scale(dev(W.f32_to_bf16_rne(xf)), cfg, ws, emit=True)
+        torch.cuda.synchronize()
+    finally:
+        L.fp4_set_wait_limit(prev)
+    assert fq.last_launches == 1
+    assert np.isnan(host(out[0])[0])
+    assert epoch(ws) == e0 + 1 and mark(ws) != 0
+    check(fq, ws, W.c1_x(256, CHUNK, seed=79), cfg, emit=True, launches=1)

@@ -15,7 +15,7 @@ import torch
 
 import oracle as O
 from precision_rl_amd import workloads as W
-from ts_workspace import chunk_max_bits, check_after, epoch, ts_grid
+from ts_workspace import chunk_max_bits, check_after, epoch, mark, ts_grid
 
 pytestmark = pytest.mark.gpu
 
@@ -139,3 +139,29 @@ def test_one_launch_tensor_scale_in_a_graph(fq, ws):
         fq.fp4_tensor_scale_ws(xs[rep], cfg, ws, out=outs[rep])
         assert bits(outs[rep]) == want[rep]
         check_after(ws, e0, ts_grid(2048 * 2048 // 16))
+
+
+def test_wait_gives_up_with_nan_and_workspace_recovers(fq, ws):
+    # a wait limit of 0 makes workgroup 0's gather give up at once: s_t is NaN, the epoch still
+    # advances with the launch's give-up mark beside it (workgroups of that launch that start later
+    # store nothing), and the next call with the default limit is exact again and clears the mark
+    L = fq.lib()
+    cfg = fq.Fp4Config()
+    # 512 workgroups; every chunk maximum of this tensor is far above any value of the next one, so
+    # a word left over from this launch and taken by the next call's gather would change its s_t
+    xf = np.random.default_rng(77).standard_normal((512, 16384)).astype(np.float32) * 4096.0
+    x = dev(W.f32_to_bf16_rne(xf))
+    e0 = epoch(ws)
+    prev = L.fp4_set_wait_limit(0)
+    try:
+        got = fq.fp4_tensor_scale_ws(x, cfg, ws)
+        torch.cuda.synchronize()
+    finally:
+        L.fp4_set_wait_limit(prev)
+    assert np.isnan(got.cpu().numpy()[0])
+    assert epoch(ws) == e0 + 1 and mark(ws) != 0
+    e1 = epoch(ws)
+    xh2 = W.c1_x(512, 16384, seed=79)
+    want2 = np.float32(O.tensor_scale(O.Cfg(), xh2)).view(np.uint32)
+    assert bits(fq.fp4_tensor_scale_ws(dev(xh2), cfg, ws)) == want2
+    check_after(ws, e1, ts_grid(512 * 16384 // 16), amax_bits=int(chunk_max_bits(xh2, xh2.size).max()))

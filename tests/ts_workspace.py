@@ -1,15 +1,17 @@
 """Reading the tensor-scale workspace after a call (test helper).
 
-Layout, in 32-bit words: the epoch at word 0; sixteen copies of the one-launch
-fused form's published word (tag << 32 | bits of s_t) from word 64, a 256-byte
-line apart; one 64-bit word per workgroup from word 2048 (tag << 32 | bits of
-the workgroup's largest finite |y|).  Every completed reduction advances the
-epoch by one and tags each of its workgroups' words with the new epoch.
+Layout, in 32-bit words: a 64-bit state word at word 0 (the epoch in word 0, in
+word 1 the mark of the last launch whose wait gave up, 0 after a launch that did
+not); sixteen copies of the one-launch fused form's published word (tag << 32 |
+bits of s_t) from word 64, a 256-byte line apart; one 64-bit word per workgroup
+from word 2048 (tag << 32 | bits of the workgroup's largest finite |y|).  Every
+completed reduction advances the epoch by one and tags each of its workgroups'
+words with the new epoch.
 """
 import numpy as np
 import torch
 
-EPOCH, PUB, PUB_COPIES, LINE, GATHER = 0, 64, 16, 64, 2048
+EPOCH, MARK, PUB, PUB_COPIES, LINE, GATHER = 0, 1, 64, 16, 64, 2048
 TS_GROUPS_PER_WG, TS_MAX_WG = 1024, 1024      # one-launch tensor scale: groups per workgroup, grid cap
 FUSED_GROUPS_PER_WG = 512                     # fused tensor scale + quantize
 
@@ -21,6 +23,10 @@ def words(ws):
 
 def epoch(ws):
     return int(words(ws)[EPOCH])
+
+
+def mark(ws):
+    return int(words(ws)[MARK])
 
 
 def ts_grid(ngroups):
@@ -38,6 +44,7 @@ def check_after(ws, epoch_before, nwg, ts_bits=None, wg_max_bits=None, amax_bits
     w = words(ws)
     e = (epoch_before + 1) & 0xFFFFFFFF
     assert int(w[EPOCH]) == e, (int(w[EPOCH]), e)
+    assert int(w[MARK]) == 0, "a completed call leaves no give-up mark"
     g = w[GATHER:GATHER + 2 * nwg].reshape(nwg, 2)        # little endian: (low, high)
     assert (g[:, 1] == e).all(), "a workgroup word without this call's tag"
     if ts_bits is not None:
