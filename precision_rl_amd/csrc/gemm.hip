@@ -213,9 +213,13 @@ struct LdsTile {
     static constexpr int RA = 64 * WM, RB = 64 * WN;      // rows of A and B per tile
     static constexpr int ROWS = RA + RB;                  // stacked: A rows, then B rows
     static constexpr int CODE_BYTES = ROWS * 128;         // one stage of codes
+    // scale loads with nothing to load (not the first stage of a chunk, or
+    // past the last row block) still issue, with an empty range, into a sink
+    // that every such load of every wave shares
+    static constexpr int SINK_BYTES = 1024;
     // Stages whose scales one load per row brings: 4 (32 bytes of a row), or 2
     // where double-buffered chunks of 4 would not fit in LDS beside the codes.
-    static constexpr int CHUNK = 2 * CODE_BYTES + 2 * ROWS * 32 + 4 * ((ROWS / 32 + 3) / 4) * 1024 <= 160 * 1024 ? 4 : 2;
+    static constexpr int CHUNK = 2 * CODE_BYTES + 2 * ROWS * 32 + SINK_BYTES <= 160 * 1024 ? 4 : 2;
     static constexpr int SPITCH = 8 * CHUNK;              // bytes of a row's scales in one chunk
     static constexpr int SROWS = 1024 / SPITCH;           // rows per wave load of scales (64 lanes x 16 bytes)
     static constexpr int SCALE_BYTES = ROWS * SPITCH;     // one chunk of scales
@@ -224,9 +228,15 @@ struct LdsTile {
     static constexpr int NSCALE = ROWS / SROWS;           // wave loads of scales per chunk
     static constexpr int NSQ = (NSCALE + 3) / 4;          // scale loads every wave issues per stage
     static constexpr int BATCH = NCW + NSQ;               // loads every wave issues per stage
-    // scale loads with nothing to load (not the first stage of a chunk, or
-    // past the last row block) still issue, with an empty range, into a sink
-    static constexpr int SINK_BYTES = 4 * NSQ * 1024;
+    // The scale loads issued with the code loads of stage t are those of stage
+    // t + LEAD.  Chunks of 2 stages (LEAD 1): one stage ahead of the codes.
+    // Their chunk buffer is free by then, the codes' buffer is not.
+    static constexpr int LEAD = CHUNK == 2 ? 1 : 0;
+    // Loads of this wave that may still be in flight once stage s + 1 is in:
+    // those issued after its codes and scales.
+    static constexpr int WAIT = LEAD * NSQ;
+    // ... once stage 0 is in, after the loads of stages 0 and 1
+    static constexpr int WAIT0 = BATCH + LEAD * NSQ;
     static constexpr int LDS_BYTES = 2 * CODE_BYTES + 2 * SCALE_BYTES + SINK_BYTES;
     static_assert(NCODE % 4 == 0, "code loads split evenly over the 4 waves");
     static_assert(RA % SROWS == 0, "a wave load of scales lies within A or within B");
@@ -273,15 +283,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int 
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 
-// This wave's loads of stage t, all issued whatever t, so that the K loop has
-// no branches: code load q (stacked rows 8 i .. 8 i + 7, i = wave + 4 q) into
-// code buffer t % 2, and scale load q (stacked rows 32 j .. 32 j + 31,
-// j = wave + 4 q) into scale buffer (t / 4) % 2 when t starts a chunk.  Loads
-// with nothing to load (t past the last stage, a scale load off a chunk start,
-// j past the last row block) get an empty range: they move no data and write
-// zeros into LDS the kernel no longer reads (scale loads into the sink).
-// PART selects which of the loads to issue: 0 all, 1 the scale loads and the
-// first half of the code loads, 2 the second half of the code loads.
+// This wave's code loads of stage t, then its scale loads for stage t + LEAD,
+// all issued whatever t, so that the K loop has no branches: code load q
+// (stacked rows 8 i .. 8 i + 7, i = wave + 4 q) into code buffer t % 2, and
+// scale load q (stacked rows 32 j .. 32 j + 31, j = wave + 4 q) into scale
+// buffer (u / CHUNK) % 2, u = t + LEAD, when u starts a chunk.  Loads with
+// nothing to load (a stage past the last, a scale load off a chunk start, j
+// past the last row block) get an empty range: they move no data and write
+// zeros into LDS the kernel no longer reads (scale loads into the sink).  The
+// scale loads go last in their batch.  With chunks of 2 stages they go out one
+// stage ahead, and the barrier before which the next stage must be in lets
+// them still be in flight, so they have two stages to land.  Each touches one
+// cache line per row for 16 bytes of it: loaded with the codes of their own
+// stage, they made every other stage of 256 x 256 tiles about 30% longer.
+// (With chunks of 4 the same lead measured 2% slower on 256 x 192 tiles.)
+// PART selects which loads to issue: 0 all, 1 the first half of the code
+// loads, 2 the second half and the scale loads.
+template <int WM, int WN>
+__device__ __forceinline__ void issue_scales(uint8_t* smem, const Bases& bs, const int* soff, int wave, int t,
+                                             int steps) {
+    using T = LdsTile<WM, WN>;
+    const bool chunk = t < steps && (t & (T::CHUNK - 1)) == 0;
+    uint8_t* sb = smem + 2 * T::CODE_BYTES + ((t / T::CHUNK) & 1) * T::SCALE_BYTES;
+    uint8_t* sink = smem + 2 * T::CODE_BYTES + 2 * T::SCALE_BYTES;
+    #pragma unroll
+    for (int q = 0; q < T::NSQ; ++q) {
+        const int j = wave + 4 * q;
+        const bool real = chunk && j < T::NSCALE;
+        const __amdgpu_buffer_rsrc_t r =
+            j * T::SROWS < T::RA ? rsrc(bs.as, real ? bs.nas : 0) : rsrc(bs.bs, real ? bs.nbs : 0);
+        const int so = soff[q];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(real ? sb + j * 1024 : sink), 16, so, t * 8, 0, 0);
+    }
+}
+
 template <int WM, int WN, int PART = 0>
 __device__ __forceinline__ void issue_stage(uint8_t* smem, const Bases& bs, const int* voff, const int* soff,
                                             int wave, int t, int steps) {
@@ -298,19 +333,8 @@ __device__ __forceinline__ void issue_stage(uint8_t* smem, const Bases& bs, cons
         __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 2 * WM ? ra : rb, (lds_ptr_t)(cb + (wave + 4 * q) * 1024), 16,
                                                  vo, t * 128, 0, 0);
     }
-    if constexpr (PART == 2) return;
-    const bool chunk = live && (t & (T::CHUNK - 1)) == 0;
-    uint8_t* sb = smem + 2 * T::CODE_BYTES + ((t / T::CHUNK) & 1) * T::SCALE_BYTES;
-    uint8_t* sink = smem + 2 * T::CODE_BYTES + 2 * T::SCALE_BYTES;
-    #pragma unroll
-    for (int q = 0; q < T::NSQ; ++q) {
-        const int j = wave + 4 * q;
-        const bool real = chunk && j < T::NSCALE;
-        const __amdgpu_buffer_rsrc_t r =
-            j * T::SROWS < T::RA ? rsrc(bs.as, real ? bs.nas : 0) : rsrc(bs.bs, real ? bs.nbs : 0);
-        const int so = soff[q];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)((real ? sb : sink) + j * 1024), 16, so, t * 8, 0, 0);
-    }
+    if constexpr (PART == 1) return;
+    issue_scales<WM, WN>(smem, bs, soff, wave, t + T::LEAD, steps);
 }
 
 // Operands of K slice KS of stage st for this wave: A rows of 32-row blocks
@@ -599,10 +623,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint
     v2u32 sa[WM], sb[WN], na[WM], nb[WN];   // scale words of this stage and the next
     const uint8_t* sbase = smem + 2 * T::CODE_BYTES;
 
+    if constexpr (T::LEAD) issue_scales<WM, WN>(smem, bs, soff, wave, 0, steps);
     issue_stage<WM, WN>(smem, bs, voff, soff, wave, 0, steps);
     issue_stage<WM, WN>(smem, bs, voff, soff, wave, 1, steps);
-    // stage 0 is in once only stage 1's loads remain (loads complete in order)
-    __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(T::BATCH));
+    // stage 0 is in once only the loads issued after its codes and scales remain
+    // (loads complete in order)
+    __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(T::WAIT0));
     barrier_only();
     read_scales<WM, WN>(sbase, 0, scA, scB, sa, sb);
     if constexpr (WM * WN >= 16) {
@@ -624,7 +650,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint
             interleave<3 * WM * WN, WM + WN, 0, WM * WN>();
             // as below: stage s read and stage s + 1 in, for every wave after the barrier
             __builtin_amdgcn_s_waitcnt(FP4Q_LGKMCNT0);
-            __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
+            __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(T::WAIT));
             barrier_only();
             read_scales<WM, WN>(sbase, s + 1, scA, scB, na_, nb_);
             read_ops<WM, WN, 0>(smem, s + 1, roff, rowA0, rowB0, xa, xb);
@@ -658,10 +684,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint32_t tm, uint
             read_ops<WM, WN, 3>(smem, s, roff, rowA0, rowB0, a3, b3);
             mfmas<WM, WN, 1>(acc, a1, b1, ca, cb, kc);
             interleave<2 * WM * WN, 2 * (WM + WN), 0>();
-            // this wave's reads of stage s and its loads of stage s + 1 are done; after
-            // the barrier every wave's are, so stage s + 2 may load into stage s's buffers
+            // this wave's reads of stage s and its loads of stage s + 1 are done; after the
+            // barrier every wave's are, so stage s + 2 may load into stage s's buffers
             __builtin_amdgcn_s_waitcnt(FP4Q_LGKMCNT0);
-            __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(0));
+            __builtin_amdgcn_s_waitcnt(FP4Q_VMCNT(T::WAIT));
             barrier_only();
             read_scales<WM, WN>(sbase, s + 1, scA, scB, na_, nb_);
             read_ops<WM, WN, 0>(smem, s + 1, roff, rowA0, rowB0, a0, b0);
