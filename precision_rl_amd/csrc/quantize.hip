@@ -36,21 +36,30 @@ namespace {
 
 // Half-groups per lane (load slots); even, since slots are transposed in pairs.
 // MXFP4 stochastic rounding without the RHT runs fastest with two (twice the
-// workgroups, so more of them in flight); every other kernel with four
-// (measured; NVFP4 SR and the RHT kernels lose with two).
+// workgroups, so more of them in flight); every other kernel is built with four,
+// and single-tensor launches take two where that measured faster (launch_t).
 template <int FMT, int MODE, bool RHT>
 constexpr int halves_per_lane() { return FMT == 1 && MODE == MODE_SR && !RHT ? 2 : 4; }
 // Groups per workgroup.
 template <int FMT, int MODE, bool RHT>
 constexpr uint32_t chunk_groups() { return kThreads * (halves_per_lane<FMT, MODE, RHT>() / 2); }
-// Single-tensor launches without the RHT take two slots instead of four for RTN
-// and guided rounding (twice the workgroups, so more loads in flight across the
-// chip: 16384 x 4096 MXFP4 RTN 29.5 against 30.0 us, guided 31.0 against 31.6,
-// NVFP4 RTN 29.7 against 30.1, guided 32.2 against 32.5; on 4096 x 2048 NVFP4
-// RTN 5.35 against 5.78 us, guided 5.82 against 6.56), and for SR when they
-// would have fewer workgroups than this (8 per compute unit); NVFP4 SR on large
-// tensors and the grouped launches stay faster with four (C4's grouped rollout
-// RTN: 36.3 against 38.1 us).
+// Single-tensor launches take two slots instead of four (twice the workgroups,
+// so more loads in flight across the chip) for:
+//  - RTN and guided rounding without the RHT (16384 x 4096 MXFP4 RTN 29.5
+//    against 30.0 us, guided 31.0 against 31.6, NVFP4 RTN 29.7 against 30.1,
+//    guided 32.2 against 32.5; on 4096 x 2048 NVFP4 RTN 5.35 against 5.78 us,
+//    guided 5.82 against 6.56);
+//  - RTN and guided rounding with the RHT, whose slots then go through the DPP
+//    pair exchange instead of the LDS transpose (65536 x 8192: MXFP4 RTN 225.5
+//    against 233 us, NVFP4 238 against 243.5, uniform 235.5 against 244.5);
+//  - uniform SR without the RHT (65536 x 8192: 235 against 245.5 us);
+//  - SR without the RHT when four slots would give fewer workgroups than this
+//    (8 per compute unit).
+// SR with the RHT is bound by VALU issue, and the pair exchange and the
+// reciprocal table shared by half as many groups make it slower on two slots
+// (C5, uniform + RHT + SR: 259-264 against 240-242 us); NVFP4 E2M1 SR on large
+// tensors measured the same either way and the grouped launches are faster with
+// four (C4's grouped rollout RTN: 36.3 against 38.1 us).
 constexpr uint32_t kSmallLaunchBlocks = 2048;
 
 // Number of nonzero nibbles of w.
@@ -98,12 +107,13 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     // half-group of slot s: hg0 + 64 s; group owned after transposing slots 2k, 2k+1: gk(k)
     const uint32_t hg0 = wg * (2u * kChunkGroups) + (threadIdx.x >> 6) * (64u * kH) + lane;
     const uint32_t nhg = 2u * p.ngroups;
-    // With the RHT the slots go through LDS (see below) and lane l then owns
-    // groups W + l and W + 64 + l of its wave's 128 groups W ..; otherwise the
-    // DPP pair exchange gives lane 2m groups G + m and lane 2m+1 groups G + 32 + m
-    // for each pair of slots.
+    // With the RHT on four slots the slots go through LDS (see below) and lane l
+    // then owns groups W + l and W + 64 + l of its wave's 128 groups W ..;
+    // otherwise (no RHT, or two slots) the DPP pair exchange gives lane 2m groups
+    // G + m and lane 2m+1 groups G + 32 + m for each pair of slots.
+    constexpr bool kLdsT = RHT && kH == 4;
     auto gk = [&](int k) {
-        return RHT ? ((hg0 - lane) >> 1) + 64u * k + lane : (hg0 + 128u * k + 64u * q) >> 1;
+        return kLdsT ? ((hg0 - lane) >> 1) + 64u * k + lane : (hg0 + 128u * k + 64u * q) >> 1;
     };
 
     // Lanes past the end load the last half-group instead (in bounds, no
@@ -156,8 +166,9 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         rden = 1.0f / denom;
         rden_ok = denom >= 0x1p-125f && denom <= 0x1p125f;
     }
-    if constexpr (RHT) {
-        // The RHT kernels are bound by arithmetic: the slots go through LDS,
+    if constexpr (kLdsT) {
+        // The RHT kernels on four slots (SR, and the grouped, fused, fake and
+        // diagnostic launches) are bound by arithmetic: the slots go through LDS,
         // which costs no VALU instructions, instead of the DPP exchange.  Half-
         // group h of the wave goes to (h & 1) * 2048 + (h >> 1) * 16, so lane l
         // then reads groups l and 64 + l as two 16-byte pieces each; the writes
@@ -194,7 +205,7 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     for (int k = 0; k < kG; ++k) {
         const uint32_t g = gk(k);
         uint32_t gw[8];
-        if constexpr (RHT) {
+        if constexpr (kLdsT) {
             #pragma unroll
             for (int j = 0; j < 4; ++j) { gw[j] = w[2 * k][j]; gw[4 + j] = w[2 * k + 1][j]; }
         } else {
@@ -220,8 +231,8 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
             amax_key = amax_bits16(gw) << 16;
         }
         // an MXFP4 block is groups 2b and 2b+1: in lanes l and l ^ 1 after the LDS
-        // transpose (RHT), in lanes l and l ^ 2 after the pair exchange
-        if constexpr (FMT == 1) amax_key = max(amax_key, RHT ? dpp_swap1(amax_key) : dpp_swap2(amax_key));
+        // transpose, in lanes l and l ^ 2 after the pair exchange
+        if constexpr (FMT == 1) amax_key = max(amax_key, kLdsT ? dpp_swap1(amax_key) : dpp_swap2(amax_key));
         bool finite = amax_key < 0x7F800000u;
 
         uint32_t sc;
@@ -509,8 +520,9 @@ hipError_t launch_t(const QuantParams& p, hipStream_t s) {
     constexpr int kH = halves_per_lane<FMT, MODE, RHT>();
     constexpr uint32_t kChunkGroups = chunk_groups<FMT, MODE, RHT>();
     const uint32_t blocks = (p.ngroups + kChunkGroups - 1) / kChunkGroups;
-    if constexpr (kH == 4 && !RHT) {   // the RHT kernels' LDS transpose is written for four slots
-        if (MODE != MODE_SR || blocks < kSmallLaunchBlocks) {
+    if constexpr (kH == 4) {
+        const bool two = MODE != MODE_SR || (!RHT && (GRID == 1 || blocks < kSmallLaunchBlocks));
+        if (two) {
             const uint32_t b2 = (p.ngroups + kThreads - 1) / kThreads;
             hipLaunchKernelGGL((k_quantize<FMT, GRID, MODE, RHT, EMIT, CONTIG, 2>), dim3(b2), dim3(kThreads),
                                0, s, p);

@@ -208,11 +208,11 @@ def test_c5_uniform_rht16_sr_65536x8192(fq):
 @pytest.mark.parametrize("grid", [0, 1])
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_both_slot_counts_at_the_small_launch_threshold(fq, fmt, grid, rows, pad):
-    # A single-tensor SR launch below 2048 workgroups of four slots takes two slots
-    # per lane (RTN and guided always take two): 8191 x 2048 (NVFP4: 2047 workgroups
-    # of four) launches two, 8192 x 2048 launches four, and 8193 x 2048 with padded
-    # rows launches four with a ragged last chunk.  All equal the oracle in every
-    # mode and on both grids, on the whole tensor.
+    # A single-tensor E2M1 SR launch below 2048 workgroups of four slots takes two
+    # slots per lane (RTN, guided and uniform SR always take two): 8191 x 2048
+    # (NVFP4: 2047 workgroups of four) launches two, 8192 x 2048 launches four, and
+    # 8193 x 2048 with padded rows launches four with a ragged last chunk.  All
+    # equal the oracle in every mode and on both grids, on the whole tensor.
     cols = 2048
     say("slot threshold", fmt, grid, rows, cols, pad)
     xh = W.c1_x(rows, cols, seed=21)
@@ -235,3 +235,36 @@ def test_both_slot_counts_at_the_small_launch_threshold(fq, fmt, grid, rows, pad
     sc, ss = fq.fp4_quantize(x, scfg, ts_t)
     o_sc, o_ss = O.quantize(O.Cfg(format=fmt, grid=grid, sr_seed=5, sr_offset=9), O.SR, xh, ts)
     assert (sc.cpu().numpy() == o_sc).all() and (ss.cpu().numpy() == o_ss).all()
+
+
+@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_rht_on_two_and_four_slots_whole_tensor(fq, fmt, grid):
+    # With the RHT, RTN and guided rounding take two slots per lane (the DPP pair
+    # exchange) and SR four (the LDS transpose), at every size: 8193 x 2048 with
+    # padded rows (a ragged last chunk) equals the oracle on the whole tensor in
+    # all three modes, with emission.
+    rows, cols, pad = 8193, 2048, 24
+    say("rht slots", fmt, grid, rows, cols, pad)
+    xh = W.c1_x(rows, cols, seed=23)
+    xrh = W.c1_rollout(rows, cols, seed=23)
+    cfg = fq.Fp4Config(format=fmt, grid=grid, rht16=True, rht_seed=11)
+    oc = O.Cfg(format=fmt, grid=grid, rht16=True, rht_seed=11)
+    x, xr = dev(xh, pad), dev(xrh, pad)
+    ts_t = fq.fp4_tensor_scale(xr, cfg) if fmt == 0 else None
+    ts = O.tensor_scale(oc, xrh) if fmt == 0 else 1.0
+    if fmt == 0:
+        assert f32bits(ts_t.item()) == f32bits(ts)
+    rc, rs, rb = fq.fp4_quantize(xr, cfg, ts_t, emit=True)
+    o_rc, o_rs, o_rb = O.quantize(oc, O.RTN, xrh, ts, emit=True)
+    assert (rc.cpu().numpy() == o_rc).all() and (rs.cpu().numpy() == o_rs).all()
+    assert (rb.cpu().numpy() == o_rb).all()
+    gc, gs = fq.fp4_quantize_guided(x, cfg, rb, rs, ts_t)
+    o_gc, o_gs = O.quantize(oc, O.GUIDED, xh, ts, guide_bits=o_rb, guide_scales=o_rs)
+    assert (gc.cpu().numpy() == o_gc).all() and (gs.cpu().numpy() == o_gs).all()
+    scfg = fq.Fp4Config(format=fmt, grid=grid, rounding=fq.SR, rht16=True, rht_seed=11, sr_seed=5, sr_offset=9)
+    sc, ss = fq.fp4_quantize(x, scfg, ts_t)
+    o_sc, o_ss = O.quantize(O.Cfg(format=fmt, grid=grid, rht16=True, rht_seed=11, sr_seed=5, sr_offset=9), O.SR, xh,
+                            ts)
+    assert (sc.cpu().numpy() == o_sc).all() and (ss.cpu().numpy() == o_ss).all()
+

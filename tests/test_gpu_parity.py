@@ -114,6 +114,8 @@ CASES = [
     (1, 0, 0, True, "student"),
     (1, 0, 1, True, "student"),
     (0, 0, 1, True, "outlier"),
+    (0, 1, 0, True, "outlier"),
+    (0, 1, 1, False, "outlier"),
 ]
 
 
