@@ -55,11 +55,12 @@ constexpr uint32_t chunk_groups() { return kThreads * (halves_per_lane<FMT, MODE
 //  - uniform SR without the RHT (65536 x 8192: 235 against 245.5 us);
 //  - SR without the RHT when four slots would give fewer workgroups than this
 //    (8 per compute unit).
-// SR with the RHT is bound by VALU issue, and the pair exchange and the
-// reciprocal table shared by half as many groups make it slower on two slots
-// (C5, uniform + RHT + SR: 259-264 against 240-242 us); NVFP4 E2M1 SR on large
-// tensors measured the same either way and the grouped launches are faster with
-// four (C4's grouped rollout RTN: 36.3 against 38.1 us).
+// SR with the RHT is bound by VALU issue as much as by memory, and the pair
+// exchange and the reciprocal table shared by half as many groups make it
+// slower on two slots (C5, uniform + RHT + SR: 259-264 against 240-242 us); it
+// takes eight on large tensors instead (below).  NVFP4 E2M1 SR on large tensors
+// measured the same either way and the grouped launches are faster with four
+// (C4's grouped rollout RTN: 36.3 against 38.1 us).
 constexpr uint32_t kSmallLaunchBlocks = 2048;
 
 // Number of nonzero nibbles of w.
@@ -107,11 +108,11 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
     // half-group of slot s: hg0 + 64 s; group owned after transposing slots 2k, 2k+1: gk(k)
     const uint32_t hg0 = wg * (2u * kChunkGroups) + (threadIdx.x >> 6) * (64u * kH) + lane;
     const uint32_t nhg = 2u * p.ngroups;
-    // With the RHT on four slots the slots go through LDS (see below) and lane l
-    // then owns groups W + l and W + 64 + l of its wave's 128 groups W ..;
+    // With the RHT on four or eight slots the slots go through LDS (see below)
+    // and lane l then owns groups W + l + 64 k of its wave's groups W ..;
     // otherwise (no RHT, or two slots) the DPP pair exchange gives lane 2m groups
     // G + m and lane 2m+1 groups G + 32 + m for each pair of slots.
-    constexpr bool kLdsT = RHT && kH == 4;
+    constexpr bool kLdsT = RHT && kH % 4 == 0;
     auto gk = [&](int k) {
         return kLdsT ? ((hg0 - lane) >> 1) + 64u * k + lane : (hg0 + 128u * k + 64u * q) >> 1;
     };
@@ -167,34 +168,41 @@ __device__ __forceinline__ void quantize_chunk(const QuantParams& p, uint32_t wg
         rden_ok = denom >= 0x1p-125f && denom <= 0x1p125f;
     }
     if constexpr (kLdsT) {
-        // The RHT kernels on four slots (SR, and the grouped, fused, fake and
-        // diagnostic launches) are bound by arithmetic: the slots go through LDS,
-        // which costs no VALU instructions, instead of the DPP exchange.  Half-
-        // group h of the wave goes to (h & 1) * 2048 + (h >> 1) * 16, so lane l
-        // then reads groups l and 64 + l as two 16-byte pieces each; the writes
-        // and the reads both touch consecutive 16-byte slots.  The wave's own
-        // LDS operations complete in order, so it needs no workgroup barrier.
-        static_assert(kH == 4, "the LDS transpose assumes four slots");
+        // The RHT kernels on four or eight slots (SR, and the grouped, fused,
+        // fake and diagnostic launches) are bound by arithmetic: the slots go
+        // through LDS, which costs no VALU instructions, instead of the DPP
+        // exchange, four at a time.  In round r, half-group h of the wave's
+        // slots 4 r .. 4 r + 3 goes to (h & 1) * 2048 + (h >> 1) * 16, so lane l
+        // then reads groups l and 64 + l of the round as two 16-byte pieces
+        // each; the writes and the reads both touch consecutive 16-byte slots.
+        // The wave's own LDS operations complete in order, so it needs no
+        // workgroup barrier.
+        static_assert(kH % 4 == 0, "the LDS transpose takes rounds of four slots");
         char* base = reinterpret_cast<char*>(rht_transpose_lds() + (threadIdx.x >> 6) * 256);
         char* wp = base + (lane & 1u) * 2048u + (lane >> 1) * 16u;
-        // the diagnostic kernel calls this once per chunk: the previous chunk's
-        // reads come before these writes
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        #pragma unroll
-        for (int s = 0; s < kH; ++s)
-            *reinterpret_cast<v4u32*>(wp + 512 * s) = (v4u32){w[s][0], w[s][1], w[s][2], w[s][3]};
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         char* rp = base + lane * 16u;
         #pragma unroll
-        for (int k = 0; k < kG; ++k) {
-            const v4u32 a = *reinterpret_cast<const v4u32*>(rp + 1024 * k);
-            const v4u32 b = *reinterpret_cast<const v4u32*>(rp + 2048 + 1024 * k);
-            w[2 * k][0] = a.x; w[2 * k][1] = a.y; w[2 * k][2] = a.z; w[2 * k][3] = a.w;
-            w[2 * k + 1][0] = b.x; w[2 * k + 1][1] = b.y; w[2 * k + 1][2] = b.z; w[2 * k + 1][3] = b.w;
+        for (int r = 0; r < kH / 4; ++r) {
+            // the previous round's reads (and, in the diagnostic kernel, which calls
+            // this once per chunk, the previous chunk's) come before these writes
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            #pragma unroll
+            for (int s = 0; s < 4; ++s)
+                *reinterpret_cast<v4u32*>(wp + 512 * s) =
+                    (v4u32){w[4 * r + s][0], w[4 * r + s][1], w[4 * r + s][2], w[4 * r + s][3]};
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            #pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const v4u32 a = *reinterpret_cast<const v4u32*>(rp + 1024 * k);
+                const v4u32 b = *reinterpret_cast<const v4u32*>(rp + 2048 + 1024 * k);
+                const int s0 = 4 * r + 2 * k;   // group 2 r + k of the lane
+                w[s0][0] = a.x; w[s0][1] = a.y; w[s0][2] = a.z; w[s0][3] = a.w;
+                w[s0 + 1][0] = b.x; w[s0 + 1][1] = b.y; w[s0 + 1][2] = b.z; w[s0 + 1][3] = b.w;
+            }
         }
     }
     // MXFP4 RTN and guided without the RHT convert straight from the bf16 bits;
@@ -520,6 +528,17 @@ hipError_t launch_t(const QuantParams& p, hipStream_t s) {
     constexpr int kH = halves_per_lane<FMT, MODE, RHT>();
     constexpr uint32_t kChunkGroups = chunk_groups<FMT, MODE, RHT>();
     const uint32_t blocks = (p.ngroups + kChunkGroups - 1) / kChunkGroups;
+    if constexpr (RHT && MODE == MODE_SR) {
+        // eight slots: four groups per lane share the wave's fixed work (load
+        // addresses, the reciprocal table), where that still gives this many
+        // workgroups (C5: 237.0 against 240.5 us)
+        const uint32_t b8 = (p.ngroups + 4 * kThreads - 1) / (4 * kThreads);
+        if (b8 >= kSmallLaunchBlocks) {
+            hipLaunchKernelGGL((k_quantize<FMT, GRID, MODE, RHT, EMIT, CONTIG, 8>), dim3(b8), dim3(kThreads), 0, s,
+                               p);
+            return hipGetLastError();
+        }
+    }
     if constexpr (kH == 4) {
         const bool two = MODE != MODE_SR || (!RHT && (GRID == 1 || blocks < kSmallLaunchBlocks));
         if (two) {

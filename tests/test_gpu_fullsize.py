@@ -268,3 +268,28 @@ def test_rht_on_two_and_four_slots_whole_tensor(fq, fmt, grid):
                             ts)
     assert (sc.cpu().numpy() == o_sc).all() and (ss.cpu().numpy() == o_ss).all()
 
+
+@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_rht_sr_on_eight_slots_whole_tensor(fq, fmt, grid):
+    # A single-tensor SR launch with the RHT takes eight slots per lane once that
+    # still gives 2048 workgroups: 16385 x 2048 (2097280 groups, 2049 workgroups of
+    # 1024 groups, the last one ragged) with padded rows equals the oracle on the
+    # whole tensor, with and without emitted guide bits.
+    rows, cols, pad = 16385, 2048, 24
+    say("rht sr eight slots", fmt, grid, rows, cols, pad)
+    xh = W.c1_x(rows, cols, seed=29)
+    cfg = fq.Fp4Config(format=fmt, grid=grid, rounding=fq.SR, rht16=True, rht_seed=13, sr_seed=17, sr_offset=3)
+    oc = O.Cfg(format=fmt, grid=grid, rht16=True, rht_seed=13, sr_seed=17, sr_offset=3)
+    x = dev(xh, pad)
+    ts_t = fq.fp4_tensor_scale(x, cfg) if fmt == 0 else None
+    ts = O.tensor_scale(oc, xh) if fmt == 0 else 1.0
+    if fmt == 0:
+        assert f32bits(ts_t.item()) == f32bits(ts)
+    o_c, o_s, o_b = O.quantize(oc, O.SR, xh, ts, emit=True)
+    c, sc, b = fq.fp4_quantize(x, cfg, ts_t, emit=True)
+    assert (c.cpu().numpy() == o_c).all() and (sc.cpu().numpy() == o_s).all()
+    assert (b.cpu().numpy() == o_b).all()
+    c2, sc2 = fq.fp4_quantize(x, cfg, ts_t)
+    assert (c2.cpu().numpy() == o_c).all() and (sc2.cpu().numpy() == o_s).all()
+
