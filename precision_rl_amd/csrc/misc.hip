@@ -214,7 +214,15 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) 
 #ifndef FP4Q_GUIDE_SLOTS
 #define FP4Q_GUIDE_SLOTS 2
 #endif
-constexpr int kGuideSlots = FP4Q_GUIDE_SLOTS;
+constexpr int kGuideSlots = FP4Q_GUIDE_SLOTS;   // guide_unpack
+// guide_pack: four units per lane for one tensor where that still gives
+// kPackWideBlocks workgroups (16384 x 4096 MXFP4: 8.6 against 9.0 us on two,
+// 9.2-9.5 on eight), else two (in graphs, 4096 x 1536 NVFP4: 2.9 against 3.15
+// us on four, 8192 x 4096 NVFP4 6.1 against 6.35); eight in the grouped launch
+// (the nine tensors of an MoE layer: 12.1 against 12.7 us on four, 13.3 on two)
+constexpr int kPackSlotsWide = 4;
+constexpr uint32_t kPackWideBlocks = 2048;
+constexpr int kPackSlotsGrouped = 8;
 
 // Workgroup wg of guide_pack over one tensor.  Every load of the workgroup is
 // issued before any of its data is used: lanes past the last whole unit read
@@ -223,23 +231,22 @@ constexpr int kGuideSlots = FP4Q_GUIDE_SLOTS;
 // scale loads, two memory round trips per wave.)  An odd NVFP4 group count
 // leaves a last unit of one group (8 bytes of codes), which the lane that owns
 // it handles on its own.
-template <int FMT>
+template <int FMT, int S>
 __device__ __forceinline__ void guide_pack_wg(const GuideParams& p, uint32_t wg) {
     const uint32_t nfull = p.ngroups >> 1;              // units of two groups
-    const uint32_t u0 = wg * (kThreads * kGuideSlots) + (threadIdx.x >> 6) * (64u * kGuideSlots) +
-                        (threadIdx.x & 63u);
+    const uint32_t u0 = wg * (kThreads * S) + (threadIdx.x >> 6) * (64u * S) + (threadIdx.x & 63u);
     if (nfull > 0) {
-        v4u32 c[kGuideSlots];
-        uint32_t sc[kGuideSlots];
+        v4u32 c[S];
+        uint32_t sc[S];
         #pragma unroll
-        for (int s = 0; s < kGuideSlots; ++s) {
+        for (int s = 0; s < S; ++s) {
             const uint32_t u = min(u0 + 64u * s, nfull - 1u);
             c[s] = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p.in) + u);
             if constexpr (FMT == 0) sc[s] = p.scales_in[2 * u] | ((uint32_t)p.scales_in[2 * u + 1] << 8);
             else sc[s] = p.scales_in[u];
         }
         #pragma unroll
-        for (int s = 0; s < kGuideSlots; ++s) {
+        for (int s = 0; s < S; ++s) {
             const uint32_t u = u0 + 64u * s;
             if (u >= nfull) continue;
             const uint32_t bits = gather_nibble_lsbs(c[s].x) | (gather_nibble_lsbs(c[s].y) << 8) |
@@ -255,7 +262,7 @@ __device__ __forceinline__ void guide_pack_wg(const GuideParams& p, uint32_t wg)
     }
     if (p.ngroups & 1u) {   // NVFP4 only: the last unit is group 2 nfull alone
         #pragma unroll
-        for (int s = 0; s < kGuideSlots; ++s) {
+        for (int s = 0; s < S; ++s) {
             if (u0 + 64u * s != nfull) continue;
             const v2u32 h = reinterpret_cast<const v2u32*>(p.in)[2 * nfull];
             const uint32_t bits = gather_nibble_lsbs(h.x) | (gather_nibble_lsbs(h.y) << 8);
@@ -265,9 +272,9 @@ __device__ __forceinline__ void guide_pack_wg(const GuideParams& p, uint32_t wg)
     }
 }
 
-template <int FMT>
+template <int FMT, int S>
 __global__ __launch_bounds__(kThreads) void k_guide_pack(const GuideParams p) {
-    guide_pack_wg<FMT>(p, blockIdx.x);
+    guide_pack_wg<FMT, S>(p, blockIdx.x);
 }
 
 // Up to kMaxGroup tensors in one launch: tensor t takes workgroups
@@ -275,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_guide_pack(const GuideParams p) {
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_guide_pack_grouped(const GroupedGuideParams gp) {
     const uint32_t t = group_of<kMaxGroup>(gp.wg_start, gp.n, blockIdx.x);
-    guide_pack_wg<FMT>(gp.t[t], blockIdx.x - gp.wg_start[t]);
+    guide_pack_wg<FMT, kPackSlotsGrouped>(gp.t[t], blockIdx.x - gp.wg_start[t]);
 }
 
 __device__ __forceinline__ uint32_t bits4_to_bytes(uint32_t b) {
@@ -480,15 +487,22 @@ hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantP
 
 hipError_t launch_guide_pack(int format, const GuideParams& p, hipStream_t s) {
     const uint32_t units = (p.ngroups + 1u) >> 1;
-    const dim3 b((units + kThreads * kGuideSlots - 1) / (kThreads * kGuideSlots)), t(kThreads);
-    if (format == 0) hipLaunchKernelGGL(k_guide_pack<0>, b, t, 0, s, p);
-    else hipLaunchKernelGGL(k_guide_pack<1>, b, t, 0, s, p);
+    const uint32_t b4 = (units + kThreads * kPackSlotsWide - 1) / (kThreads * kPackSlotsWide);
+    const dim3 t(kThreads);
+    if (b4 >= kPackWideBlocks) {
+        if (format == 0) hipLaunchKernelGGL((k_guide_pack<0, kPackSlotsWide>), dim3(b4), t, 0, s, p);
+        else hipLaunchKernelGGL((k_guide_pack<1, kPackSlotsWide>), dim3(b4), t, 0, s, p);
+    } else {
+        const dim3 b((units + kThreads * 2 - 1) / (kThreads * 2));
+        if (format == 0) hipLaunchKernelGGL((k_guide_pack<0, 2>), b, t, 0, s, p);
+        else hipLaunchKernelGGL((k_guide_pack<1, 2>), b, t, 0, s, p);
+    }
     return hipGetLastError();
 }
 
 static uint32_t guide_pack_wgs(uint32_t ngroups) {
     const uint32_t units = (ngroups + 1u) >> 1;
-    return (units + kThreads * kGuideSlots - 1) / (kThreads * kGuideSlots);
+    return (units + kThreads * kPackSlotsGrouped - 1) / (kThreads * kPackSlotsGrouped);
 }
 
 hipError_t launch_guide_pack_grouped(int format, GroupedGuideParams gp, hipStream_t s) {

@@ -293,3 +293,26 @@ def test_rht_sr_on_eight_slots_whole_tensor(fq, fmt, grid):
     c2, sc2 = fq.fp4_quantize(x, cfg, ts_t)
     assert (c2.cpu().numpy() == o_c).all() and (sc2.cpu().numpy() == o_s).all()
 
+
+
+@pytest.mark.parametrize("fmt,rows,cols", [
+    (1, 16384, 4096),     # four units per lane, 2048 workgroups (C2)
+    (1, 16383, 4096),     # four units per lane, the last workgroup partly filled
+    (1, 16376, 4096),     # 2047 workgroups of four units: two units per lane instead
+    (0, 1397419, 48),     # NVFP4, odd group count: four per lane, the last workgroup one half unit
+    (0, 1397077, 48),     # NVFP4, odd group count, just below the four-unit threshold
+])
+def test_guide_pack_both_slot_counts_whole_tensor(fq, fmt, rows, cols):
+    # guide_pack takes four units per lane where that still gives 2048 workgroups, else two:
+    # both against the oracle on the whole tensor, on either side of the threshold
+    t0 = time.time()
+    B = 32 if fmt else 16
+    n = rows * cols
+    rng = np.random.default_rng(rows)
+    codes = rng.integers(0, 256, n // 2, dtype=np.uint8)
+    scales = rng.integers(0, 256, n // B, dtype=np.uint8)
+    cfg = fq.Fp4Config(format=fmt)
+    gb, gs = fq.guide_pack(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), cfg, rows, cols)
+    o_gb, o_gs = O.guide_pack(O.Cfg(format=fmt), codes, scales, rows, cols)
+    assert (gb.cpu().numpy() == o_gb).all() and (gs.cpu().numpy() == o_gs).all()
+    say(f"guide_pack {rows}x{cols} fmt {fmt}: whole tensor bit-exact ({time.time() - t0:.1f} s)")
