@@ -457,10 +457,17 @@ def cpu_baseline(args, W, oracle_mod, h, threads=1, runs=3):
 # ---------------------------------------------------------------- other workloads
 def mismatch_counts(fq, x, cfg, rcodes, rscales, ts):
     """Full-code guided diagnostic of x against a rollout's codes: how often the 1-bit guide
-    cannot reproduce the rollout's codeword (non-adjacent) or its code (mismatched)."""
+    cannot reproduce the rollout's codeword (non-adjacent) or its code (mismatched), and how often
+    the trainer's own RTN quantization of x (its own tensor scale for NVFP4) differs from the
+    rollout's code: the training/rollout mismatch that guided rounding removes."""
     n, nonadj, mism = (int(v) for v in fq.fp4_guide_mismatch(x, cfg, rcodes, rscales, ts).cpu())
+    own_ts = fq.fp4_tensor_scale(x, cfg) if cfg.format == fq.NVFP4 else None
+    own, _ = fq.fp4_quantize(x, cfg, own_ts)
+    d = own ^ rcodes
+    rtn = int(((d & 0xF) != 0).sum().item() + ((d >> 4) != 0).sum().item())
     return {"elements": n, "non_adjacent": nonadj, "mismatched": mism,
-            "non_adjacent_frac": nonadj / max(n, 1), "mismatched_frac": mism / max(n, 1)}
+            "non_adjacent_frac": nonadj / max(n, 1), "mismatched_frac": mism / max(n, 1),
+            "rtn_differs": rtn, "rtn_differs_frac": rtn / max(n, 1)}
 
 
 def _u8(torch):
@@ -615,6 +622,11 @@ def wl_c4(args, fq, torch, W, ceiling):
         ok = ok and all(torch.equal(a, b) for a, b in zip(tr[t], fq.fp4_quantize_guided(xs[t], cfg, *guides[t], tss[t])))
         ok = ok and all(torch.equal(a, b) for a, b in zip(pk[t], fq.guide_pack(roll[t][0], roll[t][1], cfg, rr, cc)))
     r = {"grouped_matches_single": bool(ok)}
+    # the trainer's tensors against the rollout's codes, summed over the layer's nine tensors
+    mm = [mismatch_counts(fq, xs[t], cfg, roll[t][0], roll[t][1], tss[t]) for t in range(len(shapes))]
+    tot = {k: sum(m[k] for m in mm) for k in ("elements", "non_adjacent", "mismatched", "rtn_differs")}
+    r["guide_mismatch_counts"] = dict(tot, **{k + "_frac": tot[k] / tot["elements"]
+                                              for k in ("non_adjacent", "mismatched", "rtn_differs")})
     # timing: the layer's inputs in two copies (2 x 160 MiB per side) and outputs in four sets, so that the
     # Infinity Cache serves neither the reads nor the writes
     R = 4
