@@ -555,6 +555,18 @@ def wl_c1(args, fq, torch, W, ceiling):
                         gr, ts_rtn_check)
     r["tensor_scale_and_rtn_one_launch_graph"] = dict(report(ms, 2.5625 * n, n, ceiling), replays_match_eager=ok,
                                                       launches=fused_launches)
+    # supplementary: sixteen tensors of this shape (the 32 input copies in two sets) quantized by one
+    # grouped launch, which pays the launch and ramp once for 16 x 16 MiB; checked against single-tensor
+    # launches first.  Not the single-tensor workload above, whose figures stand as measured.
+    G = 16
+    gouts = [[(oc[(G * k + t) % R], os_[(G * k + t) % R]) for t in range(G)] for k in range(R // G)]
+    fq.fp4_quantize_grouped(xs[:G], cfg, tss[:G], outs=gouts[0])
+    gok = all(torch.equal(a, b) for t in range(G) for a, b in zip(gouts[0][t], fq.fp4_quantize(xs[t], cfg, tss[t])))
+    ms = back_to_back(torch, lambda i: fq.fp4_quantize_grouped(xs[G * (i % 2):G * (i % 2) + G], cfg,
+                                                               tss[G * (i % 2):G * (i % 2) + G],
+                                                               outs=gouts[i % (R // G)]), it)
+    r["quantize_rtn_16_tensors_grouped"] = dict(report(ms, 2.5625 * n * G, n * G, ceiling), tensors=G,
+                                                grouped_matches_single=bool(gok))
     return r
 
 
