@@ -275,10 +275,12 @@ def test_grouped_experts_vs_oracle(fq, K):
                       f"grouped expert {e} {dtype}")
 
 
-def test_grouped_large_tiles_sampled(fq):
-    # 8 experts x 1024 tokens x [1536, 512] weights: 256 tiles of 256 x 192 in one launch
-    E, M, N, K = 8, 1024, 1536, 512
-    say(f"gemm grouped large E={E} M={M} N={N} K={K}")
+@pytest.mark.parametrize("K,dtype", [(512, torch.float32), (4096, torch.bfloat16)])
+def test_grouped_large_tiles_sampled(fq, K, dtype):
+    # 8 experts x 1024 tokens x [1536, K] weights: 256 tiles of 256 x 192 in one launch; K = 4096 with
+    # bf16 out is the grouped product bench.py times (16 stages, so the K loop body runs)
+    E, M, N = 8, 1024, 1536
+    say(f"gemm grouped large E={E} M={M} N={N} K={K} {dtype}")
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).ravel()).cuda()
     rng = np.random.default_rng(12)
     prods, host = [], []
@@ -287,9 +289,10 @@ def test_grouped_large_tiles_sampled(fq):
         b, bsc = W.mx_operand(N, K, seed=130 + e, stream=0)
         prods.append((dev(a), dev(asc), dev(b), dev(bsc), M, N, K))
         host.append((a, asc, b, bsc))
-    outs = fq.fp4_gemm_mxfp4_grouped(prods, dtype=torch.float32)
+    outs = fq.fp4_gemm_mxfp4_grouped(prods, dtype=dtype)
     torch.cuda.synchronize()
     for e, (a, asc, b, bsc) in enumerate(host):
-        rows = np.sort(rng.choice(M, 16, replace=False))
+        rows = np.sort(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 14, replace=False)]))
         ref, mag = O.gemm_mx(a[rows], asc[rows], b, bsc, len(rows), N, K)
-        check(outs[e].cpu().numpy()[rows].astype(np.float64), ref, mag, K, False, f"grouped large expert {e}")
+        got = outs[e].float().cpu().numpy()[rows].astype(np.float64)
+        check(got, ref, mag, K, dtype == torch.bfloat16, f"grouped large expert {e} K={K}")
