@@ -6,7 +6,9 @@ form it times them:
 * one deep guidance-cache layer (8 expert weights 4096x1536 + activations
   8192x4096): the grouped rollout quantize with guide emission, the grouped
   trainer guided quantize, and the grouped guide_pack of the nine tensors;
-* the guided fake quantization of the MoE activations (16384x4096, MXFP4).
+* the guided fake quantization of the MoE activations (16384x4096, MXFP4);
+* sixteen copies of the NVFP4 activation (4096x2048, rows rotated as bench.py
+  rotates them) quantized by one grouped launch under the rollout's tensor scale.
 
 Sampled rows (first, last and random ones) of every output are compared bit for
 bit with the oracle.  The oracle's inputs come from the input generators and
@@ -151,3 +153,29 @@ def test_c2_guided_fake_quantize(fq):
         want = O.dequantize(oc, ogc, ogsc, 1.0, 1, cols, out_bf16=True)
         assert (out[r].view(torch.int16).cpu().numpy() == want.view(np.int16)).all(), r
     say(f"C2 guided fake quantization: {len(idx)} rows bit-exact ({time.time() - t0:.1f} s)")
+
+
+def test_c1_sixteen_tensors_grouped(fq):
+    rows, cols = W.c1_shape()
+    t0 = time.time()
+    G = 16
+    cfg, oc = fq.Fp4Config(), O.Cfg()
+    xh, xrh = W.c1_x(rows, cols), W.c1_rollout(rows, cols)
+    x0 = dev(xh)
+    xs = [torch.roll(x0, s * 61, 0) for s in range(G)]      # as bench.py rotates its copies
+    # rotating rows leaves the maximum alone: one tensor scale, the rollout's, for every copy
+    ts = fq.fp4_tensor_scale(dev(xrh), cfg)
+    o_ts = O.tensor_scale(oc, xrh)
+    assert f32bits(ts.item()) == f32bits(o_ts)
+    n = rows * cols
+    outs = [(poisoned(n // 2), poisoned(n // 16)) for _ in range(G)]
+    fq.fp4_quantize_grouped(xs, cfg, [ts] * G, outs=outs)       # as bench.py times it
+    torch.cuda.synchronize()
+    for t in range(G):
+        c, sc = outs[t]
+        for r in sample_rows(rows, 8, seed=60 + t):
+            src = (r - 61 * t) % rows
+            oc_r, os_r = O.quantize(oc, O.RTN, xh[src:src + 1], o_ts, row0=r)
+            assert (rows_of(c, r, cols // 2) == oc_r).all(), ("codes", t, r)
+            assert (rows_of(sc, r, cols // 16) == os_r).all(), ("scales", t, r)
+    say(f"C1 x 16 grouped: {G} tensors, sampled rows bit-exact ({time.time() - t0:.1f} s)")
