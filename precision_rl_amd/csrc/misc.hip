@@ -155,25 +155,30 @@ void launch_amax(bool rht, bool contig, uint32_t blocks, const AmaxParams& p, hi
 
 // ---------------------------------------------------------------- dequantize
 // Work unit: 16 bytes of output, i.e. 8 elements to bf16 (one dword of codes)
-// or 4 elements to fp32 (16 bits of codes).  In each of its kDqSlots slots the
+// or 4 elements to fp32 (16 bits of codes).  In each of its slots the
 // 64 lanes of a wave handle 64 consecutive units, so every store instruction
 // of a wave writes 1 KiB contiguously (when ld_out == cols).
 
-#ifndef FP4Q_DQ_SLOTS
-#define FP4Q_DQ_SLOTS 2
-#endif
-constexpr int kDqSlots = FP4Q_DQ_SLOTS;
+// Two slots; bf16 output on four where that still gives kDqWideBlocks
+// workgroups (2^27 elements and up).  Back to back, with codes from HBM, four
+// are faster (131072 x 8 x 128 NVFP4 to bf16: 110.6 against 115.8 us; 16384 x
+// 4096 MXFP4: 29.0 against 29.4), but in the five-kernel step, where the codes
+// come from the Infinity Cache just after the guided quantize wrote them, the
+// 16384 x 4096 dequantize took 27.6 against 26.9 us; eight slots were slower in
+// both (113.5, and 30.5 back to back).
+constexpr int kDqSlots = 2;
+constexpr int kDqSlotsWide = 4;
+constexpr uint64_t kDqWideBlocks = 16384;
 
-template <int FMT, int GRID, bool BF16>
+template <int FMT, int GRID, bool BF16, int S>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) {
     constexpr uint32_t E = BF16 ? 8u : 4u;                 // elements per unit
     const uint64_t nunits = (uint64_t)p.ngroups * (16u / E);
-    const uint64_t u0 = (uint64_t)blockIdx.x * (kThreads * kDqSlots) + (threadIdx.x >> 6) * (64u * kDqSlots) +
-                        (threadIdx.x & 63u);
+    const uint64_t u0 = (uint64_t)blockIdx.x * (kThreads * S) + (threadIdx.x >> 6) * (64u * S) + (threadIdx.x & 63u);
     const float ts = FMT == 0 ? *p.ts : 1.0f;
-    uint32_t c[kDqSlots], sc[kDqSlots];
+    uint32_t c[S], sc[S];
     #pragma unroll
-    for (int s = 0; s < kDqSlots; ++s) {
+    for (int s = 0; s < S; ++s) {
         const uint64_t u = u0 + 64u * s;
         c[s] = sc[s] = 0u;
         if (u < nunits) {
@@ -183,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const DequantParams p) 
         }
     }
     #pragma unroll
-    for (int s = 0; s < kDqSlots; ++s) {
+    for (int s = 0; s < S; ++s) {
         const uint64_t u = u0 + 64u * s;
         if (u >= nunits) continue;
         float v[8];
@@ -472,8 +477,15 @@ uint32_t* static_ts_workspace(hipError_t* err) {
 
 hipError_t launch_dequantize(int format, int grid, bool bf16_out, const DequantParams& p, hipStream_t s) {
     const uint64_t units = (uint64_t)p.ngroups * (bf16_out ? 2u : 4u);
-    const dim3 b((uint32_t)((units + kThreads * kDqSlots - 1) / (kThreads * kDqSlots))), t(kThreads);
-#define FP4Q_DQ(F, G, B) hipLaunchKernelGGL((k_dequantize<F, G, B>), b, t, 0, s, p)
+    const uint64_t b4 = (units + kThreads * kDqSlotsWide - 1) / (kThreads * kDqSlotsWide);
+    const bool wide = bf16_out && b4 >= kDqWideBlocks;
+    const dim3 b(wide ? (uint32_t)b4 : (uint32_t)((units + kThreads * kDqSlots - 1) / (kThreads * kDqSlots))),
+        t(kThreads);
+#define FP4Q_DQ(F, G, B)                                                                   \
+    do {                                                                                   \
+        if (wide) hipLaunchKernelGGL((k_dequantize<F, G, B, kDqSlotsWide>), b, t, 0, s, p); \
+        else hipLaunchKernelGGL((k_dequantize<F, G, B, kDqSlots>), b, t, 0, s, p);          \
+    } while (0)
     if (format == 0) {
         if (grid == 0) { if (bf16_out) FP4Q_DQ(0, 0, true); else FP4Q_DQ(0, 0, false); }
         else { if (bf16_out) FP4Q_DQ(0, 1, true); else FP4Q_DQ(0, 1, false); }

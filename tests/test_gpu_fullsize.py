@@ -316,3 +316,40 @@ def test_guide_pack_both_slot_counts_whole_tensor(fq, fmt, rows, cols):
     o_gb, o_gs = O.guide_pack(O.Cfg(format=fmt), codes, scales, rows, cols)
     assert (gb.cpu().numpy() == o_gb).all() and (gs.cpu().numpy() == o_gs).all()
     say(f"guide_pack {rows}x{cols} fmt {fmt}: whole tensor bit-exact ({time.time() - t0:.1f} s)")
+
+
+@pytest.mark.parametrize("fmt,rows,cols,pad", [
+    (0, 1048576, 128, 0),     # NVFP4 to bf16, 2^27 elements: four slots per lane, 16384 workgroups (C3)
+    (0, 1048575, 128, 8),     # four slots, the last workgroup partly filled, padded output rows
+    (0, 1048448, 128, 0),     # 16382 workgroups of four slots: two slots per lane instead
+    (1, 524288, 256, 0),      # MXFP4 to bf16, four slots
+])
+def test_dequantize_both_slot_counts_whole_tensor(fq, fmt, rows, cols, pad):
+    # bf16 dequantize takes four slots per lane where that still gives 16384 workgroups, else two:
+    # both against the oracle on the whole tensor, on either side of the threshold
+    t0 = time.time()
+    B = 32 if fmt else 16
+    n = rows * cols
+    rng = np.random.default_rng(rows + fmt)
+    codes = rng.integers(0, 256, n // 2, dtype=np.uint8)
+    if fmt:
+        scales = rng.integers(110, 145, n // B, dtype=np.uint8)          # E8M0 around 2^0
+    else:
+        scales = rng.integers(0, 0x7F, n // B, dtype=np.uint8)           # finite E4M3 magnitudes
+    ts = 0.37109375
+    cfg = fq.Fp4Config(format=fmt)
+    tst = torch.tensor([ts], dtype=torch.float32, device="cuda")
+    if pad:
+        buf = torch.full((rows, cols + pad), -23131, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        out = buf[:, :cols]
+    else:
+        out = torch.full((rows, cols), -23131, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    fq.fp4_dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), cfg, rows, cols,
+                      tst if fmt == 0 else None, out=out)
+    torch.cuda.synchronize()
+    want = O.dequantize(O.Cfg(format=fmt), codes, scales, ts if fmt == 0 else 1.0, rows, cols, out_bf16=True)
+    got = out.contiguous().view(torch.int16).cpu().numpy().reshape(-1)
+    assert (got == want.view(np.int16)).all(), np.nonzero(got != want.view(np.int16))[0][:5]
+    if pad:
+        assert (buf.view(torch.int16)[:, cols:] == -23131).all()
+    say(f"dequantize {rows}x{cols} fmt {fmt} pad {pad}: whole tensor bit-exact ({time.time() - t0:.1f} s)")
