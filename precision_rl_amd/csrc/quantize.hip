@@ -493,10 +493,16 @@ hipError_t launch_mismatch_g(bool rht, bool contig, const QuantParams& p, hipStr
     return hipGetLastError();
 }
 
+// Fake quantization takes two slots for RTN and guided rounding without the RHT,
+// as the single-tensor quantize does (16384 x 4096 MXFP4 guided, bf16 out: 44.3
+// against 46.9 us on four, 50.2 on eight); the others keep the quantizer's count.
+template <int FMT, int MODE, bool RHT>
+constexpr int fake_halves() { return !RHT && MODE != MODE_SR ? 2 : halves_per_lane<FMT, MODE, RHT>(); }
+
 template <int FMT, int GRID, int MODE, bool RHT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_fake_quantize(const QuantParams p) {
     __shared__ float tab[128];
-    quantize_chunk<FMT, GRID, MODE, RHT, false, CONTIG, 1>(p, blockIdx.x, tab);
+    quantize_chunk<FMT, GRID, MODE, RHT, false, CONTIG, 1, fake_halves<FMT, MODE, RHT>()>(p, blockIdx.x, tab);
 }
 
 template <int FMT, int GRID, int MODE>
@@ -507,7 +513,8 @@ hipError_t launch_fake_m(bool rht, bool contig, const QuantParams& p, hipStream_
         if (contig) hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, true, true>), b, t, 0, s, p);
         else hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, true, false>), b, t, 0, s, p);
     } else {
-        const dim3 b((p.ngroups + chunk_groups<FMT, MODE, false>() - 1) / chunk_groups<FMT, MODE, false>());
+        constexpr uint32_t cg = kThreads * (fake_halves<FMT, MODE, false>() / 2);
+        const dim3 b((p.ngroups + cg - 1) / cg);
         if (contig) hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, false, true>), b, t, 0, s, p);
         else hipLaunchKernelGGL((k_fake_quantize<FMT, GRID, MODE, false, false>), b, t, 0, s, p);
     }

@@ -33,7 +33,7 @@ def dev(u16, pad=0):
 @pytest.mark.parametrize("fmt,grid,rnd,rht", [(0, 0, 0, False), (1, 0, 0, False), (1, 0, 1, False),
                                               (0, 1, 1, True), (0, 0, 1, True), (1, 1, 0, False),
                                               (1, 0, 1, True), (1, 1, 0, True)])
-@pytest.mark.parametrize("shape,pad", [((256, 512), 0), ((37, 544), 24), ((1, 64), 0)])
+@pytest.mark.parametrize("shape,pad", [((256, 512), 0), ((37, 544), 24), ((1, 64), 0), ((1031, 1056), 8)])
 def test_fake_quantize_vs_oracle(fq, fmt, grid, rnd, rht, shape, pad):
     rows, cols = shape
     if cols % (32 if fmt else 16):
